@@ -1,0 +1,474 @@
+"""Pins for the fp64 oracle, against facts fixed independently of its code.
+
+Each test checks the oracle against something it does not share code with:
+hand-derived fixtures (tests/golden/), closed forms, library routines
+(numpy.cumsum, math.fsum, scipy.signal.lfilter, numpy.matmul, complex
+arithmetic), exact rational arithmetic over random association trees, O(T^2)
+brute force, and adjoint identities (tangent-linear dot products and central
+finite differences). A plausible slip anywhere in the oracle -- a dropped term,
+a wrong sign, an off-by-one shift, a transposed operand, a segment leak --
+makes at least one of these fail.
+"""
+import json
+import math
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.signal
+
+import gen
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _arr(v):
+    return None if v is None else np.array(v, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# hand-derived fixtures
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", _load("scalar_hand.json")["cases"], ids=lambda c: c["name"])
+def test_scalar_hand_fixture(oracle_lib, case):
+    o = oracle_lib
+    g, x, dy = _arr(case["g"]), _arr(case["x"]), _arr(case["dy"])
+    h0, cu = _arr(case["h0"]), case["cu_seqlens"]
+    h = o.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=case["reverse"])
+    assert np.array_equal(h, _arr(case["h"]))
+    dx, dg, dh0 = o.scan_bwd(g, h, dy, h0=h0, cu_seqlens=cu, reverse=case["reverse"])
+    assert np.array_equal(dx, _arr(case["dx"]))
+    assert np.array_equal(dg, _arr(case["dg"]))
+    assert np.array_equal(dh0, _arr(case["dh0"]))
+
+
+@pytest.mark.parametrize("case", _load("log_hand.json")["cases"], ids=lambda c: c["name"])
+def test_log_hand_fixture(oracle_lib, case):
+    with np.errstate(divide="ignore"):
+        la, lb = np.log(_arr(case["a"])), np.log(_arr(case["b"]))
+        lh0 = None if case["h0"] is None else np.log(_arr(case["h0"]))
+    h = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0, reverse=case["reverse"])
+    np.testing.assert_allclose(h, _arr(case["h"]), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("case", _load("matrix_hand.json")["cases"], ids=lambda c: c["name"])
+def test_matrix_hand_fixture(oracle_lib, case):
+    o = oracle_lib
+    A, B, dy = _arr(case["A"]), _arr(case["B"]), _arr(case["dy"])
+    h = o.matrix_affine_scan_fwd(A, B, h0=_arr(case["h0"]), reverse=case["reverse"])
+    assert np.array_equal(h, _arr(case["h"]))
+    dA, dB, dh0 = o.matrix_affine_scan_bwd(A, h, dy, h0=_arr(case["h0"]), reverse=case["reverse"])
+    assert np.array_equal(dB, _arr(case["dB"]))
+    assert np.array_equal(dA, _arr(case["dA"]))
+    assert np.array_equal(dh0, _arr(case["dh0"]))
+
+
+# ---------------------------------------------------------------------------
+# special cases and closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_zero_gate_gives_x(oracle_lib, reverse):
+    """a_t = 0 erases the prefix (RG-LRU audit, 'Exact real chunk algebra'): h = x exactly."""
+    r = _rng(1)
+    x = r.standard_normal((5, 77))
+    h0 = r.standard_normal((3, 5))
+    cu = np.array([0, 10, 10, 77], dtype=np.int32)
+    h = oracle_lib.scan_fwd(np.zeros_like(x), x, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(h, x)
+    dy = r.standard_normal(x.shape)
+    dx, dg, _ = oracle_lib.scan_bwd(np.zeros_like(x), h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(dx, dy)
+
+
+def test_unit_gate_is_cumsum(oracle_lib):
+    """a_t = 1 turns the scan into h0 + a running sum; compare with exact fsum prefixes."""
+    r = _rng(2)
+    x = r.standard_normal((4, 300))
+    h0 = r.standard_normal(4)
+    h = oracle_lib.scan_fwd(np.ones_like(x), x, h0=h0)
+    for i in range(4):
+        exact = np.array([math.fsum([h0[i], *x[i, : t + 1]]) for t in range(300)])
+        np.testing.assert_allclose(h[i], exact, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(h[i], h0[i] + np.cumsum(x[i]), rtol=0, atol=1e-12)
+    dy = r.standard_normal(x.shape)
+    dx, _, _ = oracle_lib.scan_bwd(np.ones_like(x), h, dy, h0=h0)
+    np.testing.assert_allclose(dx, np.cumsum(dy[:, ::-1], axis=1)[:, ::-1], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("a", [0.3, 0.9, -0.7, 1.05])
+def test_constant_gate_geometric(oracle_lib, a):
+    """Constant a with x = 1: h_n = a^n h0 + (1 - a^n)/(1 - a); random x: scipy lfilter."""
+    T = 200
+    h0 = 0.75
+    h = oracle_lib.scan_fwd(np.full((1, T), a), np.ones((1, T)), h0=np.array([h0]))[0]
+    n = np.arange(1, T + 1)
+    closed = a ** n * h0 + (1 - a ** n) / (1 - a)
+    np.testing.assert_allclose(h, closed, rtol=1e-12, atol=1e-12)
+    x = _rng(3).standard_normal(T)
+    h = oracle_lib.scan_fwd(np.full((1, T), a), x[None], h0=np.array([h0]))[0]
+    ref, _ = scipy.signal.lfilter([1.0], [1.0, -a], x, zi=[a * h0])
+    np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-11)
+
+
+def test_brute_force_sum_of_products(oracle_lib):
+    """h_t = (prod_{r=s..t} g_r) h0 + sum_u (prod_{r=u+1..t} g_r) x_u, O(T^2), every segment."""
+    r = _rng(4)
+    T = 48
+    g = r.uniform(-1.2, 1.2, (3, T))
+    x = r.standard_normal((3, T))
+    cu = np.array([0, 5, 5, 20, 48], dtype=np.int32)
+    h0 = r.standard_normal((4, 3))
+    for reverse in (False, True):
+        h = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+        ref = np.zeros_like(h)
+        for row in range(3):
+            for s in range(4):
+                idx = list(range(cu[s], cu[s + 1]))
+                if reverse:
+                    idx = idx[::-1]
+                for j, t in enumerate(idx):
+                    tot = np.prod([g[row, idx[q]] for q in range(0, j + 1)]) * h0[s, row]
+                    for i in range(j + 1):
+                        tot += np.prod([g[row, idx[q]] for q in range(i + 1, j + 1)]) * x[row, idx[i]]
+                    ref[row, t] = tot
+        np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-12)
+
+
+def _compose(e, l):
+    """(P, Q) of 'apply e then l' for maps h -> P h + Q."""
+    return (l[0] * e[0], l[0] * e[1] + l[1])
+
+
+def _tree_reduce(items, rnd):
+    """Combine a list of maps in order with a random binary bracketing."""
+    if len(items) == 1:
+        return items[0]
+    cut = rnd.randint(1, len(items) - 1)
+    return _compose(_tree_reduce(items[:cut], rnd), _tree_reduce(items[cut:], rnd))
+
+
+def test_regrouping_exact_rationals(oracle_lib):
+    """The affine monoid (minGRU page, 'One associative-scan family') is associative: any
+    bracketing of the steps, in exact rationals, gives the same prefix, and the fp64
+    oracle must agree with it."""
+    rnd = random.Random(5)
+    for trial in range(40):
+        T = rnd.randint(1, 16)
+        g = [Fraction(rnd.randint(-9, 9), rnd.randint(1, 8)) for _ in range(T)]
+        x = [Fraction(rnd.randint(-9, 9), rnd.randint(1, 8)) for _ in range(T)]
+        h0 = Fraction(rnd.randint(-5, 5), 3)
+        ref = []
+        for t in range(T):
+            P, Q = _tree_reduce(list(zip(g[: t + 1], x[: t + 1])), rnd)
+            P2, Q2 = _tree_reduce(list(zip(g[: t + 1], x[: t + 1])), rnd)
+            assert (P, Q) == (P2, Q2)
+            ref.append(P * h0 + Q)
+        h = oracle_lib.scan_fwd(np.array([[float(v) for v in g]]), np.array([[float(v) for v in x]]),
+                                h0=np.array([float(h0)]))[0]
+        refd = np.array([float(v) for v in ref])
+        np.testing.assert_allclose(h, refd, rtol=1e-13, atol=1e-13)
+
+
+def test_reverse_is_flip_scan_flip(oracle_lib):
+    r = _rng(6)
+    T = 101
+    g, x = r.uniform(0, 1, (4, T)), r.standard_normal((4, T))
+    cu = np.array([0, 1, 40, 40, 101], dtype=np.int32)
+    h0 = r.standard_normal((4, 4))
+    hr = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=True)
+    for s in range(4):
+        a, b = cu[s], cu[s + 1]
+        if b == a:
+            continue
+        hf = oracle_lib.scan_fwd(g[:, a:b][:, ::-1], x[:, a:b][:, ::-1], h0=h0[s])
+        assert np.array_equal(hr[:, a:b], hf[:, ::-1])
+
+
+def test_varlen_equals_separate_sequences(oracle_lib):
+    """cu_seqlens packing: each sequence is scanned on its own, no cross-document leakage."""
+    r = _rng(7)
+    T = 300
+    g, x, dy = r.uniform(0, 1, (3, T)), r.standard_normal((3, T)), r.standard_normal((3, T))
+    cu = gen.segments_random(r, T, 9)
+    h0 = r.standard_normal((9, 3))
+    # poison one segment: nothing else may change
+    s_bad = int(np.argmax(np.diff(cu)))
+    g[:, cu[s_bad]:cu[s_bad + 1]] = np.nan
+    for reverse in (False, True):
+        h = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+        dx, dg, dh0 = oracle_lib.scan_bwd(g, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+        for s in range(9):
+            a, b = cu[s], cu[s + 1]
+            if b == a:
+                assert np.all(dh0[s] == 0)
+                continue
+            hs = oracle_lib.scan_fwd(g[:, a:b], x[:, a:b], h0=h0[s], reverse=reverse)
+            assert np.array_equal(h[:, a:b], hs, equal_nan=True)
+            dxs, dgs, dh0s = oracle_lib.scan_bwd(g[:, a:b], hs, dy[:, a:b], h0=h0[s], reverse=reverse)
+            assert np.array_equal(dx[:, a:b], dxs, equal_nan=True)
+            assert np.array_equal(dg[:, a:b], dgs, equal_nan=True)
+            if s != s_bad:
+                assert np.all(np.isfinite(h[:, a:b])) and np.all(np.isfinite(dg[:, a:b]))
+
+
+def test_exact_integer_mode(oracle_lib):
+    """g in {0,1}, x in {-1,0,1}: the scan is exact integer arithmetic."""
+    r = _rng(8)
+    g, x, dy = gen.exact_mode(r, (3, 500), max_run=64)
+    h0 = r.integers(-1, 2, size=3).astype(np.float64)
+    h = oracle_lib.scan_fwd(g, x, h0=h0)
+    for i in range(3):
+        st = int(h0[i])
+        for t in range(500):
+            st = int(g[i, t]) * st + int(x[i, t])
+            assert h[i, t] == st
+
+
+# ---------------------------------------------------------------------------
+# backward: adjoint identities
+# ---------------------------------------------------------------------------
+def _tangent_scalar(g, x, h0, gd, xd, h0d, cu, reverse):
+    """Forward-mode derivative of the scalar scan: hd_t = gd_t h_{t-1} + g_t hd_{t-1} + xd_t."""
+    rows, T = g.shape
+    h = np.zeros_like(g)
+    hd = np.zeros_like(g)
+    for s in range(len(cu) - 1):
+        idx = list(range(cu[s], cu[s + 1]))
+        if reverse:
+            idx = idx[::-1]
+        st = h0[s].copy()
+        std = h0d[s].copy()
+        for t in idx:
+            std = gd[:, t] * st + g[:, t] * std + xd[:, t]
+            st = g[:, t] * st + x[:, t]
+            h[:, t], hd[:, t] = st, std
+    return h, hd
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_scalar_adjoint_dot_product(oracle_lib, reverse):
+    """<dy, J v> = <J^T dy, v> with J v from the tangent-linear recurrence."""
+    r = _rng(9)
+    T = 257
+    g, x = r.uniform(-1, 1, (4, T)), r.standard_normal((4, T))
+    cu = gen.segments_random(r, T, 6)
+    h0 = r.standard_normal((6, 4))
+    gd, xd, h0d = r.standard_normal(g.shape), r.standard_normal(g.shape), r.standard_normal(h0.shape)
+    dy = r.standard_normal(g.shape)
+    href, hd = _tangent_scalar(g, x, h0, gd, xd, h0d, cu, reverse)
+    h = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+    np.testing.assert_allclose(h, href, rtol=1e-13, atol=1e-13)
+    dx, dg, dh0 = oracle_lib.scan_bwd(g, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    lhs = np.sum(dy * hd)
+    rhs = np.sum(dg * gd) + np.sum(dx * xd) + np.sum(dh0 * h0d)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_scalar_finite_differences(oracle_lib):
+    r = _rng(10)
+    T = 24
+    g, x = r.uniform(-1, 1, (2, T)), r.standard_normal((2, T))
+    cu = np.array([0, 9, 24], dtype=np.int32)
+    h0 = r.standard_normal((2, 2))
+    dy = r.standard_normal(g.shape)
+    for reverse in (False, True):
+        L = lambda g_, x_, h0_: np.sum(dy * oracle_lib.scan_fwd(g_, x_, h0=h0_, cu_seqlens=cu, reverse=reverse))
+        h = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+        dx, dg, dh0 = oracle_lib.scan_bwd(g, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+        eps = 1e-6
+        for (i, t) in [(0, 0), (0, 8), (1, 9), (1, 23), (0, 15)]:
+            for arr, grad in ((g, dg), (x, dx)):
+                p, m = arr.copy(), arr.copy()
+                p[i, t] += eps
+                m[i, t] -= eps
+                args_p = (p, x, h0) if arr is g else (g, p, h0)
+                args_m = (m, x, h0) if arr is g else (g, m, h0)
+                fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+                assert abs(fd - grad[i, t]) < 1e-6 * max(1, abs(fd))
+        for s in range(2):
+            for i in range(2):
+                p, m = h0.copy(), h0.copy()
+                p[s, i] += eps
+                m[s, i] -= eps
+                fd = (L(g, x, p) - L(g, x, m)) / (2 * eps)
+                assert abs(fd - dh0[s, i]) < 1e-6 * max(1, abs(fd))
+
+
+# ---------------------------------------------------------------------------
+# log space
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_equals_linear(oracle_lib, reverse):
+    """The log-space form is the same recurrence: compare with the linear scan on
+    a = exp(log_a), b = exp(log_b), using the log-space workload's distributions."""
+    d = gen.logspace(B=2, D=8, T=2048)
+    la, lb = d["log_a"].astype(np.float64), d["log_b"].astype(np.float64)
+    cu = np.array([0, 700, 700, 2048], dtype=np.int32)
+    lh0 = _rng(11).standard_normal((3, 16))
+    h = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    hl = oracle_lib.scan_fwd(np.exp(la), np.exp(lb), h0=np.exp(lh0), cu_seqlens=cu, reverse=reverse)
+    np.testing.assert_allclose(h, hl, rtol=1e-11, atol=0)
+
+
+def test_log_wide_dynamic_range(oracle_lib):
+    """Shifting every log_b by c scales h by e^c (the recurrence is linear in b);
+    with c = -600 the values sit near fp64's lower range and stay accurate."""
+    r = _rng(12)
+    la = -np.log1p(np.exp(r.standard_normal((2, 500))))
+    lb = r.standard_normal((2, 500))
+    h1 = oracle_lib.scan_log_fwd(la, lb)
+    h2 = oracle_lib.scan_log_fwd(la, lb - 600.0)
+    np.testing.assert_allclose(h2, h1 * np.exp(-600.0), rtol=1e-12)
+    assert np.all(h2 > 0)
+
+
+def test_log_zero_gate_restarts(oracle_lib):
+    r = _rng(13)
+    la = -np.log1p(np.exp(r.standard_normal((3, 64))))
+    lb = r.standard_normal((3, 64))
+    la[:, 20] = -np.inf
+    h = oracle_lib.scan_log_fwd(la, lb, log_h0=r.standard_normal(3))
+    np.testing.assert_allclose(h[:, 20], np.exp(lb[:, 20]), rtol=1e-15)
+    h_tail = oracle_lib.scan_log_fwd(la[:, 21:], lb[:, 21:], log_h0=np.log(h[:, 20]))
+    np.testing.assert_allclose(h[:, 21:], h_tail, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# matrix-affine
+# ---------------------------------------------------------------------------
+def test_matrix_k1_is_scalar(oracle_lib):
+    r = _rng(14)
+    g, x = r.uniform(-1, 1, (3, 90)), r.standard_normal((3, 90))
+    cu = np.array([0, 30, 90], dtype=np.int32)
+    h0 = r.standard_normal((2, 3))
+    for reverse in (False, True):
+        hs = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+        hm = oracle_lib.matrix_affine_scan_fwd(g[..., None, None], x[..., None, None], h0=h0[..., None, None],
+                                               cu_seqlens=cu, reverse=reverse)
+        assert np.array_equal(hm[..., 0, 0], hs)
+
+
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (2, 3)])
+def test_matrix_brute_force_products(oracle_lib, kv):
+    """h_t = (A_t...A_s) h0 + sum_u (A_t...A_{u+1}) B_u with numpy matmul, every segment."""
+    k, v = kv
+    r = _rng(15 + k)
+    T = 20
+    A = r.standard_normal((2, T, k, k)) * 0.6
+    B = r.standard_normal((2, T, k, v))
+    cu = np.array([0, 7, 20], dtype=np.int32)
+    h0 = r.standard_normal((2, 2, k, v))
+    for reverse in (False, True):
+        h = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, cu_seqlens=cu, reverse=reverse)
+        for row in range(2):
+            for s in range(2):
+                idx = list(range(cu[s], cu[s + 1]))
+                if reverse:
+                    idx = idx[::-1]
+                for j, t in enumerate(idx):
+                    M = np.eye(k)
+                    acc = np.zeros((k, v))
+                    for i in range(j, -1, -1):
+                        acc = acc + M @ B[row, idx[i]]
+                        M = M @ A[row, idx[i]]
+                    acc = acc + M @ h0[s, row]
+                    np.testing.assert_allclose(h[row, t], acc, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_rotation_is_complex_scan(oracle_lib):
+    """k=2, v=1 with A = r Rot(theta) is multiplication by r e^{i theta}; its adjoint
+    (A^T) is multiplication by r e^{-i theta}."""
+    d = gen.matrix_rot2(B=1, N=3, T=400)
+    A, B, dy = (d[n].astype(np.float64) for n in ("A", "B", "dy"))
+    h = oracle_lib.matrix_affine_scan_fwd(A, B)
+    a = A[..., 0, 0] + 1j * A[..., 1, 0]
+    b = B[..., 0, 0] + 1j * B[..., 1, 0]
+    z = np.zeros_like(b)
+    st = np.zeros(b.shape[0], dtype=complex)
+    for t in range(b.shape[1]):
+        st = a[:, t] * st + b[:, t]
+        z[:, t] = st
+    np.testing.assert_allclose(h[..., 0, 0], z.real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h[..., 1, 0], z.imag, rtol=1e-12, atol=1e-12)
+    dA, dB, _ = oracle_lib.matrix_affine_scan_bwd(A, h, dy)
+    w = dy[..., 0, 0] + 1j * dy[..., 1, 0]
+    lam = np.zeros_like(w)
+    st = np.zeros(w.shape[0], dtype=complex)
+    for t in range(w.shape[1] - 1, -1, -1):
+        nxt = np.conj(a[:, t + 1]) if t + 1 < w.shape[1] else 0.0
+        st = w[:, t] + nxt * st
+        lam[:, t] = st
+    np.testing.assert_allclose(dB[..., 0, 0], lam.real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dB[..., 1, 0], lam.imag, rtol=1e-12, atol=1e-12)
+
+
+def test_matrix_reset_gives_B(oracle_lib):
+    d = gen.matrix_orth4(B=1, N=2, T=64, p_reset=0.1)
+    A, B = d["A"].astype(np.float64), d["B"].astype(np.float64)
+    h = oracle_lib.matrix_affine_scan_fwd(A, B, h0=np.ones((1, 2, 4, 4)))
+    assert d["reset"].any()
+    assert np.array_equal(h[d["reset"]], B[d["reset"]])
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+def test_matrix_adjoint_dot_product(oracle_lib, kv, reverse):
+    k, v = kv
+    r = _rng(20 + k)
+    T = 60
+    A = r.standard_normal((3, T, k, k)) * 0.5
+    B = r.standard_normal((3, T, k, v))
+    cu = np.array([0, 13, 13, 60], dtype=np.int32)
+    h0 = r.standard_normal((3, 3, k, v))
+    Ad, Bd, h0d = r.standard_normal(A.shape), r.standard_normal(B.shape), r.standard_normal(h0.shape)
+    dy = r.standard_normal(B.shape)
+    h = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, cu_seqlens=cu, reverse=reverse)
+    hd = np.zeros_like(h)
+    for s in range(3):
+        idx = list(range(cu[s], cu[s + 1]))
+        if reverse:
+            idx = idx[::-1]
+        st, std = h0[s].copy(), h0d[s].copy()
+        for t in idx:
+            std = Ad[:, t] @ st + A[:, t] @ std + Bd[:, t]
+            st = A[:, t] @ st + B[:, t]
+            hd[:, t] = std
+    dA, dB, dh0 = oracle_lib.matrix_affine_scan_bwd(A, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    lhs = np.sum(dy * hd)
+    rhs = np.sum(dA * Ad) + np.sum(dB * Bd) + np.sum(dh0 * h0d)
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
+
+
+def test_matrix_finite_differences(oracle_lib):
+    r = _rng(30)
+    k, v, T = 2, 2, 12
+    A = r.standard_normal((1, T, k, k)) * 0.7
+    B = r.standard_normal((1, T, k, v))
+    h0 = r.standard_normal((1, 1, k, v))
+    dy = r.standard_normal(B.shape)
+    L = lambda A_, B_, h0_: np.sum(dy * oracle_lib.matrix_affine_scan_fwd(A_, B_, h0=h0_))
+    h = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0)
+    dA, dB, dh0 = oracle_lib.matrix_affine_scan_bwd(A, h, dy, h0=h0)
+    eps = 1e-6
+    for (t, p, q) in [(0, 0, 1), (5, 1, 0), (11, 1, 1)]:
+        P, M = A.copy(), A.copy()
+        P[0, t, p, q] += eps
+        M[0, t, p, q] -= eps
+        fd = (L(P, B, h0) - L(M, B, h0)) / (2 * eps)
+        assert abs(fd - dA[0, t, p, q]) < 1e-6 * max(1, abs(fd))
+    P, M = h0.copy(), h0.copy()
+    P[0, 0, 1, 0] += eps
+    M[0, 0, 1, 0] -= eps
+    fd = (L(A, B, P) - L(A, B, M)) / (2 * eps)
+    assert abs(fd - dh0[0, 0, 1, 0]) < 1e-6 * max(1, abs(fd))

@@ -1,0 +1,376 @@
+"""Python binding of libmscan, the MI355X (gfx950) affine associative scan.
+
+Thin argument marshalling over the C ABI in ``include/mscan.h``: every step of
+every scan runs in the library's HIP kernels; PyTorch only provides device
+memory and the current stream. There is no CPU or eager fallback: a missing
+library or a missing GPU raises.
+
+Entry points (same names as the C ABI):
+    scan_fwd(g, x, h0=None, cu_seqlens=None, reverse=False) -> h
+    scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dx, dg, dh0)
+    scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False) -> h
+    matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False) -> h
+    matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dA, dB, dh0)
+
+Scalar tensors are [..., T] (every leading axis is an independent row, time
+contiguous); matrix tensors are [..., T, k, k] and [..., T, k, v]. ``h0`` is
+[nseg, rows] ([nseg, rows, k, v] for matrices) or, with one sequence, the shape
+of the leading axes. ``cu_seqlens`` is an int32 device tensor in the flash-attn
+convention. Inputs are fp32, or bf16 for the scalar scan's g and x; outputs
+are fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "lib", "library_path", "Problem", "MscanError",
+    "scan_fwd", "scan_bwd", "scan_log_fwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
+    "scan_causal", "scan_bidirectional_branched",
+    "workspace_bytes", "OP_SCAN_FWD", "OP_SCAN_BWD", "OP_SCAN_LOG_FWD", "OP_MATRIX_FWD", "OP_MATRIX_BWD",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmscan.so")
+
+OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD = range(5)
+_F32, _BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error"}
+
+
+class MscanError(RuntimeError):
+    def __init__(self, fn, status, detail=""):
+        self.status = status
+        msg = f"{fn}: {_STATUS.get(status, status)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("T", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+        ("cu_seqlens", ctypes.c_void_p), ("nseg", ctypes.c_int32), ("reverse", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"libmscan.so not found at {library_path}; build it with `python -m associative_scan_amd.build`")
+    L = ctypes.CDLL(library_path)
+    P, p, sz, i32 = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "mscan_workspace_bytes": (sz, [P, i32, i32, i32]),
+        "mscan_workspace_init": (i32, [p, sz, p]),
+        "scan_fwd": (i32, [P, i32, p, p, p, p, p, sz, p]),
+        "scan_bwd": (i32, [P, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "scan_log_fwd": (i32, [P, p, p, p, p, p, sz, p]),
+        "matrix_affine_scan_fwd": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
+        "matrix_affine_scan_bwd": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "mscan_status_string": (ctypes.c_char_p, [i32]),
+        "mscan_last_hip_error": (ctypes.c_char_p, []),
+        "mscan_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    if L.mscan_abi_version() != 1:
+        raise ImportError("libmscan ABI version mismatch")
+    return L
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _rows_view(t: torch.Tensor, name: str, tail: int = 0):
+    """(rows, T, row_stride) of a tensor viewed as [rows, T, *tail] with the
+    trailing (T, *tail) block contiguous and a uniform stride between rows."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() < 1 + tail:
+        raise ValueError(f"{name} needs at least {1 + tail} dims")
+    inner = t.shape[t.dim() - 1 - tail:]
+    T = int(inner[0])
+    block = 1
+    for d in inner[1:]:
+        block *= int(d)
+    # trailing block contiguous
+    expect = 1
+    for i in range(t.dim() - 1, t.dim() - 2 - tail, -1):
+        if t.shape[i] != 1 and t.stride(i) != expect:
+            raise ValueError(f"{name}: time (and matrix) axes must be contiguous")
+        expect *= t.shape[i]
+    lead = t.shape[: t.dim() - 1 - tail]
+    rows = 1
+    for d in lead:
+        rows *= int(d)
+    if rows == 0 or T == 0:
+        return rows, T, T
+    # leading axes must collapse to one uniform stride (in units of the trailing block)
+    stride_el = None
+    exp = None
+    for i in range(len(lead) - 1, -1, -1):
+        if lead[i] == 1:
+            continue
+        if stride_el is None:
+            stride_el = t.stride(i)
+            exp = stride_el * lead[i]
+        else:
+            if t.stride(i) != exp:
+                raise ValueError(f"{name}: leading axes do not collapse to a single row stride")
+            exp *= lead[i]
+    if stride_el is None:
+        stride_el = T * block
+    if stride_el % block:
+        raise ValueError(f"{name}: row stride not a multiple of the per-step block")
+    return rows, T, stride_el // block
+
+
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def _workspace(device, stream_handle, nbytes):
+    """A zero-initialised workspace of at least nbytes for (device, stream)."""
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            size = max(nbytes, 1 << 16)
+            buf = torch.empty(size, dtype=torch.uint8, device=device)
+            st = lib.mscan_workspace_init(_ptr(buf), size, ctypes.c_void_p(stream_handle))
+            if st != 0:
+                raise MscanError("mscan_workspace_init", st, lib.mscan_last_hip_error().decode())
+            _ws_cache[key] = buf
+        return buf
+
+
+def workspace_bytes(prob: Problem, op: int, k: int = 1, v: int = 1) -> int:
+    return int(lib.mscan_workspace_bytes(ctypes.byref(prob), op, k, v))
+
+
+def _segments(cu_seqlens, device, T):
+    if cu_seqlens is None:
+        return None, 1
+    if not isinstance(cu_seqlens, torch.Tensor):
+        cu_seqlens = torch.tensor(cu_seqlens, dtype=torch.int32, device=device)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    if cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
+    return cu_seqlens, cu_seqlens.numel() - 1
+
+
+def _h0(h0, nseg, rows, tail, name="h0"):
+    if h0 is None:
+        return None
+    if h0.dtype != torch.float32 or not h0.is_cuda or not h0.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+    need = nseg * rows
+    for d in tail:
+        need *= d
+    if h0.numel() != need:
+        raise ValueError(f"{name} must hold nseg*rows states ({need} values), got {h0.numel()}")
+    return h0
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MscanError(fn, status, lib.mscan_last_hip_error().decode() if status == 4 else "")
+
+
+def _in_dtype(t, name):
+    if t.dtype == torch.float32:
+        return _F32
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    raise ValueError(f"{name}: only float32 and bfloat16 inputs are supported")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def scan_fwd(g, x, h0=None, cu_seqlens=None, reverse=False, out=None):
+    """h_t = g_t h_{t-1} + x_t per row and per packed sequence (fp32 result)."""
+    if g.shape != x.shape or g.dtype != x.dtype:
+        raise ValueError("g and x must have the same shape and dtype")
+    rows, T, stride = _rows_view(g, "g")
+    if _rows_view(x, "x")[2] != stride:
+        raise ValueError("g and x must share the row stride")
+    dt = _in_dtype(g, "g")
+    dev = g.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    h0 = _h0(h0, nseg, rows, ())
+    h = torch.empty(g.shape, dtype=torch.float32, device=dev) if out is None else out
+    if stride != T and out is None:
+        raise ValueError("strided rows need an explicit `out` with the same row stride")
+    if h.shape != g.shape or _rows_view(h, "out")[2] != stride:
+        raise ValueError("out must match g's shape and row stride")
+    if rows == 0 or T == 0:
+        return h
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    need = workspace_bytes(prob, OP_SCAN_FWD)
+    ws = _workspace(dev, sh, need)
+    _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
+                                    _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    return h
+
+
+def scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
+    """Adjoint of scan_fwd: (dx, dg, dh0) given the forward's output h and dy."""
+    if h.dtype != torch.float32 or dy.dtype != torch.float32:
+        raise ValueError("h and dy must be float32")
+    if g.shape != h.shape or dy.shape != h.shape:
+        raise ValueError("g, h and dy must have the same shape")
+    rows, T, stride = _rows_view(g, "g")
+    for t, n in ((h, "h"), (dy, "dy")):
+        if _rows_view(t, n)[2] != stride:
+            raise ValueError("g, h and dy must share the row stride")
+    if stride != T:
+        raise ValueError("scan_bwd takes contiguous rows")
+    dt = _in_dtype(g, "g")
+    dev = g.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    h0 = _h0(h0, nseg, rows, ())
+    dx = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    dg = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    dh0 = torch.empty((nseg, rows), dtype=torch.float32, device=dev) if need_dh0 else None
+    if rows == 0 or T == 0:
+        if dh0 is not None:
+            dh0.zero_()
+        return dx, dg, dh0
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_BWD))
+    _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
+                                    _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    return dx, dg, dh0
+
+
+def scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
+    """h = exp of the log-space scan of h_t = a_t h_{t-1} + b_t (fp32 in, fp32 out)."""
+    if log_a.shape != log_b.shape or log_a.dtype != torch.float32 or log_b.dtype != torch.float32:
+        raise ValueError("log_a and log_b must be float32 tensors of one shape")
+    rows, T, stride = _rows_view(log_a, "log_a")
+    if _rows_view(log_b, "log_b")[2] != stride or stride != T:
+        raise ValueError("scan_log_fwd takes contiguous rows")
+    dev = log_a.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    log_h0 = _h0(log_h0, nseg, rows, (), "log_h0")
+    h = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
+    if rows == 0 or T == 0:
+        return h
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_FWD))
+    _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
+                                            _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    return h
+
+
+def _mat_dims(A, Bh, nameB):
+    if A.dtype != torch.float32 or Bh.dtype != torch.float32:
+        raise ValueError("matrix scan inputs must be float32")
+    if A.dim() < 3 or Bh.dim() < 3:
+        raise ValueError("matrix inputs are [..., T, k, k] and [..., T, k, v]")
+    k, v = int(A.shape[-1]), int(Bh.shape[-1])
+    if A.shape[-2] != k or Bh.shape[-2] != k or A.shape[:-2] != Bh.shape[:-2]:
+        raise ValueError(f"A must be [..., T, k, k] and {nameB} [..., T, k, v] with matching leading axes")
+    rows, T, stride = _rows_view(A, "A", tail=2)
+    if _rows_view(Bh, nameB, tail=2)[2] != stride or stride != T:
+        raise ValueError("matrix scans take contiguous rows")
+    return rows, T, k, v
+
+
+def matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False):
+    """h_t = A_t h_{t-1} + B_t with k x k transitions and k x v states."""
+    rows, T, k, v = _mat_dims(A, B, "B")
+    dev = A.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    h0 = _h0(h0, nseg, rows, (k, v))
+    h = torch.empty(B.shape, dtype=torch.float32, device=dev)
+    if rows == 0 or T == 0:
+        return h
+    prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_FWD, k, v))
+    _check("matrix_affine_scan_fwd", lib.matrix_affine_scan_fwd(
+        ctypes.byref(prob), k, v, _ptr(A), _ptr(B), _ptr(h0), _ptr(h), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    return h
+
+
+def matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
+    """Adjoint of matrix_affine_scan_fwd: (dA, dB, dh0)."""
+    rows, T, k, v = _mat_dims(A, h, "h")
+    if dy.shape != h.shape or dy.dtype != torch.float32:
+        raise ValueError("dy must match h")
+    dev = A.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    h0 = _h0(h0, nseg, rows, (k, v))
+    dA = torch.empty(A.shape, dtype=torch.float32, device=dev)
+    dB = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    dh0 = torch.empty((nseg, rows, k, v), dtype=torch.float32, device=dev) if need_dh0 else None
+    if rows == 0 or T == 0:
+        if dh0 is not None:
+            dh0.zero_()
+        return dA, dB, dh0
+    prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_BWD, k, v))
+    _check("matrix_affine_scan_bwd", lib.matrix_affine_scan_bwd(
+        ctypes.byref(prob), k, v, _ptr(A), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dA), _ptr(dB), _ptr(dh0),
+        _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    return dA, dB, dh0
+
+
+# ---------------------------------------------------------------------------
+# autograd wrappers in the README's calling convention
+# ---------------------------------------------------------------------------
+class _ScanFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, g, x, h0, cu_seqlens, reverse):
+        h = scan_fwd(g, x, h0=h0, cu_seqlens=cu_seqlens, reverse=reverse)
+        ctx.save_for_backward(g, h, h0, cu_seqlens)
+        ctx.reverse = reverse
+        ctx.x_dtype = x.dtype
+        return h
+
+    @staticmethod
+    def backward(ctx, dy):
+        g, h, h0, cu = ctx.saved_tensors
+        dx, dg, dh0 = scan_bwd(g, h, dy.contiguous().float(), h0=h0, cu_seqlens=cu, reverse=ctx.reverse,
+                               need_dh0=h0 is not None and ctx.needs_input_grad[2])
+        if dh0 is not None and h0 is not None:
+            dh0 = dh0.view(h0.shape)
+        return dg.to(g.dtype), dx.to(ctx.x_dtype), dh0, None, None
+
+
+def scan_causal(gates, tokens, cu_seqlens=None, h0=None):
+    """Differentiable causal scan h[t] = gates[t] h[t-1] + tokens[t] (fp32 output)."""
+    return _ScanFn.apply(gates, tokens, h0, cu_seqlens, False)
+
+
+def scan_bidirectional_branched(gates_fwd, tokens_fwd, gates_bwd, tokens_bwd, cu_seqlens=None):
+    """Two independent branches: a causal scan and a reverse-in-time scan."""
+    return (_ScanFn.apply(gates_fwd, tokens_fwd, None, cu_seqlens, False),
+            _ScanFn.apply(gates_bwd, tokens_bwd, None, cu_seqlens, True))

@@ -1,0 +1,176 @@
+// C ABI of libmscan: host-side validation, workspace sizing and dispatch.
+// Every check runs before any HIP call; nothing is enqueued on an error.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mscan.h"
+#include "mscan_launch.hpp"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+mscan_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MSCAN_OK;
+  strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return MSCAN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Problem shape checks shared by every op.
+mscan_status check_problem(const mscan_problem* p) {
+  if (!p) return MSCAN_ERR_INVALID;
+  if (p->rows < 1 || p->T < 1 || p->row_stride < p->T) return MSCAN_ERR_INVALID;
+  if (p->T > (int64_t)INT32_MAX) return MSCAN_ERR_INVALID;  // cu_seqlens offsets are int32
+  if (p->nseg < 1) return MSCAN_ERR_INVALID;
+  if (!p->cu_seqlens && p->nseg != 1) return MSCAN_ERR_INVALID;
+  if (p->cu_seqlens && ((uintptr_t)p->cu_seqlens & 3u)) return MSCAN_ERR_INVALID;
+  if (p->reverse != 0 && p->reverse != 1) return MSCAN_ERR_INVALID;
+  return MSCAN_OK;
+}
+
+// Tiles per row of the scalar kernels for one input type.
+int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
+  return mscan::scalar_tiles(p->T, p->row_stride, mscan::scalar_vec(in_dtype), mscan::scalar_tile_elems(in_dtype));
+}
+
+// Workspace for either input type: header + 3 descriptor words per tile.
+size_t scalar_ws_bytes(const mscan_problem* p) {
+  int64_t nt = scalar_tiles_for(p, MSCAN_F32);
+  const int64_t nb = scalar_tiles_for(p, MSCAN_BF16);
+  if (nb > nt) nt = nb;
+  if (nt <= 1) return mscan::kWsHeaderBytes;
+  return mscan::kWsHeaderBytes + (size_t)p->rows * (size_t)nt * 3u * sizeof(uint64_t);
+}
+
+mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
+  const double blocks = (double)p->rows * (double)tiles_per_row;
+  if (blocks > 4294967295.0) return MSCAN_ERR_UNSUPPORTED;  // 32-bit tile ids / grid size
+  return MSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
+  (void)k;
+  (void)v;
+  if (check_problem(prob) != MSCAN_OK) return 0;
+  switch (op) {
+    case MSCAN_OP_SCAN_FWD:
+    case MSCAN_OP_SCAN_BWD:
+      return scalar_ws_bytes(prob);
+    default:
+      return 0;
+  }
+}
+
+mscan_status mscan_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned16(ws) || ws_bytes < mscan::kWsHeaderBytes) return MSCAN_ERR_INVALID;
+  return hip_status(mscan::launch_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
+                      const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
+  if (!g || !x || !h) return MSCAN_ERR_INVALID;
+  if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
+  const int64_t nt = scalar_tiles_for(prob, in_dtype);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (nt > 1 && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob))) return MSCAN_ERR_WORKSPACE;
+  mscan::ScalarArgs a{};
+  a.g = g;
+  a.b = x;
+  a.h0 = h0;
+  a.out0 = h;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse;
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_scalar(a, in_dtype, false, (hipStream_t)stream));
+}
+
+mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, const float* h,
+                      const float* dy, const float* h0, float* dx, float* dg, float* dh0, void* ws,
+                      size_t ws_bytes, void* stream) {
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
+  if (!g || !h || !dy || !dx || !dg) return MSCAN_ERR_INVALID;
+  if (!aligned16(g) || !aligned16(h) || !aligned16(dy) || !aligned16(dx) || !aligned16(dg))
+    return MSCAN_ERR_INVALID;
+  if ((h0 && ((uintptr_t)h0 & 3u)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
+  const int64_t nt = scalar_tiles_for(prob, in_dtype);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (nt > 1 && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob))) return MSCAN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (dh0 && prob->cu_seqlens) {
+    // empty sequences have no element to write their (zero) gradient
+    const mscan_status z = hip_status(mscan::launch_zero(dh0, (size_t)prob->nseg * (size_t)prob->rows * 4u, st));
+    if (z != MSCAN_OK) return z;
+  }
+  mscan::ScalarArgs a{};
+  a.g = g;
+  a.b = dy;
+  a.hs = h;
+  a.h0 = h0;
+  a.out0 = dx;
+  a.out1 = dg;
+  a.dh0 = dh0;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse ? 0 : 1;  // the adjoint runs against the forward's order
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_scalar(a, in_dtype, true, st));
+}
+
+mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
+                          const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  (void)prob; (void)log_a; (void)log_b; (void)log_h0; (void)h; (void)ws; (void)ws_bytes; (void)stream;
+  return MSCAN_ERR_UNSUPPORTED;
+}
+
+mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,
+                                    const float* B, const float* h0, float* h, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  (void)prob; (void)k; (void)v; (void)A; (void)B; (void)h0; (void)h; (void)ws; (void)ws_bytes; (void)stream;
+  return MSCAN_ERR_UNSUPPORTED;
+}
+
+mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, const float* A,
+                                    const float* h, const float* dy, const float* h0, float* dA,
+                                    float* dB, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  (void)prob; (void)k; (void)v; (void)A; (void)h; (void)dy; (void)h0; (void)dA; (void)dB; (void)dh0;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return MSCAN_ERR_UNSUPPORTED;
+}
+
+const char* mscan_status_string(int status) {
+  switch (status) {
+    case MSCAN_OK: return "ok";
+    case MSCAN_ERR_INVALID: return "invalid argument";
+    case MSCAN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MSCAN_ERR_WORKSPACE: return "workspace missing or too small";
+    case MSCAN_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* mscan_last_hip_error(void) { return g_last_hip_error; }
+
+int mscan_abi_version(void) { return MSCAN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Private interface between the C ABI (mscan_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+// Arguments of the scalar forward / backward kernels (see scan_scalar.hip).
+struct ScalarArgs {
+  const void* g;        // gates, fp32 or bf16
+  const void* b;        // forward: x (same type as g); backward: dy (fp32)
+  const float* hs;      // backward: forward states h
+  const float* h0;      // [nseg][rows] or null
+  float* out0;          // forward: h; backward: dx
+  float* out1;          // backward: dg
+  float* dh0;           // backward: [nseg][rows] or null
+  const int32_t* cu;    // cu_seqlens or null
+  int32_t nseg;
+  int32_t rev;          // processing order runs from high t to low t
+  int64_t rows, T, stride;
+  int32_t ntiles;       // tiles per row (set by the launcher)
+  void* ws;             // workspace (only used when ntiles > 1)
+};
+
+// Elements per tile of the scalar kernels, and tiles per row for a given T.
+int64_t scalar_tile_elems(int in_dtype);
+int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile);
+int scalar_vec(int in_dtype);
+hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
+
+// Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so
+// callers may capture it in a graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
+
+// Workspace header bytes (control words) ahead of the per-tile descriptors.
+constexpr size_t kWsHeaderBytes = 128;
+
+}  // namespace mscan

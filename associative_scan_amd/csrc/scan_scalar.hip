@@ -1,0 +1,531 @@
+// Scalar affine scan kernels: forward h_t = g_t h_{t-1} + x_t and its adjoint.
+//
+// Forward: associative-scan-triton README, intro / quick start (the recurrence)
+// and "how it works" (chunked scan with the running prefix carried across
+// chunks, cu_seqlens packing, bidirectional branches).
+// Backward: same README, "how it works" (d_tokens is a reverse scan on shifted
+// gates; d_gates = shifted states * d_tokens), fused into one kernel that reads
+// only the forward's inputs and outputs ("Triton scan kernels", "Autograd
+// integration and the reversed-scan backward").
+//
+// Both directions are the same affine scan run along a "processing order":
+//   forward : element (a, b) = (g_t, x_t), order = time (reversed if reverse),
+//             a sequence's first element becomes (0, g h0 + x);
+//   backward: element (a, b) = (g of the previous element in the backward's
+//             order, dy_t), order = opposite of the forward's, a sequence's
+//             first element becomes (0, dy); outputs dx = lam,
+//             dg = lam * (forward state before t, h0 at the sequence start),
+//             dh0 = g * lam at the forward's first element of each sequence.
+//
+// Work decomposition (one workgroup = one tile of one row):
+//   tile   = WAVES waves x SUBS sub-chunks x 64 lanes x EL elements (contiguous
+//            in memory; lanes of a sub-chunk read consecutive 16-byte vectors),
+//   a lane = EL consecutive elements, summarised serially into (P, Q),
+//   a wave = SUBS independent 64-lane DPP scans chained through lane 63,
+//   waves  = chained through LDS,
+//   tiles of one row = chained by decoupled look-back through the workspace
+//            (only when a row needs more than one tile).
+// Rows whose start is not 16-byte aligned are handled by aligning vector
+// groups to absolute addresses and masking the elements outside the row.
+#include "mscan_device.hpp"
+#include "mscan_launch.hpp"
+
+namespace mscan {
+
+// ---------------------------------------------------------------------------
+// input element types
+// ---------------------------------------------------------------------------
+template <typename Tin>
+struct InTraits;
+
+template <>
+struct InTraits<float> {
+  static constexpr int VEC = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ void load16(const float* p, float* o) {
+    const v4f v = *(const v4f*)p;
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+};
+
+template <>
+struct InTraits<uint16_t> {  // bf16 bit patterns, widened exactly
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ void load16(const uint16_t* p, float* o) {
+    const v4u v = *(const v4u*)p;
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
+    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ float load1(const uint16_t* p) {
+    return __uint_as_float((uint32_t)(*p) << 16);
+  }
+};
+
+// N consecutive elements starting at a 16-byte aligned address
+template <typename T, int N>
+__device__ __forceinline__ void load_span(const T* p, float (&o)[N]) {
+  constexpr int V = InTraits<T>::VEC;
+#pragma unroll
+  for (int i = 0; i < N / V; ++i) InTraits<T>::load16(p + i * V, o + i * V);
+}
+
+template <int N>
+__device__ __forceinline__ void store_span(float* p, const float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const v4f t = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+    __builtin_nontemporal_store(t, (v4f*)(p + 4 * i));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cu_seqlens helpers
+// ---------------------------------------------------------------------------
+// Number of entries of the sorted array cu[0..n) that are <= key, by a 64-way
+// wave-parallel search (every lane returns the same value).
+__device__ __forceinline__ int wave_count_le(const int32_t* cu, int n, int64_t key) {
+  const int l = lane_id();
+  int lo = 0;
+  while (n > 64) {
+    const int step = (n + 63) / 64;
+    const int idx = lo + l * step;
+    const bool le = (idx < lo + n) && ((int64_t)cu[idx] <= key);
+    const int cnt = __popcll(__ballot(le));
+    if (cnt == 0) return lo;
+    const int nlo = lo + (cnt - 1) * step + 1;
+    const int hi = min(lo + cnt * step, lo + n);
+    n = hi - nlo;
+    lo = nlo;
+    if (n <= 0) return lo;
+  }
+  const bool le = (l < n) && ((int64_t)cu[lo + l] <= key);
+  return lo + __popcll(__ballot(le));
+}
+
+constexpr int kCuSlice = 1024;  // cu_seqlens entries cached in LDS per tile
+
+struct SegSlice {
+  const int32_t* v;  // slice values (LDS or global)
+  int n;             // entries
+  int k0;            // absolute index of v[0]
+};
+
+// Largest i in [0, n) with v[i] <= q (0 if none).
+__device__ __forceinline__ int slice_find(const SegSlice& s, int64_t q) {
+  int lo = 0, hi = s.n;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)s.v[mid] <= q) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <typename Tin, bool BWD, int WAVES, int SUBS, int GPL, bool VARLEN, bool MULTI>
+__global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
+  constexpr int VEC = InTraits<Tin>::VEC;
+  constexpr int EL = VEC * GPL;          // elements per lane per sub-chunk
+  constexpr int WREG = SUBS * 64 * EL;   // elements per wave
+  constexpr int TILE = WAVES * WREG;     // elements per tile
+  static_assert(EL <= 16, "per-lane span too long");
+
+  __shared__ float s_aggP[WAVES], s_aggQ[WAVES];
+  __shared__ float s_carry;
+  __shared__ uint32_t s_tile, s_epoch;
+  __shared__ int32_t s_cu[VARLEN ? kCuSlice : 1];
+  __shared__ int32_t s_cu_n, s_cu_k0;
+
+  const int l = lane_id();
+  const int w = (int)(threadIdx.x >> 6);
+
+  Workspace ws{};
+  uint32_t tile, epoch = 0;
+  if constexpr (MULTI) {
+    ws = ws_view(a.ws);
+    if (threadIdx.x == 0) {
+      s_tile = __hip_atomic_fetch_add(ws.hdr + kHdrTileCtr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_epoch = ld_u32(ws.hdr + kHdrEpoch);
+    }
+    __syncthreads();
+    tile = s_tile;
+    epoch = s_epoch;
+  } else {
+    tile = blockIdx.x;
+  }
+  if constexpr (MULTI) {
+    // a tile id past the grid means the workspace was not re-armed (not zeroed
+    // before first use): flag it and touch nothing
+    if (tile >= gridDim.x) {
+      if (threadIdx.x == 0) {
+        st_u32(ws.hdr + kHdrError, 2u);
+        ws_finish(ws, gridDim.x, epoch);
+      }
+      return;
+    }
+  }
+  const int64_t r = tile / (uint32_t)a.ntiles;
+  const int c = (int)(tile - (uint32_t)r * (uint32_t)a.ntiles);
+  const int64_t T = a.T;
+  const int64_t rowoff = r * a.stride;
+  const int lead = (int)(rowoff % VEC);
+  const int64_t urow = ((T - 1 + lead) / VEC + 1) * VEC;  // padded row length
+  const bool rev = a.rev != 0;
+  const int64_t jt0 = (int64_t)c * TILE;
+  const int64_t ut_lo = rev ? urow - jt0 - TILE : jt0;     // tile span in padded coords
+  const bool interior = (ut_lo >= lead) && (ut_lo + TILE <= lead + T);
+  const int64_t base = rowoff - lead;                       // element index of padded u = 0
+
+  const Tin* gp = (const Tin*)a.g;
+
+  // padded coordinate of the lowest element of (sub-chunk s) for this lane
+  auto span_lo = [&](int s) -> int64_t {
+    const int64_t j0 = jt0 + (int64_t)w * WREG + (int64_t)s * 64 * EL + (int64_t)l * EL;
+    return rev ? urow - j0 - EL : j0;
+  };
+
+  // ---- cu_seqlens slice covering this tile ------------------------------
+  SegSlice seg{nullptr, 0, 0};
+  if constexpr (VARLEN) {
+    const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
+    if (w == 0) {
+      int ka = 0, n = 0;
+      if (plo < phi) {
+        ka = max(wave_count_le(a.cu, a.nseg + 1, plo) - 1, 0);
+        const int kb = min(wave_count_le(a.cu, a.nseg + 1, phi - 1), a.nseg);
+        n = max(kb - ka + 1, 1);
+      }
+      if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
+    }
+    __syncthreads();
+    const int n = s_cu_n, k0 = s_cu_k0;
+    if (n <= kCuSlice) {
+      for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
+      __syncthreads();
+      seg = SegSlice{s_cu, n, k0};
+    } else {
+      seg = SegSlice{a.cu + k0, n, k0};
+    }
+  }
+
+  // ---- load -------------------------------------------------------------
+  // processing-order registers: A = transition, B = injection
+  float A[SUBS][EL], B[SUBS][EL];
+  float G[BWD ? SUBS : 1][EL], N[BWD ? SUBS : 1][EL];  // bwd: own gate, next forward state
+  {
+    float t0[EL], t1[EL], t2[EL];
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      const int64_t u0 = span_lo(s);
+      if (interior) {
+        load_span<Tin, EL>(gp + base + u0, t0);
+        if constexpr (!BWD) {
+          load_span<Tin, EL>((const Tin*)a.b + base + u0, t1);
+        } else {
+          load_span<float, EL>((const float*)a.b + base + u0, t1);
+          load_span<float, EL>(a.hs + base + u0, t2);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          const int64_t t = u0 + e - lead;
+          const bool ok = (t >= 0) && (t < T);
+          t0[e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : 1.f;
+          if constexpr (!BWD) {
+            t1[e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : 0.f;
+          } else {
+            t1[e] = ok ? ((const float*)a.b)[rowoff + t] : 0.f;
+            t2[e] = ok ? a.hs[rowoff + t] : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int p = rev ? EL - 1 - e : e;  // physical component of processing element e
+        if constexpr (!BWD) {
+          A[s][e] = t0[p];
+          B[s][e] = t1[p];
+        } else {
+          G[s][e] = t0[p];
+          B[s][e] = t1[p];
+          N[s][e] = t2[p];
+        }
+      }
+    }
+  }
+
+  // ---- backward: shift gates forward and states backward by one element
+  if constexpr (BWD) {
+    // physical position of processing element j of this row (padded coords)
+    auto u_of = [&](int64_t j) -> int64_t { return rev ? urow - 1 - j : j; };
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      float gprev = __shfl_up(G[s][EL - 1], 1, 64);
+      float hnext = __shfl_down(N[s][0], 1, 64);
+      if (s > 0) {
+        const float gl = readlane_f(G[s - 1][EL - 1], 63);
+        if (l == 0) gprev = gl;
+      } else if (l == 0) {
+        const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
+        const int64_t t = u_of(j) - lead;
+        gprev = (j >= 0 && t >= 0 && t < T) ? InTraits<Tin>::load1(gp + rowoff + t) : 0.f;
+      }
+      if (s + 1 < SUBS) {
+        const float hn = readlane_f(N[s + 1][0], 0);
+        if (l == 63) hnext = hn;
+      } else if (l == 63) {
+        const int64_t j = jt0 + (int64_t)(w + 1) * WREG;  // element after this wave's span
+        const int64_t t = u_of(j) - lead;
+        hnext = (t >= 0 && t < T) ? a.hs[rowoff + t] : 0.f;
+      }
+#pragma unroll
+      for (int e = EL - 1; e > 0; --e) A[s][e] = G[s][e - 1];
+      A[s][0] = gprev;
+#pragma unroll
+      for (int e = 0; e < EL - 1; ++e) N[s][e] = N[s][e + 1];
+      N[s][EL - 1] = hnext;
+    }
+  }
+
+  // ---- sequence boundaries ------------------------------------------------
+  // first: a sequence's first element in processing order; last: its last.
+  uint32_t lastmask[BWD ? SUBS : 1];
+  const float* h0p = a.h0;
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) {
+    const int64_t u0 = span_lo(s);
+    uint32_t lm = 0;
+    if constexpr (!VARLEN) {
+      // one sequence per row: first / last are the row's ends
+      const int64_t tf = rev ? T - 1 : 0, tl = rev ? 0 : T - 1;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int64_t t = u0 + (rev ? EL - 1 - e : e) - lead;
+        if (t == tf) {
+          const float hv = h0p ? h0p[r] : 0.f;
+          if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
+          A[s][e] = 0.f;
+        }
+        if constexpr (BWD) {
+          if (t == tl) {
+            N[s][e] = h0p ? h0p[r] : 0.f;
+            lm |= 1u << e;
+          }
+        }
+      }
+    } else {
+      // walk the elements in physical order against the cu slice
+      const int64_t q0 = u0 - lead;
+      if (seg.n > 0) {
+        int k = slice_find(seg, max(q0, (int64_t)0));
+#pragma unroll
+        for (int ep = 0; ep < EL; ++ep) {
+          const int64_t q = q0 + ep;
+          if (q < 0 || q >= T) continue;
+          while (k + 1 < seg.n && (int64_t)seg.v[k + 1] <= q) ++k;
+          const bool is_start = (int64_t)seg.v[k] == q;
+          const bool is_end = (k + 1 < seg.n) && ((int64_t)seg.v[k + 1] - 1 == q);
+          const int sk = min(max(seg.k0 + k, 0), a.nseg - 1);
+          const int e = rev ? EL - 1 - ep : ep;
+          const bool first = rev ? is_end : is_start;
+          const bool last = rev ? is_start : is_end;
+          const float hv = (h0p && (first || last)) ? h0p[(int64_t)sk * a.rows + r] : 0.f;
+          if (first) {
+            if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
+            A[s][e] = 0.f;
+          }
+          if constexpr (BWD) {
+            if (last) {
+              N[s][e] = hv;
+              lm |= 1u << e;
+            }
+          }
+        }
+      }
+    }
+    if constexpr (BWD) lastmask[s] = lm;
+  }
+
+  // ---- lane-serial summaries and wave scans ---------------------------
+  float P[SUBS], Q[SUBS];
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) {
+    float p = 1.f, q = 0.f;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const bool use = A[s][e] != 0.f;
+      q = use ? __builtin_fmaf(A[s][e], q, B[s][e]) : B[s][e];
+      p = use ? A[s][e] * p : 0.f;
+    }
+    P[s] = p;
+    Q[s] = q;
+  }
+  {
+    // step-major so the SUBS independent scans interleave
+    const bool v1 = (l & 15) >= 1, v2 = (l & 15) >= 2, v4 = (l & 15) >= 4, v8 = (l & 15) >= 8;
+    const bool v16 = (l & 16) != 0, v32 = l >= 32;
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr1, 0xf>(P[s], Q[s], v1);
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr2, 0xf>(P[s], Q[s], v2);
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr4, 0xf>(P[s], Q[s], v4);
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr8, 0xf>(P[s], Q[s], v8);
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast15, 0xa>(P[s], Q[s], v16);
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast31, 0xc>(P[s], Q[s], v32);
+  }
+  // wave aggregate = sub-chunk totals (lane 63) in order
+  float wP = 1.f, wQ = 0.f;
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) {
+    float sp = readlane_f(P[s], 63), sq = readlane_f(Q[s], 63);
+    lin_compose(wP, wQ, sp, sq);  // (waves so far, then sub-chunk s)
+    wP = sp;
+    wQ = sq;
+  }
+
+  // ---- across waves --------------------------------------------------------
+  float exP = 1.f, exQ = 0.f;     // composition of the waves before this one
+  float tP = wP, tQ = wQ;         // tile aggregate
+  if constexpr (WAVES > 1) {
+    if (l == 0) { s_aggP[w] = wP; s_aggQ[w] = wQ; }
+    __syncthreads();
+    tP = 1.f; tQ = 0.f;
+#pragma unroll
+    for (int i = 0; i < WAVES; ++i) {
+      if (i == w) { exP = tP; exQ = tQ; }
+      float p = s_aggP[i], q = s_aggQ[i];
+      lin_compose(tP, tQ, p, q);
+      tP = p;
+      tQ = q;
+    }
+  }
+
+  // ---- across tiles: decoupled look-back ------------------------------------
+  float carry = 0.f;
+  if constexpr (MULTI) {
+    uint64_t* rd = ws.desc + (int64_t)3 * ((int64_t)r * a.ntiles);
+    if (w == 0) {
+      const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+      if (l == 0) {
+        if (tP != 0.f) {
+          st_u64(rd + 3 * c, pack_word(tagA, tP));
+          st_u64(rd + 3 * c + 1, pack_word(tagA, tQ));
+        } else {
+          st_u64(rd + 3 * c + 2, pack_word(tagI, tQ));
+        }
+      }
+      if (c > 0) carry = lin_lookback(ws, rd, c, epoch);
+      if (l == 0) {
+        if (tP != 0.f) st_u64(rd + 3 * c + 2, pack_word(tagI, lin_apply(tP, tQ, carry)));
+        s_carry = carry;
+      }
+    }
+    __syncthreads();
+    carry = s_carry;
+  }
+
+  // ---- apply: every element from its exact carry-in ---------------------------
+  float hs = lin_apply(exP, exQ, carry);  // state entering this wave's span
+  float O[SUBS][EL];
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) {
+    const float v = lin_apply(P[s], Q[s], hs);  // state after this lane
+    float st = __shfl_up(v, 1, 64);
+    if (l == 0) st = hs;
+    hs = readlane_f(v, 63);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const bool use = A[s][e] != 0.f;
+      st = use ? __builtin_fmaf(A[s][e], st, B[s][e]) : B[s][e];
+      O[s][e] = st;
+    }
+  }
+
+  // ---- store -------------------------------------------------------------
+#pragma unroll
+  for (int s = 0; s < SUBS; ++s) {
+    const int64_t u0 = span_lo(s);
+    float o0[EL], o1[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      const int p = rev ? EL - 1 - e : e;
+      o0[p] = O[s][e];
+      if constexpr (BWD) o1[p] = O[s][e] * N[s][e];
+    }
+    if (interior) {
+      store_span<EL>(a.out0 + base + u0, o0);
+      if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int64_t t = u0 + e - lead;
+        if (t >= 0 && t < T) {
+          a.out0[rowoff + t] = o0[e];
+          if constexpr (BWD) a.out1[rowoff + t] = o1[e];
+        }
+      }
+    }
+    if constexpr (BWD) {
+      // dh0 = g * lam at each sequence's forward-first element
+      if (a.dh0 && lastmask[s]) {
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          if (!(lastmask[s] & (1u << e))) continue;
+          const int64_t t = u0 + (rev ? EL - 1 - e : e) - lead;
+          int sk = 0;
+          if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
+          a.dh0[(int64_t)sk * a.rows + r] = G[s][e] * O[s][e];
+        }
+      }
+    }
+  }
+
+  if constexpr (MULTI) {
+    if (threadIdx.x == 0) ws_finish(ws, gridDim.x, epoch);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host launch
+// ---------------------------------------------------------------------------
+template <typename Tin, bool BWD, int WAVES, int SUBS, int GPL>
+static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
+  constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
+  ScalarArgs a = a0;
+  a.ntiles = (int32_t)scalar_tiles(a.T, a.stride, InTraits<Tin>::VEC, TILE);
+  const uint64_t nblocks = (uint64_t)a.rows * (uint64_t)a.ntiles;
+  const bool multi = a.ntiles > 1, varlen = a.cu != nullptr;
+  dim3 grid((unsigned)nblocks), block(WAVES * 64);
+  if (!multi && !varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, false, false>), grid, block, 0, st, a);
+  else if (!multi && varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, true, false>), grid, block, 0, st, a);
+  else if (multi && !varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, false, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, true, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// Tile shape per input type: 4 waves x 4096 elements per tile.
+int64_t scalar_tile_elems(int in_dtype) { return in_dtype == 0 ? 4 * 4 * 64 * 4 : 4 * 2 * 64 * 8; }
+int scalar_vec(int in_dtype) { return in_dtype == 0 ? 4 : 8; }
+
+int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
+  // padded row length: rows all start aligned when the stride is a multiple of
+  // the vector width; otherwise allow for the worst misalignment
+  const int64_t umax = (stride % vec == 0) ? (T + vec - 1) / vec * vec : ((T - 1 + vec - 1) / vec + 1) * vec;
+  return (umax + tile - 1) / tile;
+}
+
+hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
+  if (in_dtype == 0) {
+    return bwd ? launch_cfg<float, true, 4, 4, 1>(a, st) : launch_cfg<float, false, 4, 4, 1>(a, st);
+  }
+  return bwd ? launch_cfg<uint16_t, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, false, 4, 2, 1>(a, st);
+}
+
+}  // namespace mscan

@@ -1,0 +1,176 @@
+/*
+ * mscan.h -- C ABI of libmscan, the MI355X (gfx950) affine associative scan.
+ *
+ * The library computes first-order affine recurrences h_t = a_t * h_{t-1} + b_t
+ * along the last (time) axis of row-major [rows][T] arrays, one independent
+ * recurrence per row and per packed sequence, with hand-written HIP kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Pointers.   Every array argument is a DEVICE pointer on the current HIP
+ *              device. Base pointers must be 16-byte aligned. Outputs must not
+ *              alias inputs. The caller owns every buffer, the workspace too;
+ *              the library never allocates, frees or synchronises.
+ *  Stream.     `stream` is a hipStream_t passed as void* (NULL = the null
+ *              stream). Calls only enqueue work on it and return at once.
+ *  Layout.     Element (r, t) of a scalar array sits at r*row_stride + t
+ *              (elements). Matrix arrays hold a row-major k x k (transition) or
+ *              k x v (injection / state) block per (r, t), with row_stride
+ *              counted in time steps. Every array of one call shares rows, T
+ *              and row_stride.
+ *  Segments.   cu_seqlens (device, int32, nseg+1 entries, nondecreasing,
+ *              cu[0] = 0, cu[nseg] = T) splits the time axis of every row into
+ *              independent sequences, as in the flash-attn convention the
+ *              associative-scan-triton README uses for packing ("how it works":
+ *              each sequence is scanned on its own, no cross-document
+ *              leakage). NULL means one sequence [0, T) and nseg must be 1.
+ *              Empty sequences are allowed and do nothing. Sequence starts are
+ *              hard boundaries: nothing, not even NaN, crosses them. The
+ *              kernels do not validate the device contents of cu_seqlens;
+ *              malformed offsets give unspecified values but every memory
+ *              access stays inside the arrays described above.
+ *  h0.         Optional initial state per (sequence, row): [nseg][rows] for
+ *              scalars, [nseg][rows][k][v] for matrices; NULL means zero. The
+ *              first step of a sequence multiplies it by its own transition:
+ *              h_s = a_s * h0 + b_s ("Our RG-LRU GPU audit", "Strengthened
+ *              fused path": nonzero initial state and its gradient).
+ *  reverse.    0: causal, h_t = a_t h_{t-1} + b_t. 1: every sequence runs from
+ *              its last element to its first, h_t = a_t h_{t+1} + b_t, with h0
+ *              entering at the last element (the second, opposite-direction
+ *              branch of the README's bidirectional scan).
+ *  Precision.  Inputs are fp32 or bf16; bf16 is widened exactly. All
+ *              accumulation and every output is fp32 ("Triton scan kernels",
+ *              "Kernel design": accumulation is fp32 regardless of input
+ *              dtype).
+ *  Workspace.  Calls that split a row into several tiles chain them through a
+ *              small device workspace of mscan_workspace_bytes() bytes. It must
+ *              be zero-filled (mscan_workspace_init) once before its first
+ *              use; every call leaves it ready for the next. Calls that overlap
+ *              in time (different streams) must not share a workspace.
+ *  Errors.     Arguments are validated on the host before any HIP call:
+ *              MSCAN_ERR_INVALID (null required pointer, bad sizes, misaligned
+ *              pointer, nseg inconsistent with cu_seqlens), MSCAN_ERR_UNSUPPORTED
+ *              (dtype or matrix shape outside the supported envelope; never
+ *              silently masked, as the minGRU page's kernel envelope raises
+ *              rather than miscomputes), MSCAN_ERR_WORKSPACE (ws_bytes too
+ *              small), MSCAN_ERR_HIP (a launch failed; mscan_last_hip_error()
+ *              gives the HIP error text). Nothing is enqueued on any error.
+ *              There is no fallback path.
+ */
+#ifndef MSCAN_H_
+#define MSCAN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSCAN_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MSCAN_API __attribute__((visibility("default")))
+#else
+#define MSCAN_API
+#endif
+
+typedef enum {
+  MSCAN_OK = 0,
+  MSCAN_ERR_INVALID = 1,
+  MSCAN_ERR_UNSUPPORTED = 2,
+  MSCAN_ERR_WORKSPACE = 3,
+  MSCAN_ERR_HIP = 4
+} mscan_status;
+
+typedef enum { MSCAN_F32 = 0, MSCAN_BF16 = 1 } mscan_dtype;
+
+/* Which computation a workspace is sized for. */
+typedef enum {
+  MSCAN_OP_SCAN_FWD = 0,
+  MSCAN_OP_SCAN_BWD = 1,
+  MSCAN_OP_SCAN_LOG_FWD = 2,
+  MSCAN_OP_MATRIX_FWD = 3,
+  MSCAN_OP_MATRIX_BWD = 4
+} mscan_op;
+
+typedef struct {
+  int64_t rows;               /* independent rows (e.g. B*C), >= 1                       */
+  int64_t T;                  /* time steps per row (packed tokens for varlen), >= 1    */
+  int64_t row_stride;         /* elements (steps for matrices) between rows, >= T       */
+  const int32_t* cu_seqlens;  /* device, nseg+1 offsets; NULL = one sequence            */
+  int32_t nseg;               /* number of sequences (1 when cu_seqlens is NULL)        */
+  int32_t reverse;            /* 0 causal, 1 reverse-in-time                            */
+} mscan_problem;
+
+/* Workspace bytes `op` needs for `prob` (k, v are ignored for scalar ops).
+ * Pure host function; returns 0 when the problem is invalid. */
+MSCAN_API size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v);
+
+/* Zero-fill a workspace before its first use (enqueues one small fill kernel). */
+MSCAN_API mscan_status mscan_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Scalar forward scan (associative-scan-triton README, intro and quick start:
+ * h[t] = g[t] * h[t-1] + x[t]; "how it works": chunked scan with a running
+ * prefix carried across chunks).
+ *   g, x : [rows][T] of in_dtype (MSCAN_F32 or MSCAN_BF16), read only.
+ *   h0   : fp32 [nseg][rows] or NULL.
+ *   h    : fp32 [rows][T], written.                                          */
+MSCAN_API mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
+                      const float* h0, float* h, void* ws, size_t ws_bytes, void* stream);
+
+/* Scalar backward: adjoint of scan_fwd given its output h (README, "how it
+ * works": d_tokens is a reverse scan on shifted gates and d_gates = shifted
+ * states * d_tokens; the fused kernel reads only the forward's inputs and
+ * outputs, as the minGRU page's reversed-scan backward does).
+ *   causal : lam_t = dy_t + g_{t+1} lam_{t+1} (no g past a sequence end),
+ *            dx_t = lam_t, dg_t = lam_t h_{t-1} (h0 before a sequence start),
+ *            dh0 = g_s lam_s at each sequence start s.
+ *   reverse: the mirror image (g_{t-1}, h_{t+1}, dh0 at the last element).
+ *   g    : [rows][T] of in_dtype; h, dy : fp32 [rows][T]; h0 : fp32 or NULL.
+ *   dx, dg : fp32 [rows][T], written. dh0 : fp32 [nseg][rows] or NULL;
+ *   an empty sequence gets dh0 = 0.                                          */
+MSCAN_API mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, const float* h,
+                      const float* dy, const float* h0, float* dx, float* dg, float* dh0,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Log-space forward ("Triton scan kernels", "One associative-scan family":
+ * parallel_scan_log carries h_t = a_t h_{t-1} + b_t in log space, a running
+ * log-coefficient sum plus a max-shifted log-sum-exp, and writes h = exp(.)).
+ *   log_a, log_b : fp32 [rows][T]; log_a = -inf (a = 0) is a reset.
+ *   log_h0 : fp32 [nseg][rows] or NULL (h0 = 0).
+ *   h : fp32 [rows][T] = exp(log h_t), written.                               */
+MSCAN_API mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
+                          const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream);
+
+/* Matrix-affine forward ("Triton scan kernels", "One associative-scan family":
+ * h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t k x v; matrix_scan is
+ * k=2, v=1 and matrix_affine_scan is generic (k, v)). Supported: (k, v) in
+ * {(1,1), (2,1), (2,2), (4,1), (4,4)}; others return MSCAN_ERR_UNSUPPORTED.
+ *   A : fp32 [rows][T][k][k]; B : fp32 [rows][T][k][v];
+ *   h0 : fp32 [nseg][rows][k][v] or NULL; h : fp32 [rows][T][k][v], written. */
+MSCAN_API mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,
+                                    const float* B, const float* h0, float* h, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/* Matrix-affine backward (same page, "Autograd integration and the
+ * reversed-scan backward": reverse-scan the output gradients with A_{t+1}^T and
+ * form dA_t from the previous forward state).
+ *   causal : lam_t = dy_t + A_{t+1}^T lam_{t+1}, dB_t = lam_t,
+ *            dA_t = lam_t h_{t-1}^T (h0 before a sequence start),
+ *            dh0 = A_s^T lam_s.   reverse: the mirror image.
+ *   A : [rows][T][k][k]; h, dy : [rows][T][k][v]; h0 : [nseg][rows][k][v] or NULL.
+ *   dA, dB written; dh0 : [nseg][rows][k][v] or NULL.                        */
+MSCAN_API mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, const float* A,
+                                    const float* h, const float* dy, const float* h0, float* dA,
+                                    float* dB, float* dh0, void* ws, size_t ws_bytes, void* stream);
+
+MSCAN_API const char* mscan_status_string(int status);
+/* Text of the last HIP error this thread saw inside the library ("" if none). */
+MSCAN_API const char* mscan_last_hip_error(void);
+MSCAN_API int mscan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSCAN_H_ */

@@ -1,0 +1,290 @@
+"""GPU parity of the scalar scan (scan_fwd / scan_bwd) against the fp64 oracle.
+
+Tolerances (per element, every output): |gpu - ref| <= tau * (1 + |ref|) with
+tau = 2e-5 for forward states and 1e-4 for gradients; bf16 inputs reach the
+oracle already rounded (exact widening). Exact-mode inputs (integer data whose
+scan is exact in any association order) must match bit for bit, which pins the
+indexing: sequence boundaries, resets, direction, shifts and tile seams.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+
+pytestmark = pytest.mark.gpu
+
+TAU_FWD, TAU_BWD = 2e-5, 1e-4
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import associative_scan_amd as m
+    return m
+
+
+def _t(a, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def _bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def close(gpu, ref, tau, what):
+    g = gpu.detach().cpu().double().numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref) / (1.0 + np.abs(ref))
+    i = int(np.argmax(err)) if err.size else 0
+    assert err.size == 0 or err.flat[i] <= tau, f"{what}: max rel err {err.flat[i]:.3e} at {np.unravel_index(i, err.shape)} (gpu {g.flat[i]!r}, ref {ref.flat[i]!r})"
+
+
+def exact(gpu, ref, what):
+    g = gpu.detach().cpu().double().numpy()
+    ref = np.asarray(ref, np.float64)
+    bad = np.nonzero(g != ref)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} mismatches, first at {tuple(b[0] for b in bad)}: gpu {g[tuple(b[0] for b in bad)]} ref {ref[tuple(b[0] for b in bad)]}"
+
+
+def run_case(m, o, g, x, dy, h0=None, cu=None, reverse=False, bits=None, check=close):
+    """Forward and backward on the GPU vs the oracle; g, x, dy numpy fp32 [rows, T]."""
+    cu_t = None if cu is None else _t(cu, torch.int32)
+    h0_t = None if h0 is None else _t(h0)
+    if bits is None:
+        gg, xx = _t(g), _t(x)
+    else:
+        gg, xx = _bf16(bits[0]), _bf16(bits[1])
+    h = m.scan_fwd(gg, xx, h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    href = o.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+    if check is close:
+        close(h, href, TAU_FWD, "h")
+    else:
+        exact(h, href, "h")
+    dx, dg, dh0 = m.scan_bwd(gg, h, _t(dy), h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    rx, rg, rh0 = o.scan_bwd(g, href, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    if check is close:
+        close(dx, rx, TAU_BWD, "dx")
+        close(dg, rg, TAU_BWD, "dg")
+        close(dh0, rh0, TAU_BWD, "dh0")
+    else:
+        exact(dx, rx, "dx")
+        exact(dg, rg, "dg")
+        exact(dh0, rh0, "dh0")
+    return h
+
+
+# ---------------------------------------------------------------------------
+# the README quick-start workload (C=4, T=128, one sequence)
+# ---------------------------------------------------------------------------
+def test_quickstart(m, oracle_lib):
+    d = gen.quickstart()
+    run_case(m, oracle_lib, d["g"], d["x"], d["dy"])
+    # the same problem stated with cu_seqlens = [0, T] runs the packed kernels
+    run_case(m, oracle_lib, d["g"], d["x"], d["dy"], cu=d["cu_seqlens"])
+
+
+# ---------------------------------------------------------------------------
+# dense rows: lengths around the vector width and the 4096-element tile
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 63, 127, 1000, 4095, 4096, 4097, 8192, 9001, 20000])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_dense_lengths(m, oracle_lib, T, reverse):
+    r = np.random.default_rng(T * 2 + reverse)
+    rows = 5
+    g = r.uniform(0, 1, (rows, T)).astype(np.float32)
+    x = r.standard_normal((rows, T)).astype(np.float32)
+    dy = r.standard_normal((rows, T)).astype(np.float32)
+    h0 = r.standard_normal(rows).astype(np.float32)
+    run_case(m, oracle_lib, g, x, dy, h0=h0, reverse=reverse)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_exact_mode_dense(m, oracle_lib, reverse):
+    r = np.random.default_rng(11 + reverse)
+    g, x, dy = gen.exact_mode(r, (6, 30000))
+    h0 = r.integers(-1, 2, 6).astype(np.float32)
+    run_case(m, oracle_lib, g, x, dy, h0=h0, reverse=reverse, check=exact)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("nseg", [1, 2, 7, 40, 300])
+def test_exact_mode_varlen(m, oracle_lib, reverse, nseg):
+    r = np.random.default_rng(100 + nseg + reverse)
+    T = 25000
+    g, x, dy = gen.exact_mode(r, (3, T))
+    cu = gen.segments_random(r, T, nseg, allow_empty=True)
+    h0 = r.integers(-1, 2, (nseg, 3)).astype(np.float32)
+    run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=reverse, check=exact)
+
+
+def test_length_one_sequences(m, oracle_lib):
+    """Every element its own sequence (more sequences than the tile caches in LDS)."""
+    r = np.random.default_rng(5)
+    T = 6000
+    g = r.uniform(0, 1, (2, T)).astype(np.float32)
+    x = r.standard_normal((2, T)).astype(np.float32)
+    dy = r.standard_normal((2, T)).astype(np.float32)
+    cu = np.arange(T + 1, dtype=np.int32)
+    h0 = r.standard_normal((T, 2)).astype(np.float32)
+    for rev in (False, True):
+        run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev)
+
+
+def test_empty_sequences_everywhere(m, oracle_lib):
+    r = np.random.default_rng(6)
+    T = 9000
+    g = r.uniform(0, 1, (2, T)).astype(np.float32)
+    x = r.standard_normal((2, T)).astype(np.float32)
+    dy = r.standard_normal((2, T)).astype(np.float32)
+    cu = np.array([0, 0, 0, 4096, 4096, 4097, 8999, 9000, 9000, 9000], dtype=np.int32)
+    h0 = r.standard_normal((len(cu) - 1, 2)).astype(np.float32)
+    for rev in (False, True):
+        run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev)
+
+
+def test_nan_poison_stays_in_its_sequence(m, oracle_lib):
+    """A sequence full of NaN/Inf changes nothing in any other sequence (bitwise)."""
+    r = np.random.default_rng(7)
+    T = 12000
+    g = r.uniform(0, 1, (3, T)).astype(np.float32)
+    x = r.standard_normal((3, T)).astype(np.float32)
+    dy = r.standard_normal((3, T)).astype(np.float32)
+    cu = np.array([0, 3000, 7000, 7001, 12000], dtype=np.int32)
+    gp, xp = g.copy(), x.copy()
+    gp[:, 3000:7000] = np.nan
+    xp[:, 3000:5000] = np.inf
+    cu_t = _t(cu, torch.int32)
+    for rev in (False, True):
+        h = m.scan_fwd(_t(g), _t(x), cu_seqlens=cu_t, reverse=rev)
+        hp = m.scan_fwd(_t(gp), _t(xp), cu_seqlens=cu_t, reverse=rev)
+        keep = np.r_[0:3000, 7000:12000]
+        assert torch.equal(h[:, keep], hp[:, keep])
+        d1 = m.scan_bwd(_t(g), h, _t(dy), cu_seqlens=cu_t, reverse=rev)
+        d2 = m.scan_bwd(_t(gp), hp, _t(dy), cu_seqlens=cu_t, reverse=rev)
+        for a, b in zip(d1[:2], d2[:2]):
+            assert torch.equal(a[:, keep], b[:, keep])
+        assert torch.equal(d1[2][[0, 2, 3]], d2[2][[0, 2, 3]])
+        close(h[:, keep], oracle_lib.scan_fwd(g, x, cu_seqlens=cu, reverse=rev)[:, keep], TAU_FWD, "h")
+
+
+@pytest.mark.parametrize("T,stride", [(1001, 1003), (4097, 4099), (8190, 8193), (5, 7)])
+def test_unaligned_rows(m, oracle_lib, T, stride):
+    """Rows that start at every alignment within a 16-byte vector (row_stride not a multiple of 4)."""
+    r = np.random.default_rng(T)
+    rows = 9
+    full_g = r.uniform(0, 1, (rows, stride)).astype(np.float32)
+    full_x = r.standard_normal((rows, stride)).astype(np.float32)
+    g, x = full_g[:, :T], full_x[:, :T]
+    h0 = r.standard_normal(rows).astype(np.float32)
+    gt, xt = _t(full_g)[:, :T], _t(full_x)[:, :T]
+    out = torch.full((rows, stride), 7.0, device=DEV)
+    for rev in (False, True):
+        h = m.scan_fwd(gt, xt, h0=_t(h0), reverse=rev, out=out[:, :T])
+        close(h, oracle_lib.scan_fwd(g, x, h0=h0, reverse=rev), TAU_FWD, "h")
+        assert torch.all(out[:, T:] == 7.0), "wrote outside the rows"
+
+
+def test_bf16_inputs(m, oracle_lib):
+    r = np.random.default_rng(8)
+    T = 15000
+    gb = gen.bf16_round(r.uniform(0, 1, (4, T)).astype(np.float32))
+    xb = gen.bf16_round(r.standard_normal((4, T)).astype(np.float32))
+    g, x = gen.bf16_bits_to_f32(gb).reshape(4, T), gen.bf16_bits_to_f32(xb).reshape(4, T)
+    dy = r.standard_normal((4, T)).astype(np.float32)
+    cu = gen.segments_random(r, T, 5)
+    h0 = r.standard_normal((5, 4)).astype(np.float32)
+    for rev in (False, True):
+        run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev, bits=(gb, xb))
+
+
+def test_workspace_reuse_across_calls(m, oracle_lib):
+    """Consecutive multi-tile calls of different sizes share one workspace."""
+    r = np.random.default_rng(9)
+    for T, rows in [(20000, 3), (9000, 11), (70000, 2), (4097, 40), (20000, 3)]:
+        g = r.uniform(0, 1, (rows, T)).astype(np.float32)
+        x = r.standard_normal((rows, T)).astype(np.float32)
+        for rev in (False, True):
+            h = m.scan_fwd(_t(g), _t(x), reverse=rev)
+            close(h, oracle_lib.scan_fwd(g, x, reverse=rev), TAU_FWD, f"h T={T}")
+
+
+def test_zero_gates_and_unit_gates(m):
+    r = np.random.default_rng(10)
+    x = r.standard_normal((3, 9000)).astype(np.float32)
+    h = m.scan_fwd(torch.zeros(3, 9000, device=DEV), _t(x))
+    assert torch.equal(h, _t(x))
+    dy = _t(r.standard_normal((3, 9000)).astype(np.float32))
+    dx, dg, _ = m.scan_bwd(torch.zeros(3, 9000, device=DEV), h, dy)
+    assert torch.equal(dx, dy)
+
+
+def test_autograd_wrappers(m, oracle_lib):
+    d = gen.quickstart()
+    g = _t(d["g"]).requires_grad_(True)
+    x = _t(d["x"]).requires_grad_(True)
+    h = m.scan_causal(g, x)
+    h.backward(_t(d["dy"]))
+    href = oracle_lib.scan_fwd(d["g"], d["x"])
+    rx, rg, _ = oracle_lib.scan_bwd(d["g"], href, d["dy"])
+    close(h, href, TAU_FWD, "h")
+    close(x.grad, rx, TAU_BWD, "dx")
+    close(g.grad, rg, TAU_BWD, "dg")
+    yf, yb = m.scan_bidirectional_branched(_t(d["g"]), _t(d["x"]), _t(d["g"]), _t(d["x"]))
+    close(yb, oracle_lib.scan_fwd(d["g"], d["x"], reverse=True), TAU_FWD, "h reverse")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the benchmark's launch configuration)
+# ---------------------------------------------------------------------------
+SAMPLE_ROWS = np.array([0, 1, 63, 64, 777, 1535, 1536, 4095, 6000, 9999, 12286, 12287])
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("T", [4096, 65536])
+def test_dense_full_size_sampled(m, oracle_lib, T):
+    """B=8, C=1536 dense workload, forward then backward on the full tensor;
+    the oracle checks a fixed sample of rows (whole rows at full T)."""
+    B, C = 8, 1536
+    full = gen.dense(B, C, T)
+    g, x, h0, dy = (_t(full[k]) for k in ("g", "x", "h0", "dy"))
+    del full
+    h = m.scan_fwd(g, x, h0=h0)
+    dx, dg, dh0 = m.scan_bwd(g, h, dy, h0=h0)
+    sub = gen.dense(B, C, T, rows=SAMPLE_ROWS)
+    href = oracle_lib.scan_fwd(sub["g"], sub["x"], h0=sub["h0"])
+    rx, rg, rh0 = oracle_lib.scan_bwd(sub["g"], href, sub["dy"], h0=sub["h0"])
+    idx = torch.as_tensor(SAMPLE_ROWS, device=DEV)
+    close(h.view(-1, T)[idx], href, TAU_FWD, "h")
+    close(dx.view(-1, T)[idx], rx, TAU_BWD, "dx")
+    close(dg.view(-1, T)[idx], rg, TAU_BWD, "dg")
+    close(dh0.view(-1)[idx], rh0.reshape(-1), TAU_BWD, "dh0")
+    assert torch.isfinite(h).all() and torch.isfinite(dg).all()
+
+
+@pytest.fixture(scope="module")
+def varlen_full():
+    return gen.varlen_bidir()
+
+
+@pytest.mark.timeout(400)
+def test_varlen_bidir_full(m, oracle_lib, varlen_full):
+    """C=1536, 65536 packed tokens in 16 sequences, bf16 inputs, both branches,
+    forward and backward, all elements checked."""
+    d = varlen_full
+    cu = d["cu_seqlens"]
+    cu_t = _t(cu, torch.int32)
+    for name in ("fwd", "bwd"):
+        b = d[name]
+        gg, xx = _bf16(b["g_bf16"]), _bf16(b["x_bf16"])
+        h = m.scan_fwd(gg, xx, cu_seqlens=cu_t, reverse=b["reverse"])
+        href = oracle_lib.scan_fwd(b["g"], b["x"], cu_seqlens=cu, reverse=b["reverse"])
+        close(h, href, TAU_FWD, f"{name} h")
+        dx, dg, dh0 = m.scan_bwd(gg, h, _t(b["dy"]), cu_seqlens=cu_t, reverse=b["reverse"])
+        rx, rg, rh0 = oracle_lib.scan_bwd(b["g"], href, b["dy"], cu_seqlens=cu, reverse=b["reverse"])
+        close(dx, rx, TAU_BWD, f"{name} dx")
+        close(dg, rg, TAU_BWD, f"{name} dg")
+        close(dh0, rh0, TAU_BWD, f"{name} dh0")

@@ -1,0 +1,105 @@
+"""Host-side checks of libmscan that need no GPU: the library loads, exports
+every entry point the header declares, sizes workspaces, and rejects bad
+arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mscan.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import associative_scan_amd as m
+    return m
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"MSCAN_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for n in ("scan_fwd", "scan_bwd", "scan_log_fwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
+              "mscan_workspace_bytes", "mscan_workspace_init", "mscan_status_string", "mscan_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(m):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", m.library_path], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(m.library_path)
+    for n in _declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_abi_and_status_strings(m):
+    assert m.lib.mscan_abi_version() == 1
+    for s in range(5):
+        assert m.lib.mscan_status_string(s)
+
+
+def _prob(m, rows=8, T=100, stride=None, cu=None, nseg=1, reverse=0):
+    return m.Problem(rows, T, T if stride is None else stride, cu, nseg, reverse)
+
+
+def test_workspace_sizes(m):
+    p = _prob(m, rows=12288, T=4096)
+    # one tile per row needs only the control header
+    assert m.workspace_bytes(p, m.OP_SCAN_FWD) == 128
+    p = _prob(m, rows=12288, T=65536)
+    # 16 tiles of 4096 per row, 3 descriptor words of 8 bytes per tile
+    assert m.workspace_bytes(p, m.OP_SCAN_FWD) == 128 + 12288 * 16 * 24
+    # rows that do not all start 16-byte aligned may need one more tile
+    p = _prob(m, rows=3, T=8190, stride=8193)
+    assert m.workspace_bytes(p, m.OP_SCAN_FWD) == 128 + 3 * 3 * 24
+    assert m.workspace_bytes(_prob(m, rows=0), m.OP_SCAN_FWD) == 0
+    assert m.workspace_bytes(_prob(m, T=10, stride=5), m.OP_SCAN_FWD) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("case", [
+    dict(rows=0), dict(T=0), dict(stride=50, T=100), dict(nseg=2), dict(reverse=2), dict(nseg=0),
+])
+def test_scan_fwd_rejects_bad_problem(m, case):
+    p = _prob(m, **case)
+    st = m.lib.scan_fwd(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, None, 0, None)
+    assert st == 1
+
+
+def test_scan_fwd_rejects_bad_pointers_and_dtypes(m):
+    p = _prob(m)
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, None, FAKE, None, FAKE, None, 0, None) == 1
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, FAKE + 4, FAKE, None, FAKE, None, 0, None) == 1   # misaligned
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE + 2, FAKE, None, 0, None) == 1   # h0 misaligned
+    assert m.lib.scan_fwd(ctypes.byref(p), 7, FAKE, FAKE, None, FAKE, None, 0, None) == 2       # dtype
+
+
+def test_scan_fwd_requires_workspace_for_long_rows(m):
+    p = _prob(m, rows=4, T=20000)
+    need = m.workspace_bytes(p, m.OP_SCAN_FWD)
+    assert need > 128
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, None, 0, None) == 3
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, FAKE, need - 8, None) == 3
+
+
+def test_scan_bwd_validation(m):
+    p = _prob(m)
+    assert m.lib.scan_bwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, None, FAKE, None, None, 0, None) == 1
+    assert m.lib.scan_bwd(ctypes.byref(p), 3, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == 2
+    assert m.lib.scan_bwd(ctypes.byref(p), 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE + 1, None, 0, None) == 1
+
+
+def test_null_problem(m):
+    st = m.lib.scan_fwd(None, 0, FAKE, FAKE, None, FAKE, None, 0, None)
+    assert st == 1

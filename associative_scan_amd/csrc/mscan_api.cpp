@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/mscan.h"
+#include "mscan_device.hpp"
 #include "mscan_launch.hpp"
 
 namespace {
@@ -38,13 +39,16 @@ int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
   return mscan::scalar_tiles(p->T, p->row_stride, mscan::scalar_vec(in_dtype), mscan::scalar_tile_elems(in_dtype));
 }
 
-// Workspace for either input type: header + 3 descriptor words per tile.
+// Workspace for either input type: header, then (only when rows are chained
+// by look-back) one epoch word per row and 3 descriptor words per tile.
 size_t scalar_ws_bytes(const mscan_problem* p) {
-  int64_t nt = scalar_tiles_for(p, MSCAN_F32);
-  const int64_t nb = scalar_tiles_for(p, MSCAN_BF16);
-  if (nb > nt) nt = nb;
-  if (nt <= 1) return mscan::kWsHeaderBytes;
-  return mscan::kWsHeaderBytes + (size_t)p->rows * (size_t)nt * 3u * sizeof(uint64_t);
+  int64_t nt = 0;
+  for (int dt = MSCAN_F32; dt <= MSCAN_BF16; ++dt) {
+    const int64_t n = scalar_tiles_for(p, dt);
+    if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
+  }
+  if (nt == 0) return mscan::kWsHeaderBytes;
+  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * 3u * sizeof(uint64_t);
 }
 
 mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
@@ -84,7 +88,8 @@ mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, co
   if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (nt > 1 && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob))) return MSCAN_ERR_WORKSPACE;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob)))
+    return MSCAN_ERR_WORKSPACE;
   mscan::ScalarArgs a{};
   a.g = g;
   a.b = x;
@@ -112,7 +117,8 @@ mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, co
   if ((h0 && ((uintptr_t)h0 & 3u)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (nt > 1 && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob))) return MSCAN_ERR_WORKSPACE;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob)))
+    return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dh0 && prob->cu_seqlens) {
     // empty sequences have no element to write their (zero) gradient

@@ -85,17 +85,18 @@ __device__ __forceinline__ void lin_wave_scan(float& P, float& Q) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace: control header + one descriptor set per tile.
+// Workspace: control header, one epoch word per row, descriptor words per tile.
 //
 // Every descriptor word is 64 bits, {tag:32 | value:32}, written and read with
 // relaxed agent-scope atomics, so each word is self-validating and no fence is
 // needed between words. tag = (epoch << 2) | kind, kind 1 = aggregate of the
-// tile alone, 2 = inclusive value (the state at the tile's end). The epoch
-// advances once per call (the last workgroup to finish bumps it and resets the
-// counters), so words from earlier calls never look valid and the workspace
-// needs no clearing between calls.
+// tile alone, 2 = inclusive value (the state at the tile's end). Each row has
+// its own epoch, which the row's last tile advances once its look-back has
+// finished (by then every tile of the row has read the epoch), so words from
+// earlier calls never look valid, nothing needs clearing between calls and no
+// atomic read-modify-write touches a shared address.
 // ---------------------------------------------------------------------------
-enum : int { kHdrEpoch = 0, kHdrTileCtr = 1, kHdrDoneCtr = 2, kHdrError = 3, kHdrWords = 32 };
+enum : int { kHdrError = 3, kHdrWords = 32 };
 enum : uint32_t { kKindAgg = 1, kKindIncl = 2 };
 
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
@@ -117,26 +118,22 @@ __device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >
 __device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 struct Workspace {
-  uint32_t* hdr;   // kHdrWords 32-bit control words
-  uint64_t* desc;  // per-tile descriptor words
+  uint32_t* hdr;    // kHdrWords 32-bit control words
+  uint32_t* epoch;  // one word per row
+  uint64_t* desc;   // per-tile descriptor words
 };
 
-__device__ __forceinline__ Workspace ws_view(void* ws) {
-  Workspace w;
-  w.hdr = (uint32_t*)ws;
-  w.desc = (uint64_t*)((char*)ws + kHdrWords * 4);
-  return w;
+// Byte offset of the descriptors: header + per-row epochs rounded up to 16 bytes.
+__host__ __device__ __forceinline__ size_t ws_desc_offset(int64_t rows) {
+  return (size_t)kHdrWords * 4 + (((size_t)rows * 4 + 15) & ~(size_t)15);
 }
 
-// Called once per workgroup at the very end; the last one re-arms the workspace.
-__device__ __forceinline__ void ws_finish(Workspace w, uint32_t nblocks, uint32_t epoch) {
-  const uint32_t done = __hip_atomic_fetch_add(w.hdr + kHdrDoneCtr, 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-  if (done == nblocks - 1) {
-    st_u32(w.hdr + kHdrTileCtr, 0u);
-    st_u32(w.hdr + kHdrDoneCtr, 0u);
-    st_u32(w.hdr + kHdrEpoch, (epoch + 1u) & 0x3fffffffu);
-  }
+__device__ __forceinline__ Workspace ws_view(void* ws, int64_t rows) {
+  Workspace w;
+  w.hdr = (uint32_t*)ws;
+  w.epoch = (uint32_t*)((char*)ws + kHdrWords * 4);
+  w.desc = (uint64_t*)((char*)ws + ws_desc_offset(rows));
+  return w;
 }
 
 // Upper bound on look-back polls before a wave gives up (then the header's

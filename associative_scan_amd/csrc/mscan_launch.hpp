@@ -27,6 +27,8 @@ struct ScalarArgs {
 int64_t scalar_tile_elems(int in_dtype);
 int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile);
 int scalar_vec(int in_dtype);
+// Whether a scalar call chains the tiles of a row by look-back (few long rows).
+bool scalar_uses_lookback(int64_t rows, int64_t ntiles);
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
 
 // Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so

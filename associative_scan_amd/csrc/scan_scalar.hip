@@ -17,14 +17,18 @@
 //             dg = lam * (forward state before t, h0 at the sequence start),
 //             dh0 = g * lam at the forward's first element of each sequence.
 //
-// Work decomposition (one workgroup = one tile of one row):
-//   tile   = WAVES waves x SUBS sub-chunks x 64 lanes x EL elements (contiguous
-//            in memory; lanes of a sub-chunk read consecutive 16-byte vectors),
-//   a lane = EL consecutive elements, summarised serially into (P, Q),
-//   a wave = SUBS independent 64-lane DPP scans chained through lane 63,
-//   waves  = chained through LDS,
-//   tiles of one row = chained by decoupled look-back through the workspace
-//            (only when a row needs more than one tile).
+// Work decomposition. A tile = WAVES waves x SUBS sub-chunks x 64 lanes x EL
+// elements, contiguous in memory (the lanes of a sub-chunk read consecutive
+// 16-byte vectors). Inside a tile:
+//   a lane    = EL consecutive elements, summarised serially into (P, Q),
+//   a wave    = SUBS independent 64-lane DPP scans chained through lane 63,
+//   the waves = chained through LDS.
+// Across the tiles of a row, two modes:
+//   row loop : one workgroup walks its row tile by tile and carries the state
+//              in registers (used whenever there are enough rows to fill the
+//              GPU; no inter-workgroup traffic, deterministic);
+//   look-back: one workgroup per tile; tiles of a row chain by decoupled
+//              look-back through the workspace (few, long rows).
 // Rows whose start is not 16-byte aligned are handled by aligning vector
 // groups to absolute addresses and masking the elements outside the row.
 #include "mscan_device.hpp"
@@ -104,7 +108,7 @@ __device__ __forceinline__ int wave_count_le(const int32_t* cu, int n, int64_t k
   return lo + __popcll(__ballot(le));
 }
 
-constexpr int kCuSlice = 1024;  // cu_seqlens entries cached in LDS per tile
+constexpr int kCuSlice = 1024;  // cu_seqlens entries cached in LDS per workgroup
 
 struct SegSlice {
   const int32_t* v;  // slice values (LDS or global)
@@ -122,10 +126,12 @@ __device__ __forceinline__ int slice_find(const SegSlice& s, int64_t q) {
   return lo;
 }
 
+enum : int { kRowLoop = 0, kLookback = 1 };
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename Tin, bool BWD, int WAVES, int SUBS, int GPL, bool VARLEN, bool MULTI>
+template <typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL>
 __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   constexpr int VEC = InTraits<Tin>::VEC;
   constexpr int EL = VEC * GPL;          // elements per lane per sub-chunk
@@ -133,380 +139,398 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   constexpr int TILE = WAVES * WREG;     // elements per tile
   static_assert(EL <= 16, "per-lane span too long");
 
-  __shared__ float s_aggP[WAVES], s_aggQ[WAVES];
+  __shared__ float s_aggP[2][WAVES], s_aggQ[2][WAVES];
   __shared__ float s_carry;
-  __shared__ uint32_t s_tile, s_epoch;
   __shared__ int32_t s_cu[VARLEN ? kCuSlice : 1];
   __shared__ int32_t s_cu_n, s_cu_k0;
 
   const int l = lane_id();
   const int w = (int)(threadIdx.x >> 6);
 
-  Workspace ws{};
-  uint32_t tile, epoch = 0;
-  if constexpr (MULTI) {
-    ws = ws_view(a.ws);
-    if (threadIdx.x == 0) {
-      s_tile = __hip_atomic_fetch_add(ws.hdr + kHdrTileCtr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_epoch = ld_u32(ws.hdr + kHdrEpoch);
-    }
-    __syncthreads();
-    tile = s_tile;
-    epoch = s_epoch;
+  int64_t r;
+  int c_first, c_last;
+  if constexpr (MODE == kRowLoop) {
+    r = blockIdx.x;
+    c_first = 0;
+    c_last = a.ntiles - 1;
   } else {
-    tile = blockIdx.x;
+    r = blockIdx.x / (uint32_t)a.ntiles;
+    c_first = c_last = (int)(blockIdx.x - (uint32_t)r * (uint32_t)a.ntiles);
   }
-  if constexpr (MULTI) {
-    // a tile id past the grid means the workspace was not re-armed (not zeroed
-    // before first use): flag it and touch nothing
-    if (tile >= gridDim.x) {
-      if (threadIdx.x == 0) {
-        st_u32(ws.hdr + kHdrError, 2u);
-        ws_finish(ws, gridDim.x, epoch);
-      }
-      return;
-    }
-  }
-  const int64_t r = tile / (uint32_t)a.ntiles;
-  const int c = (int)(tile - (uint32_t)r * (uint32_t)a.ntiles);
   const int64_t T = a.T;
   const int64_t rowoff = r * a.stride;
   const int lead = (int)(rowoff % VEC);
   const int64_t urow = ((T - 1 + lead) / VEC + 1) * VEC;  // padded row length
-  const bool rev = a.rev != 0;
-  const int64_t jt0 = (int64_t)c * TILE;
-  const int64_t ut_lo = rev ? urow - jt0 - TILE : jt0;     // tile span in padded coords
-  const bool interior = (ut_lo >= lead) && (ut_lo + TILE <= lead + T);
   const int64_t base = rowoff - lead;                       // element index of padded u = 0
-
   const Tin* gp = (const Tin*)a.g;
+  const float* h0p = a.h0;
+  const float h0row = (!VARLEN && h0p) ? h0p[r] : 0.f;
 
-  // padded coordinate of the lowest element of (sub-chunk s) for this lane
-  auto span_lo = [&](int s) -> int64_t {
-    const int64_t j0 = jt0 + (int64_t)w * WREG + (int64_t)s * 64 * EL + (int64_t)l * EL;
-    return rev ? urow - j0 - EL : j0;
-  };
+  Workspace ws{};
+  uint32_t epoch = 0;
+  if constexpr (MODE == kLookback) {
+    ws = ws_view(a.ws, a.rows);
+    epoch = ld_u32(ws.epoch + r);
+  }
 
-  // ---- cu_seqlens slice covering this tile ------------------------------
+  // ---- sequence table ------------------------------------------------------
   SegSlice seg{nullptr, 0, 0};
   if constexpr (VARLEN) {
-    const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
-    if (w == 0) {
-      int ka = 0, n = 0;
-      if (plo < phi) {
-        ka = max(wave_count_le(a.cu, a.nseg + 1, plo) - 1, 0);
-        const int kb = min(wave_count_le(a.cu, a.nseg + 1, phi - 1), a.nseg);
-        n = max(kb - ka + 1, 1);
+    if constexpr (MODE == kRowLoop) {
+      // every tile of the row needs the whole table: cache it once
+      const int n = a.nseg + 1;
+      if (n <= kCuSlice) {
+        for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[i];
+        __syncthreads();
+        seg = SegSlice{s_cu, n, 0};
+      } else {
+        seg = SegSlice{a.cu, n, 0};
       }
-      if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
-    }
-    __syncthreads();
-    const int n = s_cu_n, k0 = s_cu_k0;
-    if (n <= kCuSlice) {
-      for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
-      __syncthreads();
-      seg = SegSlice{s_cu, n, k0};
     } else {
-      seg = SegSlice{a.cu + k0, n, k0};
+      // just the entries that cover this tile
+      const int64_t jt0 = (int64_t)c_first * TILE;
+      const int64_t ut_lo = REV ? urow - jt0 - TILE : jt0;
+      const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
+      if (w == 0) {
+        int ka = 0, n = 0;
+        if (plo < phi) {
+          ka = max(wave_count_le(a.cu, a.nseg + 1, plo) - 1, 0);
+          const int kb = min(wave_count_le(a.cu, a.nseg + 1, phi - 1), a.nseg);
+          n = max(kb - ka + 1, 1);
+        }
+        if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
+      }
+      __syncthreads();
+      const int n = s_cu_n, k0 = s_cu_k0;
+      if (n <= kCuSlice) {
+        for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
+        __syncthreads();
+        seg = SegSlice{s_cu, n, k0};
+      } else {
+        seg = SegSlice{a.cu + k0, n, k0};
+      }
     }
   }
 
-  // ---- load -------------------------------------------------------------
-  // processing-order registers: A = transition, B = injection
-  float A[SUBS][EL], B[SUBS][EL];
-  float G[BWD ? SUBS : 1][EL], N[BWD ? SUBS : 1][EL];  // bwd: own gate, next forward state
-  {
-    float t0[EL], t1[EL], t2[EL];
+  float carry = 0.f;  // state entering the current tile
+  for (int c = c_first; c <= c_last; ++c) {
+    const int64_t jt0 = (int64_t)c * TILE;
+    const int64_t ut_lo = REV ? urow - jt0 - TILE : jt0;  // tile span in padded coords
+    const bool interior = (ut_lo >= lead) && (ut_lo + TILE <= lead + T);
+    // padded coordinate of the lowest element of sub-chunk s for this lane
+    auto span_lo = [&](int s) -> int64_t {
+      const int64_t j0 = jt0 + (int64_t)w * WREG + (int64_t)s * 64 * EL + (int64_t)l * EL;
+      return REV ? urow - j0 - EL : j0;
+    };
+
+    // ---- load: every vector of the tile is in flight before the first use
+    float Lg[SUBS][EL], Lb[SUBS][EL], Lh[BWD ? SUBS : 1][EL];
+    if (interior) {
 #pragma unroll
-    for (int s = 0; s < SUBS; ++s) {
-      const int64_t u0 = span_lo(s);
-      if (interior) {
-        load_span<Tin, EL>(gp + base + u0, t0);
+      for (int s = 0; s < SUBS; ++s) {
+        const int64_t u0 = span_lo(s);
+        load_span<Tin, EL>(gp + base + u0, Lg[s]);
         if constexpr (!BWD) {
-          load_span<Tin, EL>((const Tin*)a.b + base + u0, t1);
+          load_span<Tin, EL>((const Tin*)a.b + base + u0, Lb[s]);
         } else {
-          load_span<float, EL>((const float*)a.b + base + u0, t1);
-          load_span<float, EL>(a.hs + base + u0, t2);
+          load_span<float, EL>((const float*)a.b + base + u0, Lb[s]);
+          load_span<float, EL>(a.hs + base + u0, Lh[s]);
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) {
+        const int64_t u0 = span_lo(s);
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
           const int64_t t = u0 + e - lead;
           const bool ok = (t >= 0) && (t < T);
-          t0[e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : 1.f;
+          Lg[s][e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : 1.f;
           if constexpr (!BWD) {
-            t1[e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : 0.f;
+            Lb[s][e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : 0.f;
           } else {
-            t1[e] = ok ? ((const float*)a.b)[rowoff + t] : 0.f;
-            t2[e] = ok ? a.hs[rowoff + t] : 0.f;
+            Lb[s][e] = ok ? ((const float*)a.b)[rowoff + t] : 0.f;
+            Lh[s][e] = ok ? a.hs[rowoff + t] : 0.f;
           }
         }
       }
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        const int p = rev ? EL - 1 - e : e;  // physical component of processing element e
-        if constexpr (!BWD) {
-          A[s][e] = t0[p];
-          B[s][e] = t1[p];
-        } else {
-          G[s][e] = t0[p];
-          B[s][e] = t1[p];
-          N[s][e] = t2[p];
-        }
-      }
     }
-  }
-
-  // ---- backward: shift gates forward and states backward by one element
-  if constexpr (BWD) {
-    // physical position of processing element j of this row (padded coords)
-    auto u_of = [&](int64_t j) -> int64_t { return rev ? urow - 1 - j : j; };
+    // processing order: element e of a lane is physical component P_(e)
+    auto P_ = [](int e) { return REV ? EL - 1 - e : e; };
+    float A[SUBS][EL], B[SUBS][EL];
+    float G[BWD ? SUBS : 1][EL], N[BWD ? SUBS : 1][EL];  // bwd: own gate, next forward state
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
-      float gprev = __shfl_up(G[s][EL - 1], 1, 64);
-      float hnext = __shfl_down(N[s][0], 1, 64);
-      if (s > 0) {
-        const float gl = readlane_f(G[s - 1][EL - 1], 63);
-        if (l == 0) gprev = gl;
-      } else if (l == 0) {
-        const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
-        const int64_t t = u_of(j) - lead;
-        gprev = (j >= 0 && t >= 0 && t < T) ? InTraits<Tin>::load1(gp + rowoff + t) : 0.f;
-      }
-      if (s + 1 < SUBS) {
-        const float hn = readlane_f(N[s + 1][0], 0);
-        if (l == 63) hnext = hn;
-      } else if (l == 63) {
-        const int64_t j = jt0 + (int64_t)(w + 1) * WREG;  // element after this wave's span
-        const int64_t t = u_of(j) - lead;
-        hnext = (t >= 0 && t < T) ? a.hs[rowoff + t] : 0.f;
-      }
-#pragma unroll
-      for (int e = EL - 1; e > 0; --e) A[s][e] = G[s][e - 1];
-      A[s][0] = gprev;
-#pragma unroll
-      for (int e = 0; e < EL - 1; ++e) N[s][e] = N[s][e + 1];
-      N[s][EL - 1] = hnext;
-    }
-  }
-
-  // ---- sequence boundaries ------------------------------------------------
-  // first: a sequence's first element in processing order; last: its last.
-  uint32_t lastmask[BWD ? SUBS : 1];
-  const float* h0p = a.h0;
-#pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    const int64_t u0 = span_lo(s);
-    uint32_t lm = 0;
-    if constexpr (!VARLEN) {
-      // one sequence per row: first / last are the row's ends
-      const int64_t tf = rev ? T - 1 : 0, tl = rev ? 0 : T - 1;
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        const int64_t t = u0 + (rev ? EL - 1 - e : e) - lead;
-        if (t == tf) {
-          const float hv = h0p ? h0p[r] : 0.f;
-          if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
-          A[s][e] = 0.f;
-        }
-        if constexpr (BWD) {
-          if (t == tl) {
-            N[s][e] = h0p ? h0p[r] : 0.f;
-            lm |= 1u << e;
-          }
+        B[s][e] = Lb[s][P_(e)];
+        if constexpr (!BWD) {
+          A[s][e] = Lg[s][P_(e)];
+        } else {
+          G[s][e] = Lg[s][P_(e)];
+          N[s][e] = Lh[s][P_(e)];
         }
       }
-    } else {
-      // walk the elements in physical order against the cu slice
-      const int64_t q0 = u0 - lead;
-      if (seg.n > 0) {
-        int k = slice_find(seg, max(q0, (int64_t)0));
+    }
+
+    // ---- backward: shift gates forward and states backward by one element
+    if constexpr (BWD) {
+      // padded coordinate of processing element j of this row
+      auto u_of = [&](int64_t j) -> int64_t { return REV ? urow - 1 - j : j; };
 #pragma unroll
-        for (int ep = 0; ep < EL; ++ep) {
-          const int64_t q = q0 + ep;
-          if (q < 0 || q >= T) continue;
-          while (k + 1 < seg.n && (int64_t)seg.v[k + 1] <= q) ++k;
-          const bool is_start = (int64_t)seg.v[k] == q;
-          const bool is_end = (k + 1 < seg.n) && ((int64_t)seg.v[k + 1] - 1 == q);
-          const int sk = min(max(seg.k0 + k, 0), a.nseg - 1);
-          const int e = rev ? EL - 1 - ep : ep;
-          const bool first = rev ? is_end : is_start;
-          const bool last = rev ? is_start : is_end;
-          const float hv = (h0p && (first || last)) ? h0p[(int64_t)sk * a.rows + r] : 0.f;
-          if (first) {
-            if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
+      for (int s = 0; s < SUBS; ++s) {
+        float gprev = __shfl_up(G[s][EL - 1], 1, 64);
+        float hnext = __shfl_down(N[s][0], 1, 64);
+        if (s > 0) {
+          const float gl = readlane_f(G[s - 1][EL - 1], 63);
+          if (l == 0) gprev = gl;
+        } else if (l == 0) {
+          const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
+          const int64_t t = u_of(j) - lead;
+          gprev = (j >= 0 && t >= 0 && t < T) ? InTraits<Tin>::load1(gp + rowoff + t) : 0.f;
+        }
+        if (s + 1 < SUBS) {
+          const float hn = readlane_f(N[s + 1][0], 0);
+          if (l == 63) hnext = hn;
+        } else if (l == 63) {
+          const int64_t j = jt0 + (int64_t)(w + 1) * WREG;  // element after this wave's span
+          const int64_t t = u_of(j) - lead;
+          hnext = (t >= 0 && t < T) ? a.hs[rowoff + t] : 0.f;
+        }
+#pragma unroll
+        for (int e = EL - 1; e > 0; --e) A[s][e] = G[s][e - 1];
+        A[s][0] = gprev;
+#pragma unroll
+        for (int e = 0; e < EL - 1; ++e) N[s][e] = N[s][e + 1];
+        N[s][EL - 1] = hnext;
+      }
+    }
+
+    // ---- sequence boundaries ------------------------------------------------
+    // first: a sequence's first element in processing order; last: its last.
+    uint32_t lastmask[BWD ? SUBS : 1];
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      const int64_t u0 = span_lo(s);
+      uint32_t lm = 0;
+      if constexpr (!VARLEN) {
+        // one sequence per row: first / last are the row's ends
+        const int64_t tf = REV ? T - 1 : 0, tl = REV ? 0 : T - 1;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          const int64_t t = u0 + P_(e) - lead;
+          if (t == tf) {
+            if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], h0row, B[s][e]);
             A[s][e] = 0.f;
           }
           if constexpr (BWD) {
-            if (last) {
-              N[s][e] = hv;
+            if (t == tl) {
+              N[s][e] = h0row;
               lm |= 1u << e;
             }
           }
         }
-      }
-    }
-    if constexpr (BWD) lastmask[s] = lm;
-  }
-
-  // ---- lane-serial summaries and wave scans ---------------------------
-  float P[SUBS], Q[SUBS];
+      } else {
+        // walk the elements in physical order against the sequence table
+        const int64_t q0 = u0 - lead;
+        if (seg.n > 0) {
+          int k = slice_find(seg, max(q0, (int64_t)0));
 #pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    float p = 1.f, q = 0.f;
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      const bool use = A[s][e] != 0.f;
-      q = use ? __builtin_fmaf(A[s][e], q, B[s][e]) : B[s][e];
-      p = use ? A[s][e] * p : 0.f;
-    }
-    P[s] = p;
-    Q[s] = q;
-  }
-  {
-    // step-major so the SUBS independent scans interleave
-    const bool v1 = (l & 15) >= 1, v2 = (l & 15) >= 2, v4 = (l & 15) >= 4, v8 = (l & 15) >= 8;
-    const bool v16 = (l & 16) != 0, v32 = l >= 32;
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr1, 0xf>(P[s], Q[s], v1);
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr2, 0xf>(P[s], Q[s], v2);
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr4, 0xf>(P[s], Q[s], v4);
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr8, 0xf>(P[s], Q[s], v8);
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast15, 0xa>(P[s], Q[s], v16);
-#pragma unroll
-    for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast31, 0xc>(P[s], Q[s], v32);
-  }
-  // wave aggregate = sub-chunk totals (lane 63) in order
-  float wP = 1.f, wQ = 0.f;
-#pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    float sp = readlane_f(P[s], 63), sq = readlane_f(Q[s], 63);
-    lin_compose(wP, wQ, sp, sq);  // (waves so far, then sub-chunk s)
-    wP = sp;
-    wQ = sq;
-  }
-
-  // ---- across waves --------------------------------------------------------
-  float exP = 1.f, exQ = 0.f;     // composition of the waves before this one
-  float tP = wP, tQ = wQ;         // tile aggregate
-  if constexpr (WAVES > 1) {
-    if (l == 0) { s_aggP[w] = wP; s_aggQ[w] = wQ; }
-    __syncthreads();
-    tP = 1.f; tQ = 0.f;
-#pragma unroll
-    for (int i = 0; i < WAVES; ++i) {
-      if (i == w) { exP = tP; exQ = tQ; }
-      float p = s_aggP[i], q = s_aggQ[i];
-      lin_compose(tP, tQ, p, q);
-      tP = p;
-      tQ = q;
-    }
-  }
-
-  // ---- across tiles: decoupled look-back ------------------------------------
-  float carry = 0.f;
-  if constexpr (MULTI) {
-    uint64_t* rd = ws.desc + (int64_t)3 * ((int64_t)r * a.ntiles);
-    if (w == 0) {
-      const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
-      if (l == 0) {
-        if (tP != 0.f) {
-          st_u64(rd + 3 * c, pack_word(tagA, tP));
-          st_u64(rd + 3 * c + 1, pack_word(tagA, tQ));
-        } else {
-          st_u64(rd + 3 * c + 2, pack_word(tagI, tQ));
+          for (int ep = 0; ep < EL; ++ep) {
+            const int64_t q = q0 + ep;
+            if (q < 0 || q >= T) continue;
+            while (k + 1 < seg.n && (int64_t)seg.v[k + 1] <= q) ++k;
+            const bool is_start = (int64_t)seg.v[k] == q;
+            const bool is_end = (k + 1 < seg.n) && ((int64_t)seg.v[k + 1] - 1 == q);
+            const int e = REV ? EL - 1 - ep : ep;
+            const bool first = REV ? is_end : is_start;
+            const bool last = REV ? is_start : is_end;
+            if (first || last) {
+              const int sk = min(max(seg.k0 + k, 0), a.nseg - 1);
+              const float hv = h0p ? h0p[(int64_t)sk * a.rows + r] : 0.f;
+              if (first) {
+                if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
+                A[s][e] = 0.f;
+              }
+              if constexpr (BWD) {
+                if (last) {
+                  N[s][e] = hv;
+                  lm |= 1u << e;
+                }
+              }
+            }
+          }
         }
       }
-      if (c > 0) carry = lin_lookback(ws, rd, c, epoch);
-      if (l == 0) {
-        if (tP != 0.f) st_u64(rd + 3 * c + 2, pack_word(tagI, lin_apply(tP, tQ, carry)));
-        s_carry = carry;
-      }
+      if constexpr (BWD) lastmask[s] = lm;
     }
-    __syncthreads();
-    carry = s_carry;
-  }
 
-  // ---- apply: every element from its exact carry-in ---------------------------
-  float hs = lin_apply(exP, exQ, carry);  // state entering this wave's span
-  float O[SUBS][EL];
+    // ---- lane-serial summaries and wave scans ---------------------------
+    float P[SUBS], Q[SUBS];
 #pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    const float v = lin_apply(P[s], Q[s], hs);  // state after this lane
-    float st = __shfl_up(v, 1, 64);
-    if (l == 0) st = hs;
-    hs = readlane_f(v, 63);
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      const bool use = A[s][e] != 0.f;
-      st = use ? __builtin_fmaf(A[s][e], st, B[s][e]) : B[s][e];
-      O[s][e] = st;
-    }
-  }
-
-  // ---- store -------------------------------------------------------------
-#pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    const int64_t u0 = span_lo(s);
-    float o0[EL], o1[EL];
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      const int p = rev ? EL - 1 - e : e;
-      o0[p] = O[s][e];
-      if constexpr (BWD) o1[p] = O[s][e] * N[s][e];
-    }
-    if (interior) {
-      store_span<EL>(a.out0 + base + u0, o0);
-      if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
-    } else {
+    for (int s = 0; s < SUBS; ++s) {
+      float p = 1.f, q = 0.f;
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        const int64_t t = u0 + e - lead;
-        if (t >= 0 && t < T) {
-          a.out0[rowoff + t] = o0[e];
-          if constexpr (BWD) a.out1[rowoff + t] = o1[e];
-        }
+        const bool use = A[s][e] != 0.f;
+        q = use ? __builtin_fmaf(A[s][e], q, B[s][e]) : B[s][e];
+        p = use ? A[s][e] * p : 0.f;
+      }
+      P[s] = p;
+      Q[s] = q;
+    }
+    {
+      // step-major so the SUBS independent scans interleave
+      const bool v1 = (l & 15) >= 1, v2 = (l & 15) >= 2, v4 = (l & 15) >= 4, v8 = (l & 15) >= 8;
+      const bool v16 = (l & 16) != 0, v32 = l >= 32;
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr1, 0xf>(P[s], Q[s], v1);
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr2, 0xf>(P[s], Q[s], v2);
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr4, 0xf>(P[s], Q[s], v4);
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr8, 0xf>(P[s], Q[s], v8);
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast15, 0xa>(P[s], Q[s], v16);
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast31, 0xc>(P[s], Q[s], v32);
+    }
+    // wave aggregate = sub-chunk totals (lane 63) in order
+    float wP = 1.f, wQ = 0.f;
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      float sp = readlane_f(P[s], 63), sq = readlane_f(Q[s], 63);
+      lin_compose(wP, wQ, sp, sq);  // (waves so far, then sub-chunk s)
+      wP = sp;
+      wQ = sq;
+    }
+
+    // ---- across waves ------------------------------------------------------
+    float exP = 1.f, exQ = 0.f;  // composition of the waves before this one
+    float tP = wP, tQ = wQ;      // tile aggregate
+    if constexpr (WAVES > 1) {
+      const int buf = c & 1;  // alternate buffers: one barrier per tile suffices
+      if (l == 0) { s_aggP[buf][w] = wP; s_aggQ[buf][w] = wQ; }
+      __syncthreads();
+      tP = 1.f; tQ = 0.f;
+#pragma unroll
+      for (int i = 0; i < WAVES; ++i) {
+        if (i == w) { exP = tP; exQ = tQ; }
+        float p = s_aggP[buf][i], q = s_aggQ[buf][i];
+        lin_compose(tP, tQ, p, q);
+        tP = p;
+        tQ = q;
       }
     }
-    if constexpr (BWD) {
-      // dh0 = g * lam at each sequence's forward-first element
-      if (a.dh0 && lastmask[s]) {
+
+    // ---- across tiles: decoupled look-back ----------------------------------
+    if constexpr (MODE == kLookback) {
+      uint64_t* rd = ws.desc + (int64_t)3 * ((int64_t)r * a.ntiles);
+      if (w == 0) {
+        const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+        if (l == 0) {
+          if (tP != 0.f) {
+            st_u64(rd + 3 * c, pack_word(tagA, tP));
+            st_u64(rd + 3 * c + 1, pack_word(tagA, tQ));
+          } else {
+            st_u64(rd + 3 * c + 2, pack_word(tagI, tQ));
+          }
+        }
+        if (c > 0) carry = lin_lookback(ws, rd, c, epoch);
+        if (l == 0) {
+          if (tP != 0.f) st_u64(rd + 3 * c + 2, pack_word(tagI, lin_apply(tP, tQ, carry)));
+          // every earlier tile of the row has published, so all of them have
+          // read this call's epoch: the row's last tile advances it
+          if (c == a.ntiles - 1) st_u32(ws.epoch + r, (epoch + 1u) & 0x3fffffffu);
+          s_carry = carry;
+        }
+      }
+      __syncthreads();
+      carry = s_carry;
+    }
+
+    // ---- apply: every element from its exact carry-in ---------------------------
+    float hs = lin_apply(exP, exQ, carry);  // state entering this wave's span
+    float O[SUBS][EL];
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      const float v = lin_apply(P[s], Q[s], hs);  // state after this lane
+      float st = __shfl_up(v, 1, 64);
+      if (l == 0) st = hs;
+      hs = readlane_f(v, 63);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const bool use = A[s][e] != 0.f;
+        st = use ? __builtin_fmaf(A[s][e], st, B[s][e]) : B[s][e];
+        O[s][e] = st;
+      }
+    }
+    carry = lin_apply(tP, tQ, carry);  // state at the end of the tile
+
+    // ---- store -------------------------------------------------------------
+#pragma unroll
+    for (int s = 0; s < SUBS; ++s) {
+      const int64_t u0 = span_lo(s);
+      float o0[EL], o1[EL];
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        o0[P_(e)] = O[s][e];
+        if constexpr (BWD) o1[P_(e)] = O[s][e] * N[s][e];
+      }
+      if (interior) {
+        store_span<EL>(a.out0 + base + u0, o0);
+        if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
+      } else {
 #pragma unroll
         for (int e = 0; e < EL; ++e) {
-          if (!(lastmask[s] & (1u << e))) continue;
-          const int64_t t = u0 + (rev ? EL - 1 - e : e) - lead;
-          int sk = 0;
-          if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
-          a.dh0[(int64_t)sk * a.rows + r] = G[s][e] * O[s][e];
+          const int64_t t = u0 + e - lead;
+          if (t >= 0 && t < T) {
+            a.out0[rowoff + t] = o0[e];
+            if constexpr (BWD) a.out1[rowoff + t] = o1[e];
+          }
+        }
+      }
+      if constexpr (BWD) {
+        // dh0 = g * lam at each sequence's forward-first element
+        if (a.dh0 && lastmask[s]) {
+#pragma unroll
+          for (int e = 0; e < EL; ++e) {
+            if (!(lastmask[s] & (1u << e))) continue;
+            const int64_t t = u0 + P_(e) - lead;
+            int sk = 0;
+            if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
+            a.dh0[(int64_t)sk * a.rows + r] = G[s][e] * O[s][e];
+          }
         }
       }
     }
-  }
-
-  if constexpr (MULTI) {
-    if (threadIdx.x == 0) ws_finish(ws, gridDim.x, epoch);
   }
 }
 
 // ---------------------------------------------------------------------------
 // host launch
 // ---------------------------------------------------------------------------
-template <typename Tin, bool BWD, int WAVES, int SUBS, int GPL>
+// Rows at or above this count fill the GPU with one workgroup per row.
+constexpr int64_t kRowLoopMinRows = 1024;
+
+template <typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
   ScalarArgs a = a0;
   a.ntiles = (int32_t)scalar_tiles(a.T, a.stride, InTraits<Tin>::VEC, TILE);
-  const uint64_t nblocks = (uint64_t)a.rows * (uint64_t)a.ntiles;
-  const bool multi = a.ntiles > 1, varlen = a.cu != nullptr;
-  dim3 grid((unsigned)nblocks), block(WAVES * 64);
-  if (!multi && !varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, false, false>), grid, block, 0, st, a);
-  else if (!multi && varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, true, false>), grid, block, 0, st, a);
-  else if (multi && !varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_scalar<Tin, BWD, WAVES, SUBS, GPL, true, true>), grid, block, 0, st, a);
+  const bool lookback = scalar_uses_lookback(a.rows, a.ntiles);
+  const bool varlen = a.cu != nullptr;
+  const dim3 block(WAVES * 64);
+  if (!lookback) {
+    const dim3 grid((unsigned)a.rows);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+  } else {
+    const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
+    if (varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -521,11 +545,16 @@ int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
   return (umax + tile - 1) / tile;
 }
 
+bool scalar_uses_lookback(int64_t rows, int64_t ntiles) { return ntiles > 1 && rows < kRowLoopMinRows; }
+
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
+  const bool rev = a.rev != 0;
   if (in_dtype == 0) {
-    return bwd ? launch_cfg<float, true, 4, 4, 1>(a, st) : launch_cfg<float, false, 4, 4, 1>(a, st);
+    if (bwd) return rev ? launch_cfg<float, true, true, 4, 4, 1>(a, st) : launch_cfg<float, true, false, 4, 4, 1>(a, st);
+    return rev ? launch_cfg<float, false, true, 4, 4, 1>(a, st) : launch_cfg<float, false, false, 4, 4, 1>(a, st);
   }
-  return bwd ? launch_cfg<uint16_t, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, false, 4, 2, 1>(a, st);
+  if (bwd) return rev ? launch_cfg<uint16_t, true, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, true, false, 4, 2, 1>(a, st);
+  return rev ? launch_cfg<uint16_t, false, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, false, false, 4, 2, 1>(a, st);
 }
 
 }  // namespace mscan

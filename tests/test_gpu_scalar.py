@@ -238,6 +238,59 @@ def test_autograd_wrappers(m, oracle_lib):
 
 
 # ---------------------------------------------------------------------------
+# many rows: one workgroup walks each row (the mode the large workloads use)
+# ---------------------------------------------------------------------------
+ROWS_LOOP = 1024
+
+
+@pytest.mark.parametrize("T", [1, 5, 4095, 4097, 9001])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_row_loop_lengths(m, oracle_lib, T, reverse):
+    r = np.random.default_rng(1000 + T + reverse)
+    g = r.uniform(0, 1, (ROWS_LOOP, T)).astype(np.float32)
+    x = r.standard_normal((ROWS_LOOP, T)).astype(np.float32)
+    dy = r.standard_normal((ROWS_LOOP, T)).astype(np.float32)
+    h0 = r.standard_normal(ROWS_LOOP).astype(np.float32)
+    run_case(m, oracle_lib, g, x, dy, h0=h0, reverse=reverse)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_row_loop_exact_varlen(m, oracle_lib, reverse):
+    r = np.random.default_rng(2000 + reverse)
+    T = 13000
+    g, x, dy = gen.exact_mode(r, (ROWS_LOOP, T))
+    cu = gen.segments_random(r, T, 9, allow_empty=True)
+    h0 = r.integers(-1, 2, (9, ROWS_LOOP)).astype(np.float32)
+    run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=reverse, check=exact)
+
+
+def test_row_loop_many_sequences(m, oracle_lib):
+    """More sequences than the workgroup caches in LDS: the table is read from global memory."""
+    r = np.random.default_rng(2100)
+    T = 5000
+    g = r.uniform(0, 1, (ROWS_LOOP, T)).astype(np.float32)
+    x = r.standard_normal((ROWS_LOOP, T)).astype(np.float32)
+    dy = r.standard_normal((ROWS_LOOP, T)).astype(np.float32)
+    cu = gen.segments_random(r, T, 3000, allow_empty=True)
+    for rev in (False, True):
+        run_case(m, oracle_lib, g, x, dy, cu=cu, reverse=rev)
+
+
+def test_row_loop_unaligned_bf16(m, oracle_lib):
+    r = np.random.default_rng(2200)
+    T, stride = 9001, 9003
+    gb = gen.bf16_round(r.uniform(0, 1, (ROWS_LOOP, stride)).astype(np.float32)).reshape(ROWS_LOOP, stride)
+    xb = gen.bf16_round(r.standard_normal((ROWS_LOOP, stride)).astype(np.float32)).reshape(ROWS_LOOP, stride)
+    g = gen.bf16_bits_to_f32(gb).reshape(ROWS_LOOP, stride)[:, :T]
+    x = gen.bf16_bits_to_f32(xb).reshape(ROWS_LOOP, stride)[:, :T]
+    out = torch.full((ROWS_LOOP, stride), 7.0, device=DEV)
+    for rev in (False, True):
+        h = m.scan_fwd(_bf16(gb)[:, :T], _bf16(xb)[:, :T], reverse=rev, out=out[:, :T])
+        close(h, oracle_lib.scan_fwd(g, x, reverse=rev), TAU_FWD, "h")
+        assert torch.all(out[:, T:] == 7.0)
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads (the benchmark's launch configuration)
 # ---------------------------------------------------------------------------
 SAMPLE_ROWS = np.array([0, 1, 63, 64, 777, 1535, 1536, 4095, 6000, 9999, 12286, 12287])

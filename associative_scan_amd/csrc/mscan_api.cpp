@@ -39,16 +39,17 @@ int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
   return mscan::scalar_tiles(p->T, p->row_stride, mscan::scalar_vec(in_dtype), mscan::scalar_tile_elems(in_dtype));
 }
 
-// Workspace for either input type: header, then (only when rows are chained
-// by look-back) one epoch word per row and 3 descriptor words per tile.
-size_t scalar_ws_bytes(const mscan_problem* p) {
+// Workspace for a scalar-layout op: header, then (only when rows are chained by
+// look-back) one epoch word per row and `words` descriptor words per tile
+// (3 for the linear scan, 5 for the log-space scan).
+size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
   int64_t nt = 0;
-  for (int dt = MSCAN_F32; dt <= MSCAN_BF16; ++dt) {
+  for (int dt = MSCAN_F32; dt <= (f32_only ? MSCAN_F32 : MSCAN_BF16); ++dt) {
     const int64_t n = scalar_tiles_for(p, dt);
     if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
   }
   if (nt == 0) return mscan::kWsHeaderBytes;
-  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * 3u * sizeof(uint64_t);
+  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * (size_t)words * sizeof(uint64_t);
 }
 
 mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
@@ -68,7 +69,9 @@ size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
   switch (op) {
     case MSCAN_OP_SCAN_FWD:
     case MSCAN_OP_SCAN_BWD:
-      return scalar_ws_bytes(prob);
+      return scalar_ws_bytes(prob, 3, false);
+    case MSCAN_OP_SCAN_LOG_FWD:
+      return scalar_ws_bytes(prob, 5, true);
     default:
       return 0;
   }
@@ -88,7 +91,7 @@ mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, co
   if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, false)))
     return MSCAN_ERR_WORKSPACE;
   mscan::ScalarArgs a{};
   a.g = g;
@@ -117,7 +120,7 @@ mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, co
   if ((h0 && ((uintptr_t)h0 & 3u)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, false)))
     return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dh0 && prob->cu_seqlens) {
@@ -145,8 +148,28 @@ mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, co
 
 mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
                           const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream) {
-  (void)prob; (void)log_a; (void)log_b; (void)log_h0; (void)h; (void)ws; (void)ws_bytes; (void)stream;
-  return MSCAN_ERR_UNSUPPORTED;
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (!log_a || !log_b || !h) return MSCAN_ERR_INVALID;
+  if (!aligned16(log_a) || !aligned16(log_b) || !aligned16(h) || (log_h0 && ((uintptr_t)log_h0 & 3u)))
+    return MSCAN_ERR_INVALID;
+  const int64_t nt = scalar_tiles_for(prob, MSCAN_F32);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 5, true)))
+    return MSCAN_ERR_WORKSPACE;
+  mscan::ScalarArgs a{};
+  a.g = log_a;
+  a.b = log_b;
+  a.h0 = log_h0;
+  a.out0 = h;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse;
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_log(a, (hipStream_t)stream));
 }
 
 mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

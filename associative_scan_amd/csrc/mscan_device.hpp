@@ -60,30 +60,6 @@ __device__ __forceinline__ float lin_apply(float P, float Q, float h) {
   return (P != 0.f) ? __builtin_fmaf(P, h, Q) : Q;
 }
 
-// One scan step: lanes whose mask bit is set combine with the value DPP brings in.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void lin_scan_step(float& P, float& Q, bool valid) {
-  const float pe = dpp_f<CTRL, ROW_MASK>(1.f, P);
-  const float qe = dpp_f<CTRL, ROW_MASK>(0.f, Q);
-  const bool use = valid && (P != 0.f);
-  const float nP = use ? P * pe : P;
-  const float nQ = use ? __builtin_fmaf(P, qe, Q) : Q;
-  P = nP;
-  Q = nQ;
-}
-
-// Inclusive scan over the 64 lanes of a wave (lane 0 earliest):
-// four row shifts within rows of 16, then the two row broadcasts.
-__device__ __forceinline__ void lin_wave_scan(float& P, float& Q) {
-  const int l = lane_id();
-  lin_scan_step<kRowShr1, 0xf>(P, Q, (l & 15) >= 1);
-  lin_scan_step<kRowShr2, 0xf>(P, Q, (l & 15) >= 2);
-  lin_scan_step<kRowShr4, 0xf>(P, Q, (l & 15) >= 4);
-  lin_scan_step<kRowShr8, 0xf>(P, Q, (l & 15) >= 8);
-  lin_scan_step<kRowBcast15, 0xa>(P, Q, (l & 16) != 0);
-  lin_scan_step<kRowBcast31, 0xc>(P, Q, l >= 32);
-}
-
 // ---------------------------------------------------------------------------
 // Workspace: control header, one epoch word per row, descriptor words per tile.
 //
@@ -141,70 +117,214 @@ __device__ __forceinline__ Workspace ws_view(void* ws, int64_t rows) {
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 // ---------------------------------------------------------------------------
-// Decoupled look-back for scalar linear descriptors.
-// Descriptor set of tile i: agg P at desc[3i], agg Q at desc[3i+1], inclusive
-// value at desc[3i+2]. Run by one whole wave; returns the state entering tile
-// `c` of the row whose first descriptor set is `row_desc`.
+// Scan "ops": one summary type S (a map from the state before a span to the
+// state after it) and one carry type C (a state), stored as small float arrays
+// so the DPP, LDS and look-back code below can move them member by member.
+//   compose(e, l) : l := (e then l)          apply(s, c) : state after s from c
+//   hard(s)       : s ignores its input      of_carry(c) : hard summary giving c
+//   elem(a, b)    : one step                 step(a, b, c): one step applied to c
+//   first_ab(a, b, h0, has_h0): turn a sequence's first step into a hard step
+//                   with the initial state injected
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float lin_lookback(Workspace w, const uint64_t* row_desc, int c,
-                                              uint32_t epoch) {
+
+// Linear space: h -> P h + Q, carry = h. A zero P is hard.
+struct LinOps {
+  static constexpr int NS = 2, NC = 1;
+  static constexpr float kMaskA = 1.f, kMaskB = 0.f;  // identity step for masked elements
+  struct S { float v[NS]; };
+  struct C { float v[NC]; };
+  __device__ static __forceinline__ S ident() { return S{{1.f, 0.f}}; }
+  __device__ static __forceinline__ C cident() { return C{{0.f}}; }
+  __device__ static __forceinline__ bool hard(const S& s) { return s.v[0] == 0.f; }
+  __device__ static __forceinline__ void compose(const S& e, S& l) { lin_compose(e.v[0], e.v[1], l.v[0], l.v[1]); }
+  __device__ static __forceinline__ C apply(const S& s, const C& c) { return C{{lin_apply(s.v[0], s.v[1], c.v[0])}}; }
+  __device__ static __forceinline__ S of_carry(const C& c) { return S{{0.f, c.v[0]}}; }
+  __device__ static __forceinline__ C carry_of_hard(const S& s) { return C{{s.v[1]}}; }
+  __device__ static __forceinline__ S elem(float a, float b) { return S{{a, b}}; }
+  // a sequence's first step with h0 injected, as a hard step (a', b')
+  __device__ static __forceinline__ void first_ab(float& a, float& b, float h0, bool) {
+    b = __builtin_fmaf(a, h0, b);
+    a = 0.f;
+  }
+  __device__ static __forceinline__ float out(const C& c) { return c.v[0]; }
+  // one step applied to a carry (the per-element apply)
+  __device__ static __forceinline__ C step(float a, float b, const C& c) {
+    return C{{(a != 0.f) ? __builtin_fmaf(a, c.v[0], b) : b}};
+  }
+};
+
+// Log space ("Triton scan kernels", "One associative-scan family": the
+// log-space member carries a running log-coefficient sum and an online
+// max-shifted log-sum-exp, writing h = exp(.)). A step is (log a, log b).
+// Summary S = (P, m, s): P = sum of log a over the span (the running
+// log-coefficient sum, local to the span so it stays small), and the span's
+// own contribution as a max-shifted sum, log value = m + log s with s >= 1.
+// Carry C = (m, s) for log h = m + log s. Composing two pairs needs one exp
+// and no log; the output is h = e^m * s. P = -inf (a = 0) is hard.
+__device__ __forceinline__ void lse_pair(float am, float as, float bm, float bs, float& m, float& s) {
+  const float M = fmaxf(am, bm);
+  if (M == -__builtin_inff()) {
+    m = M;
+    s = 0.f;
+    return;
+  }
+  const float d = am - bm;
+  const float E = __expf(-fabsf(d));
+  s = (d >= 0.f) ? __builtin_fmaf(bs, E, as) : __builtin_fmaf(as, E, bs);
+  m = M;
+}
+
+struct LogOps {
+  static constexpr int NS = 3, NC = 2;
+  static constexpr float kMaskA = 0.f, kMaskB = -__builtin_inff();
+  struct S { float v[NS]; };
+  struct C { float v[NC]; };
+  __device__ static __forceinline__ S ident() { return S{{0.f, -__builtin_inff(), 0.f}}; }
+  __device__ static __forceinline__ C cident() { return C{{-__builtin_inff(), 0.f}}; }
+  __device__ static __forceinline__ bool hard(const S& s) { return s.v[0] == -__builtin_inff(); }
+  __device__ static __forceinline__ void compose(const S& e, S& l) {
+    if (l.v[0] == -__builtin_inff()) return;
+    float m, s;
+    lse_pair(l.v[0] + e.v[1], e.v[2], l.v[1], l.v[2], m, s);
+    l.v[0] = e.v[0] + l.v[0];
+    l.v[1] = m;
+    l.v[2] = s;
+  }
+  __device__ static __forceinline__ C apply(const S& s, const C& c) {
+    if (s.v[0] == -__builtin_inff()) return C{{s.v[1], s.v[2]}};
+    C r;
+    lse_pair(s.v[0] + c.v[0], c.v[1], s.v[1], s.v[2], r.v[0], r.v[1]);
+    return r;
+  }
+  __device__ static __forceinline__ S of_carry(const C& c) { return S{{-__builtin_inff(), c.v[0], c.v[1]}}; }
+  __device__ static __forceinline__ C carry_of_hard(const S& s) { return C{{s.v[1], s.v[2]}}; }
+  __device__ static __forceinline__ S elem(float a, float b) { return S{{a, b, 1.f}}; }
+  // a sequence's first step with log h0 injected, as a hard step (-inf, b')
+  __device__ static __forceinline__ void first_ab(float& a, float& b, float h0, bool has_h0) {
+    if (has_h0) {
+      float m, s;
+      lse_pair(a + h0, 1.f, b, 1.f, m, s);
+      b = (m == -__builtin_inff()) ? m : m + __logf(s);
+    }
+    a = -__builtin_inff();
+  }
+  __device__ static __forceinline__ float out(const C& c) {
+    return c.v[0] == -__builtin_inff() ? 0.f : __expf(c.v[0]) * c.v[1];
+  }
+  __device__ static __forceinline__ C step(float a, float b, const C& c) {
+    return apply(S{{a, b, 1.f}}, c);
+  }
+};
+
+// One DPP scan step on a summary: lanes whose mask bit is set compose the
+// summary DPP brings in (earlier) in front of their own.
+template <class Ops, int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
+  typename Ops::S e;
+  const typename Ops::S id = Ops::ident();
+#pragma unroll
+  for (int i = 0; i < Ops::NS; ++i) e.v[i] = dpp_f<CTRL, ROW_MASK>(id.v[i], x.v[i]);
+  if (valid) Ops::compose(e, x);
+}
+
+// ---------------------------------------------------------------------------
+// Decoupled look-back. Descriptor set of tile i = NS aggregate words followed
+// by NC inclusive words (the state at the tile's end). Run by one whole wave;
+// returns the state entering tile `c` of the row whose first descriptor set
+// is `row_desc`.
+// With `full`, the wave also waits until every earlier tile of the row has
+// published (the row's last tile uses this before it advances the row's
+// epoch, so that no tile of the row can still be about to read it).
+// ---------------------------------------------------------------------------
+template <class Ops>
+__device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c,
+                                                    uint32_t epoch, bool full) {
+  using S = typename Ops::S;
+  constexpr int ND = Ops::NS + Ops::NC;
   const int l = lane_id();
   const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
-  float accP = 1.f, accQ = 0.f;  // composition of the tiles already passed (later ones)
+  S acc = Ops::ident();  // composition of the tiles already passed (later ones)
+  bool found = false;    // acc already ends on an inclusive value
   int j = c - 1;
   uint32_t spins = 0;
   while (true) {
     const int jt = j - l;
     const bool inrow = jt >= 0;
-    float eP = 1.f, eQ = 0.f;
+    S e = Ops::ident();
     bool is_incl = false;
+    int stop = 64;
     while (true) {
       bool ready = !inrow;
       is_incl = false;
       if (inrow) {
-        const uint64_t wi = ld_u64(row_desc + 3 * jt + 2);
-        if (word_tag(wi) == tagI) {
+        const uint64_t* d = row_desc + (int64_t)ND * jt;
+        bool ok = true;
+        typename Ops::C cc;
+#pragma unroll
+        for (int i = 0; i < Ops::NC; ++i) {
+          const uint64_t wi = ld_u64(d + Ops::NS + i);
+          ok = ok && (word_tag(wi) == tagI);
+          cc.v[i] = word_val(wi);
+        }
+        if (ok) {
           is_incl = true;
           ready = true;
-          eP = 0.f;
-          eQ = word_val(wi);
+          e = Ops::of_carry(cc);
         } else {
-          const uint64_t wp = ld_u64(row_desc + 3 * jt);
-          const uint64_t wq = ld_u64(row_desc + 3 * jt + 1);
-          if (word_tag(wp) == tagA && word_tag(wq) == tagA) {
+          bool okA = true;
+          S ea;
+#pragma unroll
+          for (int i = 0; i < Ops::NS; ++i) {
+            const uint64_t wa = ld_u64(d + i);
+            okA = okA && (word_tag(wa) == tagA);
+            ea.v[i] = word_val(wa);
+          }
+          if (okA) {
             ready = true;
-            eP = word_val(wp);
-            eQ = word_val(wq);
+            if (jt == 0) {
+              // the row's first tile starts from the initial state, so its
+              // inclusive value follows from its aggregate: a window that
+              // reaches the row start always ends on an inclusive value
+              e = Ops::of_carry(Ops::apply(ea, Ops::cident()));
+              is_incl = true;
+            } else {
+              e = ea;
+            }
           }
         }
       }
       const uint64_t incl_mask = __ballot(is_incl);
-      const int stop = incl_mask ? __builtin_ctzll(incl_mask) : 64;
-      const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1ull);
+      stop = incl_mask ? __builtin_ctzll(incl_mask) : 64;
+      const uint64_t need = (full || stop >= 63) ? ~0ull : ((2ull << stop) - 1ull);
       const uint64_t not_ready = __ballot(!ready) & need;
       if (not_ready == 0) break;
       if (++spins > kSpinLimit) {
         if (l == 0) st_u32(w.hdr + kHdrError, 1u);
-        return 0.f;
+        return Ops::cident();
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    const uint64_t incl_mask = __ballot(is_incl);
-    const int stop = incl_mask ? __builtin_ctzll(incl_mask) : 64;
-    if (l > stop) { eP = 1.f; eQ = 0.f; }
-    // reduce lanes stop..0 in time order (higher lane = earlier tile)
+    if (!found) {
+      if (l > stop) e = Ops::ident();
+      // reduce lanes stop..0 in time order (higher lane = earlier tile)
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float pe = __shfl_down(eP, off, 64);
-      const float qe = __shfl_down(eQ, off, 64);
-      if (l + off < 64) lin_compose(pe, qe, eP, eQ);
+      for (int off = 1; off < 64; off <<= 1) {
+        S o;
+#pragma unroll
+        for (int i = 0; i < Ops::NS; ++i) o.v[i] = __shfl_down(e.v[i], off, 64);
+        if (l + off < 64) Ops::compose(o, e);
+      }
+      S win;
+#pragma unroll
+      for (int i = 0; i < Ops::NS; ++i) win.v[i] = readlane_f(e.v[i], 0);
+      Ops::compose(win, acc);
+      found = stop < 64;
     }
-    const float wP = readlane_f(eP, 0), wQ = readlane_f(eQ, 0);
-    lin_compose(wP, wQ, accP, accQ);
-    if (stop < 64) break;
+    if (j < 64) break;            // this window reached the row's first tile
+    if (found && !full) break;    // an inclusive value closes the composition
     j -= 64;
   }
-  return accQ;  // accP is 0: the window ended on an inclusive value
+  return Ops::carry_of_hard(acc);  // acc ends on an inclusive value: it is hard
 }
 
 }  // namespace mscan

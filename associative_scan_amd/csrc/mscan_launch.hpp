@@ -30,6 +30,8 @@ int scalar_vec(int in_dtype);
 // Whether a scalar call chains the tiles of a row by look-back (few long rows).
 bool scalar_uses_lookback(int64_t rows, int64_t ntiles);
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
+// Log-space forward (g = log a, b = log b, h0 = log h0; fp32).
+hipError_t launch_log(const ScalarArgs& a, hipStream_t st);
 
 // Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so
 // callers may capture it in a graph).

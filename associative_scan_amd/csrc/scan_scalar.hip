@@ -131,16 +131,19 @@ enum : int { kRowLoop = 0, kLookback = 1 };
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL>
+template <class Ops, typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL>
 __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
+  using S = typename Ops::S;
+  using C = typename Ops::C;
+  constexpr int NS = Ops::NS, NC = Ops::NC, ND = NS + NC;
   constexpr int VEC = InTraits<Tin>::VEC;
   constexpr int EL = VEC * GPL;          // elements per lane per sub-chunk
   constexpr int WREG = SUBS * 64 * EL;   // elements per wave
   constexpr int TILE = WAVES * WREG;     // elements per tile
   static_assert(EL <= 16, "per-lane span too long");
 
-  __shared__ float s_aggP[2][WAVES], s_aggQ[2][WAVES];
-  __shared__ float s_carry;
+  __shared__ float s_agg[2][WAVES][NS];
+  __shared__ float s_carry[NC];
   __shared__ int32_t s_cu[VARLEN ? kCuSlice : 1];
   __shared__ int32_t s_cu_n, s_cu_k0;
 
@@ -164,7 +167,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   const int64_t base = rowoff - lead;                       // element index of padded u = 0
   const Tin* gp = (const Tin*)a.g;
   const float* h0p = a.h0;
-  const float h0row = (!VARLEN && h0p) ? h0p[r] : 0.f;
+  const bool has_h0 = h0p != nullptr;
+  const float h0row = (!VARLEN && has_h0) ? h0p[r] : 0.f;
 
   Workspace ws{};
   uint32_t epoch = 0;
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     }
   }
 
-  float carry = 0.f;  // state entering the current tile
+  C carry = Ops::cident();  // state entering the current tile
   for (int c = c_first; c <= c_last; ++c) {
     const int64_t jt0 = (int64_t)c * TILE;
     const int64_t ut_lo = REV ? urow - jt0 - TILE : jt0;  // tile span in padded coords
@@ -245,9 +249,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         for (int e = 0; e < EL; ++e) {
           const int64_t t = u0 + e - lead;
           const bool ok = (t >= 0) && (t < T);
-          Lg[s][e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : 1.f;
+          Lg[s][e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : Ops::kMaskA;
           if constexpr (!BWD) {
-            Lb[s][e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : 0.f;
+            Lb[s][e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : Ops::kMaskB;
           } else {
             Lb[s][e] = ok ? ((const float*)a.b)[rowoff + t] : 0.f;
             Lh[s][e] = ok ? a.hs[rowoff + t] : 0.f;
@@ -320,8 +324,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         for (int e = 0; e < EL; ++e) {
           const int64_t t = u0 + P_(e) - lead;
           if (t == tf) {
-            if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], h0row, B[s][e]);
-            A[s][e] = 0.f;
+            if constexpr (!BWD) Ops::first_ab(A[s][e], B[s][e], h0row, has_h0);
+            else A[s][e] = 0.f;
           }
           if constexpr (BWD) {
             if (t == tl) {
@@ -347,10 +351,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             const bool last = REV ? is_start : is_end;
             if (first || last) {
               const int sk = min(max(seg.k0 + k, 0), a.nseg - 1);
-              const float hv = h0p ? h0p[(int64_t)sk * a.rows + r] : 0.f;
+              const float hv = has_h0 ? h0p[(int64_t)sk * a.rows + r] : 0.f;
               if (first) {
-                if constexpr (!BWD) B[s][e] = __builtin_fmaf(A[s][e], hv, B[s][e]);
-                A[s][e] = 0.f;
+                if constexpr (!BWD) Ops::first_ab(A[s][e], B[s][e], hv, has_h0);
+                else A[s][e] = 0.f;
               }
               if constexpr (BWD) {
                 if (last) {
@@ -366,107 +370,124 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     }
 
     // ---- lane-serial summaries and wave scans ---------------------------
-    float P[SUBS], Q[SUBS];
+    S sum[SUBS];
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
-      float p = 1.f, q = 0.f;
+      S run = Ops::ident();
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        const bool use = A[s][e] != 0.f;
-        q = use ? __builtin_fmaf(A[s][e], q, B[s][e]) : B[s][e];
-        p = use ? A[s][e] * p : 0.f;
+        S el = Ops::elem(A[s][e], B[s][e]);
+        Ops::compose(run, el);
+        run = el;
       }
-      P[s] = p;
-      Q[s] = q;
+      sum[s] = run;
     }
     {
       // step-major so the SUBS independent scans interleave
       const bool v1 = (l & 15) >= 1, v2 = (l & 15) >= 2, v4 = (l & 15) >= 4, v8 = (l & 15) >= 8;
       const bool v16 = (l & 16) != 0, v32 = l >= 32;
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr1, 0xf>(P[s], Q[s], v1);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr1, 0xf>(sum[s], v1);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr2, 0xf>(P[s], Q[s], v2);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr2, 0xf>(sum[s], v2);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr4, 0xf>(P[s], Q[s], v4);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr4, 0xf>(sum[s], v4);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowShr8, 0xf>(P[s], Q[s], v8);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr8, 0xf>(sum[s], v8);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast15, 0xa>(P[s], Q[s], v16);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast15, 0xa>(sum[s], v16);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) lin_scan_step<kRowBcast31, 0xc>(P[s], Q[s], v32);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast31, 0xc>(sum[s], v32);
     }
     // wave aggregate = sub-chunk totals (lane 63) in order
-    float wP = 1.f, wQ = 0.f;
+    S wagg = Ops::ident();
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
-      float sp = readlane_f(P[s], 63), sq = readlane_f(Q[s], 63);
-      lin_compose(wP, wQ, sp, sq);  // (waves so far, then sub-chunk s)
-      wP = sp;
-      wQ = sq;
+      S st;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) st.v[i] = readlane_f(sum[s].v[i], 63);
+      Ops::compose(wagg, st);  // (sub-chunks so far, then sub-chunk s)
+      wagg = st;
     }
 
     // ---- across waves ------------------------------------------------------
-    float exP = 1.f, exQ = 0.f;  // composition of the waves before this one
-    float tP = wP, tQ = wQ;      // tile aggregate
+    S ex = Ops::ident();  // composition of the waves before this one
+    S tagg = wagg;        // tile aggregate
     if constexpr (WAVES > 1) {
       const int buf = c & 1;  // alternate buffers: one barrier per tile suffices
-      if (l == 0) { s_aggP[buf][w] = wP; s_aggQ[buf][w] = wQ; }
-      __syncthreads();
-      tP = 1.f; tQ = 0.f;
+      if (l == 0) {
 #pragma unroll
-      for (int i = 0; i < WAVES; ++i) {
-        if (i == w) { exP = tP; exQ = tQ; }
-        float p = s_aggP[buf][i], q = s_aggQ[buf][i];
-        lin_compose(tP, tQ, p, q);
-        tP = p;
-        tQ = q;
+        for (int i = 0; i < NS; ++i) s_agg[buf][w][i] = wagg.v[i];
+      }
+      __syncthreads();
+      tagg = Ops::ident();
+#pragma unroll
+      for (int q = 0; q < WAVES; ++q) {
+        if (q == w) ex = tagg;
+        S x;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) x.v[i] = s_agg[buf][q][i];
+        Ops::compose(tagg, x);
+        tagg = x;
       }
     }
 
     // ---- across tiles: decoupled look-back ----------------------------------
     if constexpr (MODE == kLookback) {
-      uint64_t* rd = ws.desc + (int64_t)3 * ((int64_t)r * a.ntiles);
+      uint64_t* rd = ws.desc + (int64_t)ND * ((int64_t)r * a.ntiles);
+      uint64_t* my = rd + (int64_t)ND * c;
       if (w == 0) {
         const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+        const bool hard = Ops::hard(tagg);
         if (l == 0) {
-          if (tP != 0.f) {
-            st_u64(rd + 3 * c, pack_word(tagA, tP));
-            st_u64(rd + 3 * c + 1, pack_word(tagA, tQ));
+          if (!hard) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) st_u64(my + i, pack_word(tagA, tagg.v[i]));
           } else {
-            st_u64(rd + 3 * c + 2, pack_word(tagI, tQ));
+            const C inc = Ops::carry_of_hard(tagg);
+#pragma unroll
+            for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
         }
-        if (c > 0) carry = lin_lookback(ws, rd, c, epoch);
+        if (c > 0) carry = lookback<Ops>(ws, rd, c, epoch, c == a.ntiles - 1);
         if (l == 0) {
-          if (tP != 0.f) st_u64(rd + 3 * c + 2, pack_word(tagI, lin_apply(tP, tQ, carry)));
-          // every earlier tile of the row has published, so all of them have
-          // read this call's epoch: the row's last tile advances it
+          if (!hard) {
+            const C inc = Ops::apply(tagg, carry);
+#pragma unroll
+            for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
+          }
+          // the last tile's look-back waited for every earlier tile of the row
+          // to publish, so all of them have read this call's epoch: advance it
           if (c == a.ntiles - 1) st_u32(ws.epoch + r, (epoch + 1u) & 0x3fffffffu);
-          s_carry = carry;
+#pragma unroll
+          for (int i = 0; i < NC; ++i) s_carry[i] = carry.v[i];
         }
       }
       __syncthreads();
-      carry = s_carry;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) carry.v[i] = s_carry[i];
     }
 
     // ---- apply: every element from its exact carry-in ---------------------------
-    float hs = lin_apply(exP, exQ, carry);  // state entering this wave's span
+    C hs = Ops::apply(ex, carry);  // state entering this wave's span
     float O[SUBS][EL];
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
-      const float v = lin_apply(P[s], Q[s], hs);  // state after this lane
-      float st = __shfl_up(v, 1, 64);
-      if (l == 0) st = hs;
-      hs = readlane_f(v, 63);
+      const C v = Ops::apply(sum[s], hs);  // state after this lane
+      C st;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        st.v[i] = __shfl_up(v.v[i], 1, 64);
+        if (l == 0) st.v[i] = hs.v[i];
+        hs.v[i] = readlane_f(v.v[i], 63);
+      }
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        const bool use = A[s][e] != 0.f;
-        st = use ? __builtin_fmaf(A[s][e], st, B[s][e]) : B[s][e];
-        O[s][e] = st;
+        st = Ops::step(A[s][e], B[s][e], st);
+        O[s][e] = Ops::out(st);
       }
     }
-    carry = lin_apply(tP, tQ, carry);  // state at the end of the tile
+    carry = Ops::apply(tagg, carry);  // state at the end of the tile
 
     // ---- store -------------------------------------------------------------
 #pragma unroll
@@ -514,7 +535,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 // Rows at or above this count fill the GPU with one workgroup per row.
 constexpr int64_t kRowLoopMinRows = 1024;
 
-template <typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL>
+template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
   ScalarArgs a = a0;
@@ -524,12 +545,12 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   const dim3 block(WAVES * 64);
   if (!lookback) {
     const dim3 grid((unsigned)a.rows);
-    if (varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
   } else {
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
-    if (varlen) hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -550,11 +571,16 @@ bool scalar_uses_lookback(int64_t rows, int64_t ntiles) { return ntiles > 1 && r
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
   const bool rev = a.rev != 0;
   if (in_dtype == 0) {
-    if (bwd) return rev ? launch_cfg<float, true, true, 4, 4, 1>(a, st) : launch_cfg<float, true, false, 4, 4, 1>(a, st);
-    return rev ? launch_cfg<float, false, true, 4, 4, 1>(a, st) : launch_cfg<float, false, false, 4, 4, 1>(a, st);
+    if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, true, false, 4, 4, 1>(a, st);
+    return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, false, false, 4, 4, 1>(a, st);
   }
-  if (bwd) return rev ? launch_cfg<uint16_t, true, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, true, false, 4, 2, 1>(a, st);
-  return rev ? launch_cfg<uint16_t, false, true, 4, 2, 1>(a, st) : launch_cfg<uint16_t, false, false, 4, 2, 1>(a, st);
+  if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 2, 1>(a, st) : launch_cfg<LinOps, uint16_t, true, false, 4, 2, 1>(a, st);
+  return rev ? launch_cfg<LinOps, uint16_t, false, true, 4, 2, 1>(a, st) : launch_cfg<LinOps, uint16_t, false, false, 4, 2, 1>(a, st);
+}
+
+// Log-space forward: fp32 (log a, log b), same tiles as the fp32 scalar scan.
+hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
+  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LogOps, float, false, false, 4, 4, 1>(a, st);
 }
 
 }  // namespace mscan

@@ -58,13 +58,27 @@ mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
   return MSCAN_OK;
 }
 
+// Workspace of a matrix op: header, then (look-back only) per-row epochs and
+// k*k + 2*k*v descriptor words per tile.
+size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
+  int64_t nt = 0;
+  for (int b = 0; b < 2; ++b) {
+    const int64_t n = mscan::matrix_tiles(p->T, k, v, b == 1);
+    if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
+  }
+  if (nt == 0) return mscan::kWsHeaderBytes;
+  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * (size_t)(k * k + 2 * k * v) * sizeof(uint64_t);
+}
+
+bool matrix_shape_ok(int k, int v) {
+  return (k == 1 && v == 1) || (k == 2 && (v == 1 || v == 2)) || (k == 4 && (v == 1 || v == 4));
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
-  (void)k;
-  (void)v;
   if (check_problem(prob) != MSCAN_OK) return 0;
   switch (op) {
     case MSCAN_OP_SCAN_FWD:
@@ -72,6 +86,11 @@ size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
       return scalar_ws_bytes(prob, 3, false);
     case MSCAN_OP_SCAN_LOG_FWD:
       return scalar_ws_bytes(prob, 5, true);
+    case MSCAN_OP_MATRIX_FWD:
+    case MSCAN_OP_MATRIX_BWD:
+      if (!matrix_shape_ok(k, v)) return 0;
+      if (k == 1) return scalar_ws_bytes(prob, 3, true);
+      return matrix_ws_bytes(prob, k, v);
     default:
       return 0;
   }
@@ -175,16 +194,67 @@ mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const f
 mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,
                                     const float* B, const float* h0, float* h, void* ws,
                                     size_t ws_bytes, void* stream) {
-  (void)prob; (void)k; (void)v; (void)A; (void)B; (void)h0; (void)h; (void)ws; (void)ws_bytes; (void)stream;
-  return MSCAN_ERR_UNSUPPORTED;
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (!matrix_shape_ok(k, v)) return MSCAN_ERR_UNSUPPORTED;
+  if (k == 1) return scan_fwd(prob, MSCAN_F32, A, B, h0, h, ws, ws_bytes, stream);  // the scalar scan
+  if (!A || !B || !h) return MSCAN_ERR_INVALID;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(h) || (h0 && !aligned16(h0))) return MSCAN_ERR_INVALID;
+  const int64_t nt = mscan::matrix_tiles(prob->T, k, v, false);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+    return MSCAN_ERR_WORKSPACE;
+  mscan::MatArgs a{};
+  a.A = A;
+  a.B = B;
+  a.h0 = h0;
+  a.out0 = h;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse;
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_matrix(a, k, v, false, (hipStream_t)stream));
 }
 
 mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, const float* A,
                                     const float* h, const float* dy, const float* h0, float* dA,
                                     float* dB, float* dh0, void* ws, size_t ws_bytes, void* stream) {
-  (void)prob; (void)k; (void)v; (void)A; (void)h; (void)dy; (void)h0; (void)dA; (void)dB; (void)dh0;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return MSCAN_ERR_UNSUPPORTED;
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (!matrix_shape_ok(k, v)) return MSCAN_ERR_UNSUPPORTED;
+  if (k == 1) return scan_bwd(prob, MSCAN_F32, A, h, dy, h0, dB, dA, dh0, ws, ws_bytes, stream);
+  if (!A || !h || !dy || !dA || !dB) return MSCAN_ERR_INVALID;
+  if (!aligned16(A) || !aligned16(h) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB)) return MSCAN_ERR_INVALID;
+  if ((h0 && !aligned16(h0)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
+  const int64_t nt = mscan::matrix_tiles(prob->T, k, v, true);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+    return MSCAN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (dh0 && prob->cu_seqlens) {
+    const mscan_status z = hip_status(
+        mscan::launch_zero(dh0, (size_t)prob->nseg * (size_t)prob->rows * (size_t)(k * v) * 4u, st));
+    if (z != MSCAN_OK) return z;
+  }
+  mscan::MatArgs a{};
+  a.A = A;
+  a.B = dy;
+  a.hs = h;
+  a.h0 = h0;
+  a.out0 = dB;
+  a.out1 = dA;
+  a.dh0 = dh0;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse ? 0 : 1;  // the adjoint runs against the forward's order
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_matrix(a, k, v, true, st));
 }
 
 const char* mscan_status_string(int status) {

@@ -33,6 +33,29 @@ hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_
 // Log-space forward (g = log a, b = log b, h0 = log h0; fp32).
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st);
 
+// Arguments of the matrix-affine kernels (see scan_matrix.hip). Strides and
+// offsets count time steps; a step holds a k x k block of A and k x v blocks
+// of B / h / dy.
+struct MatArgs {
+  const float* A;       // transitions [rows][T][k][k]
+  const float* B;       // forward: injections B; backward: dy  ([rows][T][k][v])
+  const float* hs;      // backward: forward states h
+  const float* h0;      // [nseg][rows][k][v] or null
+  float* out0;          // forward: h; backward: dB
+  float* out1;          // backward: dA
+  float* dh0;           // backward: [nseg][rows][k][v] or null
+  const int32_t* cu;
+  int32_t nseg;
+  int32_t rev;          // processing order runs from high t to low t
+  int64_t rows, T, stride;
+  int32_t ntiles;
+  void* ws;
+};
+
+// Tiles per row of the matrix kernels for (k, v) (0 if unsupported).
+int64_t matrix_tiles(int64_t T, int k, int v, bool bwd);
+hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t st);
+
 // Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so
 // callers may capture it in a graph).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);

@@ -17,12 +17,13 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmscan.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("MSCAN_ARCH", "gfx950")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 # Packed fp32 VALU ops are disabled: the kernels get no v_pk_{add,mul,fma}_f32.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
 ]
 
 

@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/mscan.h"
+#include "mscan.h"
 #include "mscan_device.hpp"
 #include "mscan_launch.hpp"
 
@@ -40,8 +40,8 @@ int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
 }
 
 // Workspace for a scalar-layout op: header, then (only when rows are chained by
-// look-back) one epoch word per row and `words` descriptor words per tile
-// (3 for the linear scan, 5 for the log-space scan).
+// look-back) `words` descriptor words per tile (3 for the linear scan, 5 for
+// the log-space scan).
 size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
   int64_t nt = 0;
   for (int dt = MSCAN_F32; dt <= (f32_only ? MSCAN_F32 : MSCAN_BF16); ++dt) {
@@ -49,7 +49,7 @@ size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
     if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
   }
   if (nt == 0) return mscan::kWsHeaderBytes;
-  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * (size_t)words * sizeof(uint64_t);
+  return mscan::ws_desc_offset() + (size_t)p->rows * (size_t)nt * (size_t)words * sizeof(uint64_t);
 }
 
 mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
@@ -58,8 +58,8 @@ mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
   return MSCAN_OK;
 }
 
-// Workspace of a matrix op: header, then (look-back only) per-row epochs and
-// k*k + 2*k*v descriptor words per tile.
+// Workspace of a matrix op: header, then (look-back only) k*k + 2*k*v
+// descriptor words per tile.
 size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
   int64_t nt = 0;
   for (int b = 0; b < 2; ++b) {
@@ -67,7 +67,7 @@ size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
     if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
   }
   if (nt == 0) return mscan::kWsHeaderBytes;
-  return mscan::ws_desc_offset(p->rows) + (size_t)p->rows * (size_t)nt * (size_t)(k * k + 2 * k * v) * sizeof(uint64_t);
+  return mscan::ws_desc_offset() + (size_t)p->rows * (size_t)nt * (size_t)(k * k + 2 * k * v) * sizeof(uint64_t);
 }
 
 bool matrix_shape_ok(int k, int v) {

@@ -61,19 +61,18 @@ __device__ __forceinline__ float lin_apply(float P, float Q, float h) {
 }
 
 // ---------------------------------------------------------------------------
-// Workspace: control header, one epoch word per row, descriptor words per tile.
+// Workspace: a control header followed by the descriptor words of every tile.
 //
 // Every descriptor word is 64 bits, {tag:32 | value:32}, written and read with
 // relaxed agent-scope atomics, so each word is self-validating and no fence is
-// needed between words. tag = (epoch << 2) | kind, kind 1 = aggregate of the
-// tile alone, 2 = inclusive value (the state at the tile's end). Each row has
-// its own epoch, which the row's last tile advances once its look-back has
-// finished (by then every tile of the row has read the epoch), so words from
-// earlier calls never look valid, nothing needs clearing between calls and no
-// atomic read-modify-write touches a shared address.
+// needed between words. tag 1 = aggregate of the tile alone, tag 2 = inclusive
+// value (the state at the tile's end). The library zero-fills the words a call
+// uses (a small kernel on the same stream) right before the scan kernel, so a
+// zero tag always means "not published yet" and nothing from an earlier call,
+// of any shape, can look valid.
 // ---------------------------------------------------------------------------
 enum : int { kHdrError = 3, kHdrWords = 32 };
-enum : uint32_t { kKindAgg = 1, kKindIncl = 2 };
+enum : uint32_t { kTagAgg = 1, kTagIncl = 2 };
 
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -94,21 +93,17 @@ __device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >
 __device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 struct Workspace {
-  uint32_t* hdr;    // kHdrWords 32-bit control words
-  uint32_t* epoch;  // one word per row
-  uint64_t* desc;   // per-tile descriptor words
+  uint32_t* hdr;   // kHdrWords 32-bit control words
+  uint64_t* desc;  // per-tile descriptor words
 };
 
-// Byte offset of the descriptors: header + per-row epochs rounded up to 16 bytes.
-__host__ __device__ __forceinline__ size_t ws_desc_offset(int64_t rows) {
-  return (size_t)kHdrWords * 4 + (((size_t)rows * 4 + 15) & ~(size_t)15);
-}
+// Byte offset of the descriptors (after the control header).
+__host__ __device__ __forceinline__ constexpr size_t ws_desc_offset() { return (size_t)kHdrWords * 4; }
 
-__device__ __forceinline__ Workspace ws_view(void* ws, int64_t rows) {
+__device__ __forceinline__ Workspace ws_view(void* ws) {
   Workspace w;
   w.hdr = (uint32_t*)ws;
-  w.epoch = (uint32_t*)((char*)ws + kHdrWords * 4);
-  w.desc = (uint64_t*)((char*)ws + ws_desc_offset(rows));
+  w.desc = (uint64_t*)((char*)ws + ws_desc_offset());
   return w;
 }
 
@@ -232,17 +227,13 @@ __device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
 // by NC inclusive words (the state at the tile's end). Run by one whole wave;
 // returns the state entering tile `c` of the row whose first descriptor set
 // is `row_desc`.
-// With `full`, the wave also waits until every earlier tile of the row has
-// published (the row's last tile uses this before it advances the row's
-// epoch, so that no tile of the row can still be about to read it).
 // ---------------------------------------------------------------------------
 template <class Ops>
-__device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c,
-                                                    uint32_t epoch, bool full) {
+__device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c) {
   using S = typename Ops::S;
   constexpr int ND = Ops::NS + Ops::NC;
   const int l = lane_id();
-  const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+  const uint32_t tagA = kTagAgg, tagI = kTagIncl;
   S acc = Ops::ident();  // composition of the tiles already passed (later ones)
   bool found = false;    // acc already ends on an inclusive value
   int j = c - 1;
@@ -295,7 +286,7 @@ __device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t*
       }
       const uint64_t incl_mask = __ballot(is_incl);
       stop = incl_mask ? __builtin_ctzll(incl_mask) : 64;
-      const uint64_t need = (full || stop >= 63) ? ~0ull : ((2ull << stop) - 1ull);
+      const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1ull);
       const uint64_t not_ready = __ballot(!ready) & need;
       if (not_ready == 0) break;
       if (++spins > kSpinLimit) {
@@ -320,8 +311,7 @@ __device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t*
       Ops::compose(win, acc);
       found = stop < 64;
     }
-    if (j < 64) break;            // this window reached the row's first tile
-    if (found && !full) break;    // an inclusive value closes the composition
+    if (found || j < 64) break;  // an inclusive value, or the row's first tile, closes it
     j -= 64;
   }
   return Ops::carry_of_hard(acc);  // acc ends on an inclusive value: it is hard

@@ -103,7 +103,10 @@ struct MatOps {
   }
 };
 
-// n floats from a 16-byte (n % 4 == 0) or 8-byte (n == 2) aligned address
+// n floats from a 16-byte (n % 4 == 0) or 8-byte (n == 2) aligned address.
+// Cached accesses on purpose: the lanes of a wave touch lane-strided parts of
+// the same lines over several instructions, and those lines must stay in L1/L2
+// between them (non-temporal accesses measured several times slower here).
 template <int N>
 __device__ __forceinline__ void vload(const float* p, float* o) {
   if constexpr (N % 4 == 0) {
@@ -128,12 +131,12 @@ __device__ __forceinline__ void vstore(float* p, const float* v) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) {
       const v4f t = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-      __builtin_nontemporal_store(t, (v4f*)(p + 4 * i));
+      *(v4f*)(p + 4 * i) = t;
     }
   } else if constexpr (N == 2) {
     typedef float v2f __attribute__((ext_vector_type(2)));
     const v2f t = {v[0], v[1]};
-    __builtin_nontemporal_store(t, (v2f*)p);
+    *(v2f*)p = t;
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) p[i] = v[i];
@@ -186,11 +189,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
   const bool has_h0 = a.h0 != nullptr;
 
   Workspace ws{};
-  uint32_t epoch = 0;
-  if constexpr (MODE == kMatLookback) {
-    ws = ws_view(a.ws, a.rows);
-    epoch = ld_u32(ws.epoch + r);
-  }
+  if constexpr (MODE == kMatLookback) ws = ws_view(a.ws);
 
   // sequence table: cached whole in LDS when it fits, else read from memory
   const int32_t* cuv = a.cu;
@@ -219,6 +218,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     // ---- load ---------------------------------------------------------------
     // fwd: Am = A_t, Bm = B_t. bwd: Am = A_t (own), Bm = dy_t, Hm = h_t.
     float Am[EL][KK], Bm[EL][KV], Hm[BWD ? EL : 1][KV];
+    // a tile wholly inside the row issues every load unconditionally, so all
+    // of them are in flight together; only a row's last tile checks steps
+    const bool interior = (int64_t)(c + 1) * TILE <= T;
+    if (interior) {
+#pragma unroll
+      for (int e = 0; e < EL; ++e) {
+        const int64_t t = phys(j0 + e);
+        vload<KK>(a.A + (row0 + t) * KK, Am[e]);
+        vload<KV>(a.B + (row0 + t) * KV, Bm[e]);
+        if constexpr (BWD) vload<KV>(a.hs + (row0 + t) * KV, Hm[e]);
+      }
+    } else {
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
       const int64_t t = phys(j0 + e);
@@ -237,6 +248,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
           for (int i = 0; i < KV; ++i) Hm[e][i] = 0.f;
         }
       }
+    }
     }
 
     // ---- sequence boundaries ----------------------------------------------------
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
       uint64_t* rd = ws.desc + (int64_t)ND * ((int64_t)r * a.ntiles);
       uint64_t* my = rd + (int64_t)ND * c;
       if (w == 0) {
-        const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+        const uint32_t tagA = kTagAgg, tagI = kTagIncl;
         const bool hard = Ops::hard(tagg);
         if (l == 0) {
           if (!hard) {
@@ -396,14 +408,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
         }
-        if (c > 0) carry = lookback<Ops>(ws, rd, c, epoch, c == a.ntiles - 1);
+        if (c > 0) carry = lookback<Ops>(ws, rd, c);
         if (l == 0) {
           if (!hard) {
             const C inc = Ops::apply(tagg, carry);
 #pragma unroll
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
-          if (c == a.ntiles - 1) st_u32(ws.epoch + r, (epoch + 1u) & 0x3fffffffu);
 #pragma unroll
           for (int i = 0; i < NC; ++i) s_carry[i] = carry.v[i];
         }
@@ -502,6 +513,10 @@ static hipError_t launch_mat(const MatArgs& a0, hipStream_t st) {
     if (varlen) hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, true, kMatRowLoop, W, E>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, false, kMatRowLoop, W, E>), grid, block, 0, st, a);
   } else {
+    // fresh descriptors for this call (zero tag = not published)
+    const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(MatOps<K, V>::NS + MatOps<K, V>::NC);
+    const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
+    if (z != hipSuccess) return z;
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
     if (varlen) hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, true, kMatLookback, W, E>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, false, kMatLookback, W, E>), grid, block, 0, st, a);

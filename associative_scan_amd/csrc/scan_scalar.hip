@@ -25,10 +25,12 @@
 //   the waves = chained through LDS.
 // Across the tiles of a row, two modes:
 //   row loop : one workgroup walks its row tile by tile and carries the state
-//              in registers (used whenever there are enough rows to fill the
-//              GPU; no inter-workgroup traffic, deterministic);
-//   look-back: one workgroup per tile; tiles of a row chain by decoupled
-//              look-back through the workspace (few, long rows).
+//              in registers; used when a row fits in one tile (no workspace,
+//              no inter-workgroup traffic);
+//   look-back: one workgroup per tile; the tiles of a row chain by decoupled
+//              look-back through the workspace. Used whenever a row spans
+//              several tiles: it keeps more bytes in flight per CU than the
+//              row loop and measured faster at every benchmark row count.
 // Rows whose start is not 16-byte aligned are handled by aligning vector
 // groups to absolute addresses and masking the elements outside the row.
 #include "mscan_device.hpp"
@@ -46,7 +48,7 @@ template <>
 struct InTraits<float> {
   static constexpr int VEC = 4;  // elements per 16-byte vector
   __device__ static __forceinline__ void load16(const float* p, float* o) {
-    const v4f v = *(const v4f*)p;
+    const v4f v = __builtin_nontemporal_load((const v4f*)p);  // streamed once
     o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
   }
   __device__ static __forceinline__ float load1(const float* p) { return *p; }
@@ -56,7 +58,7 @@ template <>
 struct InTraits<uint16_t> {  // bf16 bit patterns, widened exactly
   static constexpr int VEC = 8;
   __device__ static __forceinline__ void load16(const uint16_t* p, float* o) {
-    const v4u v = *(const v4u*)p;
+    const v4u v = __builtin_nontemporal_load((const v4u*)p);  // streamed once
     o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
     o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
@@ -171,11 +173,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   const float h0row = (!VARLEN && has_h0) ? h0p[r] : 0.f;
 
   Workspace ws{};
-  uint32_t epoch = 0;
-  if constexpr (MODE == kLookback) {
-    ws = ws_view(a.ws, a.rows);
-    epoch = ld_u32(ws.epoch + r);
-  }
+  if constexpr (MODE == kLookback) ws = ws_view(a.ws);
 
   // ---- sequence table ------------------------------------------------------
   SegSlice seg{nullptr, 0, 0};
@@ -337,8 +335,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       } else {
         // walk the elements in physical order against the sequence table
         const int64_t q0 = u0 - lead;
+        int k = 0;
+        bool walk = false;
         if (seg.n > 0) {
-          int k = slice_find(seg, max(q0, (int64_t)0));
+          k = slice_find(seg, max(q0, (int64_t)0));
+          // a sequence starts or ends inside [q0, q0 + EL) only if the found
+          // start is q0 or the next start is at most q0 + EL
+          const int64_t next = (k + 1 < seg.n) ? (int64_t)seg.v[k + 1] : INT64_MAX;
+          walk = ((int64_t)seg.v[k] >= q0) || (next <= q0 + EL);
+        }
+        if (walk) {
 #pragma unroll
           for (int ep = 0; ep < EL; ++ep) {
             const int64_t q = q0 + ep;
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       uint64_t* rd = ws.desc + (int64_t)ND * ((int64_t)r * a.ntiles);
       uint64_t* my = rd + (int64_t)ND * c;
       if (w == 0) {
-        const uint32_t tagA = (epoch << 2) | kKindAgg, tagI = (epoch << 2) | kKindIncl;
+        const uint32_t tagA = kTagAgg, tagI = kTagIncl;
         const bool hard = Ops::hard(tagg);
         if (l == 0) {
           if (!hard) {
@@ -449,16 +455,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
         }
-        if (c > 0) carry = lookback<Ops>(ws, rd, c, epoch, c == a.ntiles - 1);
+        if (c > 0) carry = lookback<Ops>(ws, rd, c);
         if (l == 0) {
           if (!hard) {
             const C inc = Ops::apply(tagg, carry);
 #pragma unroll
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
-          // the last tile's look-back waited for every earlier tile of the row
-          // to publish, so all of them have read this call's epoch: advance it
-          if (c == a.ntiles - 1) st_u32(ws.epoch + r, (epoch + 1u) & 0x3fffffffu);
 #pragma unroll
           for (int i = 0; i < NC; ++i) s_carry[i] = carry.v[i];
         }
@@ -532,8 +535,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 // ---------------------------------------------------------------------------
 // host launch
 // ---------------------------------------------------------------------------
-// Rows at or above this count fill the GPU with one workgroup per row.
-constexpr int64_t kRowLoopMinRows = 1024;
 
 template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
@@ -548,6 +549,10 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
     if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
   } else {
+    // fresh descriptors for this call (zero tag = not published)
+    const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(Ops::NS + Ops::NC);
+    const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
+    if (z != hipSuccess) return z;
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
     if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
@@ -566,7 +571,13 @@ int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
   return (umax + tile - 1) / tile;
 }
 
-bool scalar_uses_lookback(int64_t rows, int64_t ntiles) { return ntiles > 1 && rows < kRowLoopMinRows; }
+// One workgroup per tile, chained by look-back, whenever a row spans several
+// tiles: measured faster than walking rows in one workgroup (more bytes in
+// flight per CU), at every row count of the benchmark workloads.
+bool scalar_uses_lookback(int64_t rows, int64_t ntiles) {
+  (void)rows;
+  return ntiles > 1;
+}
 
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
   const bool rev = a.rev != 0;

@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--T", type=int, default=4096)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-workloads", action="store_true", help="skip the packed, log-space and matrix workloads")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also launch one plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -185,6 +186,11 @@ def main():
             del gs, xs, dys
             torch.cuda.empty_cache()
 
+    # ---- the other workloads of the scan family (performance only) -----------
+    workloads = {}
+    if not args.no_workloads:
+        workloads = other_workloads(m, gen, torch, dev, stream, np)
+
     # ---- CPU baseline: the fp64 oracle on the host ----------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -245,9 +251,106 @@ def main():
         "copy_ceiling_gbps": round(copy_ceiling, 1),
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "workloads": workloads,
         "kernel_source_sha": source_sha(),
     }
     print(json.dumps(rec), flush=True)
+
+
+def _time(torch, stream, fn, reps):
+    """Average per-call milliseconds of fn() over reps back-to-back calls."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _entry(nbytes, ms, unit_count, unit):
+    return {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            f"{unit}_per_s": round(unit_count / (ms * 1e-3), 1), "bytes": nbytes}
+
+
+def other_workloads(m, gen, torch, dev, stream, np):
+    """Packed bidirectional bf16, log-space and matrix-affine workloads at their
+    full shapes. Inputs are drawn on the device with the workloads'
+    distributions (values do not affect the timing); parity of the same
+    shapes is checked by the GPU tests."""
+    out = {}
+    gt = torch.Generator(device=dev)
+    gt.manual_seed(2024)
+
+    # packed variable-length, two branches in opposite directions, bf16 inputs
+    C, Tt = 1536, 65536
+    L = gen.varlen_lengths(np.random.default_rng(3), 16, Tt, 8192)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(L)]), dtype=torch.int32, device=dev)
+    br = []
+    for _ in range(2):
+        g = torch.sigmoid(torch.randn((C, Tt), device=dev, generator=gt) + 2.0)
+        g[:, torch.rand(Tt, device=dev, generator=gt) < 1.0 / 1024] = 0.0
+        br.append((g.to(torch.bfloat16), torch.randn((C, Tt), device=dev, generator=gt).to(torch.bfloat16)))
+    dy = torch.randn((C, Tt), device=dev, generator=gt)
+    n = C * Tt
+
+    def vf():
+        return [m.scan_fwd(b[0], b[1], cu_seqlens=cu, reverse=(i == 1)) for i, b in enumerate(br)]
+
+    def vfb():
+        hs = vf()
+        for i, b in enumerate(br):
+            m.scan_bwd(b[0], hs[i], dy, cu_seqlens=cu, reverse=(i == 1), need_dh0=False)
+
+    out["varlen_bidir_bf16"] = {
+        "workload": "C=1536, 65536 packed tokens in 16 sequences, bf16 g and x, fp32 h, two branches (causal + reverse)",
+        "fwd": _entry(2 * 8 * n, _time(torch, stream, vf, 10), 2 * n, "elements"),
+        "fwd_bwd": _entry(2 * (8 + 18) * n, _time(torch, stream, vfb, 10), 2 * n, "elements")}
+    del br, dy
+    torch.cuda.empty_cache()
+
+    # log space
+    B, D, T = 8, 1024, 8192
+    la = -torch.nn.functional.softplus(torch.randn((B, D, T), device=dev, generator=gt))
+    lb = torch.randn((B, D, T), device=dev, generator=gt)
+    n = B * D * T
+    out["logspace"] = {"workload": "B=8 D=1024 T=8192 fp32, log_a = -softplus(N(0,1)), log_b ~ N(0,1)",
+                       "fwd": _entry(12 * n, _time(torch, stream, lambda: m.scan_log_fwd(la, lb), 10), n, "elements")}
+    del la, lb
+    torch.cuda.empty_cache()
+
+    # matrix-affine: rotations (k=2, v=1) and scaled orthogonal blocks (k=4, v=4)
+    R, T = 8 * 512, 8192
+    for name, k, v in (("matrix_rot2", 2, 1), ("matrix_orth4", 4, 4)):
+        if k == 2:
+            rr = 0.5 + 0.5 * torch.rand((R, T), device=dev, generator=gt)
+            th = (torch.rand((R, T), device=dev, generator=gt) * 2 - 1) * np.pi
+            A = torch.stack([torch.stack([rr * th.cos(), -rr * th.sin()], -1),
+                             torch.stack([rr * th.sin(), rr * th.cos()], -1)], -2)
+            del rr, th
+        else:
+            A = torch.randn((R, T, 4, 4), device=dev, generator=gt)
+            for j in range(4):  # Gram-Schmidt on the columns
+                for i in range(j):
+                    A[..., :, j] -= (A[..., :, i] * A[..., :, j]).sum(-1, keepdim=True) * A[..., :, i]
+                A[..., :, j] /= A[..., :, j].norm(dim=-1, keepdim=True)
+            A *= 0.9
+        A[torch.rand((R, T), device=dev, generator=gt) < 1.0 / 2048] = 0.0
+        Bm = torch.randn((R, T, k, v), device=dev, generator=gt)
+        dyk = torch.randn((R, T, k, v), device=dev, generator=gt)
+        h = m.matrix_affine_scan_fwd(A, Bm)
+        fb, bb = 4 * (k * k + 2 * k * v), 4 * (2 * k * k + 3 * k * v)
+        steps = R * T
+        tf = _time(torch, stream, lambda: m.matrix_affine_scan_fwd(A, Bm), 5)
+        tb = _time(torch, stream, lambda: m.matrix_affine_scan_bwd(A, h, dyk, need_dh0=False), 5)
+        out[name] = {"workload": f"B=8 x 512 state blocks, T=8192, k={k} v={v}, fp32, resets 1/2048",
+                     "fwd": _entry(fb * steps, tf, steps, "steps"), "bwd": _entry(bb * steps, tb, steps, "steps")}
+        del A, Bm, dyk, h
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -43,10 +43,11 @@
  *              "Kernel design": accumulation is fp32 regardless of input
  *              dtype).
  *  Workspace.  Calls that split a row into several tiles chain them through a
- *              small device workspace of mscan_workspace_bytes() bytes. It must
- *              be zero-filled (mscan_workspace_init) once before its first
- *              use; every call leaves it ready for the next. Calls that overlap
- *              in time (different streams) must not share a workspace.
+ *              small device workspace of mscan_workspace_bytes() bytes (about
+ *              0.2% of the inputs). The call itself clears the part it uses,
+ *              with a small fill kernel on `stream` before the scan kernel, so
+ *              the contents between calls do not matter. Calls that overlap in
+ *              time (different streams) must not share a workspace.
  *  Errors.     Arguments are validated on the host before any HIP call:
  *              MSCAN_ERR_INVALID (null required pointer, bad sizes, misaligned
  *              pointer, nseg inconsistent with cu_seqlens), MSCAN_ERR_UNSUPPORTED
@@ -107,7 +108,8 @@ typedef struct {
  * Pure host function; returns 0 when the problem is invalid. */
 MSCAN_API size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v);
 
-/* Zero-fill a workspace before its first use (enqueues one small fill kernel). */
+/* Zero-fill a workspace (one small fill kernel on `stream`). Optional: every
+ * call clears the part of the workspace it uses. */
 MSCAN_API mscan_status mscan_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Scalar forward scan (associative-scan-triton README, intro and quick start:

@@ -52,16 +52,17 @@ def _prob(m, rows=8, T=100, stride=None, cu=None, nseg=1, reverse=0):
 
 
 def test_workspace_sizes(m):
-    # rows >= 1024: one workgroup walks each row, only the control header is used
+    # a row that fits one 4096-element tile never chains tiles: header only
     assert m.workspace_bytes(_prob(m, rows=12288, T=4096), m.OP_SCAN_FWD) == 128
-    assert m.workspace_bytes(_prob(m, rows=12288, T=65536), m.OP_SCAN_FWD) == 128
-    # a single tile per row never chains tiles
     assert m.workspace_bytes(_prob(m, rows=3, T=4096), m.OP_SCAN_FWD) == 128
-    # few long rows chain tiles by look-back: header (128) + per-row epochs
-    # rounded to 16 bytes + 3 words of 8 bytes per tile of 4096 elements
-    assert m.workspace_bytes(_prob(m, rows=3, T=65536), m.OP_SCAN_FWD) == 128 + 16 + 3 * 16 * 24
+    # longer rows chain tiles by look-back: header (128) + 3 words of 8 bytes
+    # per tile of 4096 elements
+    assert m.workspace_bytes(_prob(m, rows=12288, T=65536), m.OP_SCAN_FWD) == 128 + 12288 * 16 * 24
+    # the log-space scan publishes 5 words per tile
+    assert m.workspace_bytes(_prob(m, rows=3, T=65536), m.OP_SCAN_LOG_FWD) == 128 + 3 * 16 * 40
+    assert m.workspace_bytes(_prob(m, rows=3, T=65536), m.OP_SCAN_FWD) == 128 + 3 * 16 * 24
     # rows that do not all start 16-byte aligned may need one more tile
-    assert m.workspace_bytes(_prob(m, rows=3, T=8190, stride=8193), m.OP_SCAN_FWD) == 128 + 16 + 3 * 3 * 24
+    assert m.workspace_bytes(_prob(m, rows=3, T=8190, stride=8193), m.OP_SCAN_FWD) == 128 + 3 * 3 * 24
     assert m.workspace_bytes(_prob(m, rows=0), m.OP_SCAN_FWD) == 0
     assert m.workspace_bytes(_prob(m, T=10, stride=5), m.OP_SCAN_FWD) == 0
 

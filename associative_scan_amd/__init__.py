@@ -61,7 +61,7 @@ class Problem(ctypes.Structure):
 def _load():
     if not os.path.exists(library_path):
         raise ImportError(
-            f"libmscan.so not found at {library_path}; build it with `python -m associative_scan_amd.build`")
+            f"libmscan.so not found at {library_path}; build it with `python associative_scan_amd/build.py`")
     L = ctypes.CDLL(library_path)
     P, p, sz, i32 = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     sig = {

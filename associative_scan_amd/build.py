@@ -1,6 +1,7 @@
 """Build libmscan.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m associative_scan_amd.build   (or call build()).
+Usage: python associative_scan_amd/build.py   (or call build()); run as a
+script, since importing the package needs the library this builds.
 Each source compiles to an object under associative_scan_amd/_build/, in
 parallel, then links into associative_scan_amd/libmscan.so.
 """

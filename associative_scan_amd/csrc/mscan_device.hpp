@@ -22,6 +22,7 @@ namespace mscan {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // DPP lane movement (GFX9 encodings; gfx950 keeps the wave-wide shifts)

@@ -46,35 +46,37 @@ struct InTraits;
 
 template <>
 struct InTraits<float> {
-  static constexpr int VEC = 4;  // elements per 16-byte vector
-  __device__ static __forceinline__ void load16(const float* p, float* o) {
+  static constexpr int VEC = 4;  // elements per vector load (16 bytes)
+  __device__ static __forceinline__ void loadv(const float* p, float* o) {
     const v4f v = __builtin_nontemporal_load((const v4f*)p);  // streamed once
     o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
   }
   __device__ static __forceinline__ float load1(const float* p) { return *p; }
 };
 
+// bf16 bit patterns, widened exactly. Four elements (8 bytes) per lane and
+// load, so that a lane's fp32 outputs are one 16-byte store and the stores of
+// a wave stay fully coalesced (two 16-byte stores per lane, 32 bytes apart,
+// measured markedly slower).
 template <>
-struct InTraits<uint16_t> {  // bf16 bit patterns, widened exactly
-  static constexpr int VEC = 8;
-  __device__ static __forceinline__ void load16(const uint16_t* p, float* o) {
-    const v4u v = __builtin_nontemporal_load((const v4u*)p);  // streamed once
+struct InTraits<uint16_t> {
+  static constexpr int VEC = 4;
+  __device__ static __forceinline__ void loadv(const uint16_t* p, float* o) {
+    const v2u v = __builtin_nontemporal_load((const v2u*)p);  // streamed once
     o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
     o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
-    o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xffff0000u);
-    o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xffff0000u);
   }
   __device__ static __forceinline__ float load1(const uint16_t* p) {
     return __uint_as_float((uint32_t)(*p) << 16);
   }
 };
 
-// N consecutive elements starting at a 16-byte aligned address
+// N consecutive elements starting at a vector-aligned address
 template <typename T, int N>
 __device__ __forceinline__ void load_span(const T* p, float (&o)[N]) {
   constexpr int V = InTraits<T>::VEC;
 #pragma unroll
-  for (int i = 0; i < N / V; ++i) InTraits<T>::load16(p + i * V, o + i * V);
+  for (int i = 0; i < N / V; ++i) InTraits<T>::loadv(p + i * V, o + i * V);
 }
 
 template <int N>
@@ -560,9 +562,9 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile shape per input type: 4 waves x 4096 elements per tile.
-int64_t scalar_tile_elems(int in_dtype) { return in_dtype == 0 ? 4 * 4 * 64 * 4 : 4 * 2 * 64 * 8; }
-int scalar_vec(int in_dtype) { return in_dtype == 0 ? 4 : 8; }
+// Tile shape, every input type: 4 waves x 4 sub-chunks x 64 lanes x 4 elements.
+int64_t scalar_tile_elems(int) { return 4 * 4 * 64 * 4; }
+int scalar_vec(int) { return 4; }
 
 int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
   // padded row length: rows all start aligned when the stride is a multiple of
@@ -585,8 +587,8 @@ hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_
     if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, true, false, 4, 4, 1>(a, st);
     return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, false, false, 4, 4, 1>(a, st);
   }
-  if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 2, 1>(a, st) : launch_cfg<LinOps, uint16_t, true, false, 4, 2, 1>(a, st);
-  return rev ? launch_cfg<LinOps, uint16_t, false, true, 4, 2, 1>(a, st) : launch_cfg<LinOps, uint16_t, false, false, 4, 2, 1>(a, st);
+  if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, uint16_t, true, false, 4, 4, 1>(a, st);
+  return rev ? launch_cfg<LinOps, uint16_t, false, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, uint16_t, false, false, 4, 4, 1>(a, st);
 }
 
 // Log-space forward: fp32 (log a, log b), same tiles as the fp32 scalar scan.

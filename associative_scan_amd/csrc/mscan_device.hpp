@@ -223,6 +223,19 @@ __device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
   if (valid) Ops::compose(e, x);
 }
 
+// Row and tile of this workgroup in look-back mode. Blocks are numbered
+// tile-major (block = c * rows + r): every row's tile c is dispatched before
+// any row's tile c + 1, so by the time a tile looks back its predecessor has
+// usually published its inclusive value and one descriptor read settles the
+// carry. Tiles still wait only on lower-numbered blocks of their own row,
+// which were dispatched earlier, so the look-back always makes progress.
+__device__ __forceinline__ void tile_of_block(int64_t rows, int64_t& r, int& c) {
+  const uint32_t b = blockIdx.x, nr = (uint32_t)rows;
+  const uint32_t q = b / nr;
+  c = (int)q;
+  r = (int64_t)(b - q * nr);
+}
+
 // ---------------------------------------------------------------------------
 // Decoupled look-back. Descriptor set of tile i = NS aggregate words followed
 // by NC inclusive words (the state at the tile's end). Run by one whole wave;
@@ -235,6 +248,27 @@ __device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t*
   constexpr int ND = Ops::NS + Ops::NC;
   const int l = lane_id();
   const uint32_t tagA = kTagAgg, tagI = kTagIncl;
+  // fast path: the immediate predecessor has published its inclusive value
+  {
+    bool ok = true;
+    typename Ops::C cc;
+#pragma unroll
+    for (int i = 0; i < Ops::NC; ++i) cc.v[i] = 0.f;
+    if (l == 0) {
+      const uint64_t* d = row_desc + (int64_t)ND * (c - 1);
+#pragma unroll
+      for (int i = 0; i < Ops::NC; ++i) {
+        const uint64_t wi = ld_u64(d + Ops::NS + i);
+        ok = ok && (word_tag(wi) == tagI);
+        cc.v[i] = word_val(wi);
+      }
+    }
+    if (__builtin_amdgcn_readfirstlane((int)ok)) {
+#pragma unroll
+      for (int i = 0; i < Ops::NC; ++i) cc.v[i] = readlane_f(cc.v[i], 0);
+      return cc;
+    }
+  }
   S acc = Ops::ident();  // composition of the tiles already passed (later ones)
   bool found = false;    // acc already ends on an inclusive value
   int j = c - 1;

@@ -9,12 +9,26 @@
 // is bound by HBM bandwidth and the blocks are far too small for matrix cores,
 // and fp32 VALU keeps the precision the page's precision guard asks for.
 //
-// Layout: one lane owns EL consecutive time steps; a step's k x k and k x v
-// blocks are contiguous, loaded as 16-byte vectors. A tile is WAVES waves x 64
-// lanes x EL steps. Inside a tile the steps are summarised per lane as
-// (P, Q) = (product of the A's, accumulated B's), scanned across the wave with
-// DPP, and across waves through LDS; across tiles the row-loop / look-back
-// modes of the scalar kernels apply unchanged (see scan_scalar.hip).
+// Work decomposition. A wave owns a window of 64 x EL consecutive time steps;
+// a tile is WAVES such windows. Each array of the window (A, B or dy, h) is
+// staged in LDS:
+//   - global -> LDS by direct loads (global_load_lds), 1 KiB per wave
+//     instruction, so HBM sees only fully coalesced 16-byte accesses and no
+//     VGPR holds data in flight;
+//   - lane l owns EL consecutive steps and reads them from LDS; the 16-byte
+//     units are XOR-swizzled (a permutation inside each aligned group of 16
+//     units) so that those lane-owned reads hit distinct banks, while every
+//     load or store instruction still covers one aligned block of memory;
+//   - outputs are written back into the slots of the inputs they replace and
+//     leave LDS with coalesced 16-byte stores.
+// Inside a tile the steps are summarised per lane as (P, Q) = (product of the
+// A's, accumulated B's), scanned across the wave with DPP and across waves
+// through LDS; across tiles the row-loop / look-back modes of the scalar
+// kernels apply unchanged (see scan_scalar.hip).
+//
+// Tiles are aligned to the row start in both directions; with `reverse` the
+// row is processed from its last tile down, each tile from its last window,
+// each window from lane 63's block, each block from its last step.
 //
 // Backward: processing order is the reverse of the forward's; element j is
 // (A of the step before it in that order, transposed; dy_j), a sequence's
@@ -56,7 +70,7 @@ struct MatOps {
     return z;
   }
   __device__ static __forceinline__ bool hard(const S& s) { return zero_k(s.v); }
-  // out = M * X for M k x k and X k x n (row-major), plus optional addend
+  // out = M * X (+ add) for M k x k and X k x n, row-major
   template <int N>
   __device__ static __forceinline__ void mul(const float* M, const float* X, const float* add, float* out) {
 #pragma unroll
@@ -69,13 +83,41 @@ struct MatOps {
         out[i * N + c] = acc;
       }
   }
-  // l := (e then l); a zero l.P keeps l (a reset or a sequence start)
+  // s := (M sP, M sQ + add), one row of the result at a time (row i needs
+  // only row i of M, and all of s, so rows are written after all are formed)
+  __device__ static __forceinline__ void premul(const float* M, S& s, const float* add) {
+    S r;
+    mul<K>(M, s.v, nullptr, r.v);
+    mul<V>(M, s.v + KK, add, r.v + KK);
+    s = r;
+  }
+  // l := (e then l) = (lP eP, lP eQ + lQ), in place one row of l at a time
+  // (row i of the result needs only row i of l); a zero l.P keeps l (a reset
+  // or a sequence start)
   __device__ static __forceinline__ void compose(const S& e, S& l) {
     if (zero_k(l.v)) return;
-    S r;
-    mul<K>(l.v, e.v, nullptr, r.v);
-    mul<V>(l.v, e.v + KK, l.v + KK, r.v + KK);
-    l = r;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float rp[K], rq[V];
+#pragma unroll
+      for (int c = 0; c < K; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) acc = __builtin_fmaf(l.v[i * K + j], e.v[j * K + c], acc);
+        rp[c] = acc;
+      }
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        float acc = l.v[KK + i * V + c];
+#pragma unroll
+        for (int j = 0; j < K; ++j) acc = __builtin_fmaf(l.v[i * K + j], e.v[KK + j * V + c], acc);
+        rq[c] = acc;
+      }
+#pragma unroll
+      for (int c = 0; c < K; ++c) l.v[i * K + c] = rp[c];
+#pragma unroll
+      for (int c = 0; c < V; ++c) l.v[KK + i * V + c] = rq[c];
+    }
   }
   __device__ static __forceinline__ C apply(const S& s, const C& c) {
     C r;
@@ -103,44 +145,118 @@ struct MatOps {
   }
 };
 
-// n floats from a 16-byte (n % 4 == 0) or 8-byte (n == 2) aligned address.
-// Cached accesses on purpose: the lanes of a wave touch lane-strided parts of
-// the same lines over several instructions, and those lines must stay in L1/L2
-// between them (non-temporal accesses measured several times slower here).
-template <int N>
-__device__ __forceinline__ void vload(const float* p, float* o) {
-  if constexpr (N % 4 == 0) {
+// ---------------------------------------------------------------------------
+// LDS staging of one array over a wave window
+// ---------------------------------------------------------------------------
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// N floats per step, EL steps per lane, 64 lanes. The window's floats are cut
+// into 16-byte units; lane l owns units [l*LU, (l+1)*LU). Unit u is kept at
+// LDS unit swz(u) = u ^ ((u >> SH) & MSK): that flips only the low 4 bits (so
+// u stays in its aligned group of 16 units, and each group of 16 / 64 units
+// is still one contiguous block of memory) and spreads the lanes that read
+// unit c of their blocks over 16 different 16-byte bank groups. swz is its
+// own inverse.
+template <int N, int EL>
+struct Stage {
+  static constexpr int FLOATS = N * 64 * EL;  // floats per window
+  static constexpr int UNITS = FLOATS / 4;
+  static constexpr int LU = N * EL / 4;       // units per lane
+  static_assert((N * EL) % 4 == 0 && (LU & (LU - 1)) == 0, "lane blocks must be whole powers-of-two of units");
+  static constexpr int SH = LU >= 16 ? ilog2c(LU) : 4;
+  static constexpr int MSK = (LU >= 16 ? 16 : LU) - 1;
+  __device__ static __forceinline__ int swz(int u) { return u ^ ((u >> SH) & MSK); }
+  // LDS float index of window float f
+  __device__ static __forceinline__ int at(int f) { return swz(f >> 2) * 4 + (f & 3); }
+
+  // window floats [0, nvalid) come from g[0, nvalid); the rest are left as
+  // they are (callers mask those steps). vec: g is 16-byte aligned.
+  __device__ static __forceinline__ void load(const float* g, float* lds, int nvalid, bool vec) {
+    const int l = lane_id();
+    if (vec && nvalid == FLOATS) {
 #pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const v4f t = *(const v4f*)(p + 4 * i);
-      o[4 * i] = t.x; o[4 * i + 1] = t.y; o[4 * i + 2] = t.z; o[4 * i + 3] = t.w;
+      for (int i = 0; i < UNITS / 64; ++i) {
+        const int u = swz(i * 64 + l);
+        __builtin_amdgcn_global_load_lds((const void*)(g + u * 4),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 256), 16, 0, 0);
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < FLOATS / 64; ++i) {
+        const int p = i * 64 + l;
+        const int f = swz(p >> 2) * 4 + (p & 3);
+        if (f < nvalid)
+          __builtin_amdgcn_global_load_lds((const void*)(g + f),
+                                           (__attribute__((address_space(3))) void*)(lds + i * 64), 4, 0, 0);
+      }
     }
-  } else if constexpr (N == 2) {
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    const v2f t = *(const v2f*)p;
-    o[0] = t.x; o[1] = t.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) o[i] = p[i];
   }
+  // window floats [0, nvalid) go to g[0, nvalid)
+  __device__ static __forceinline__ void store(float* g, const float* lds, int nvalid, bool vec) {
+    const int l = lane_id();
+    if (vec && nvalid == FLOATS) {
+#pragma unroll
+      for (int i = 0; i < UNITS / 64; ++i) {
+        const int p = i * 64 + l;
+        const v4f t = *(const v4f*)(lds + p * 4);
+        __builtin_nontemporal_store(t, (v4f*)(g + swz(p) * 4));
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < FLOATS / 64; ++i) {
+        const int p = i * 64 + l;
+        const int f = swz(p >> 2) * 4 + (p & 3);
+        if (f < nvalid) g[f] = lds[p];
+      }
+    }
+  }
+  // the N floats of window step s
+  __device__ static __forceinline__ void get(const float* lds, int s, float* o) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j) {
+        const v4f t = *(const v4f*)(lds + swz(s * (N / 4) + j) * 4);
+        o[4 * j] = t.x; o[4 * j + 1] = t.y; o[4 * j + 2] = t.z; o[4 * j + 3] = t.w;
+      }
+    } else {
+      static_assert(N == 2, "steps of 2 floats or whole units");
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f t = *(const v2f*)(lds + swz(s >> 1) * 4 + (s & 1) * 2);
+      o[0] = t.x; o[1] = t.y;
+    }
+  }
+  __device__ static __forceinline__ void put(float* lds, int s, const float* v) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j) {
+        const v4f t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        *(v4f*)(lds + swz(s * (N / 4) + j) * 4) = t;
+      }
+    } else {
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f t = {v[0], v[1]};
+      *(v2f*)(lds + swz(s >> 1) * 4 + (s & 1) * 2) = t;
+    }
+  }
+};
+
+// Completion of this wave's direct-to-LDS loads, then of its LDS writes, made
+// visible to all of its lanes (the staging areas are private to one wave).
+__device__ __forceinline__ void wait_stage_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// n floats from global memory (plain loads; h0 / halo values)
 template <int N>
-__device__ __forceinline__ void vstore(float* p, const float* v) {
-  if constexpr (N % 4 == 0) {
+__device__ __forceinline__ void gload(const float* p, float* o) {
 #pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const v4f t = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-      *(v4f*)(p + 4 * i) = t;
-    }
-  } else if constexpr (N == 2) {
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    const v2f t = {v[0], v[1]};
-    *(v2f*)p = t;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) p[i] = v[i];
-  }
+  for (int i = 0; i < N; ++i) o[i] = p[i];
 }
 
 // Largest i in [0, n) with v[i] <= q (0 if none).
@@ -154,7 +270,7 @@ __device__ __forceinline__ int seg_find(const int32_t* v, int n, int64_t q) {
 }
 
 constexpr int kMatCuLds = 1024;  // cu_seqlens entries cached in LDS per workgroup
-enum : int { kMatRowLoop = 0, kMatLookback = 1 };
+enum : int { kMatSingle = 0, kMatLookback = 1 };
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -165,113 +281,114 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
   using S = typename Ops::S;
   using C = typename Ops::C;
   constexpr int KK = K * K, KV = K * V, NS = Ops::NS, NC = Ops::NC, ND = NS + NC;
-  constexpr int WSTEPS = 64 * EL;      // steps per wave
+  constexpr int WSTEPS = 64 * EL;       // steps per wave window
   constexpr int TILE = WAVES * WSTEPS;  // steps per tile
+  using SA = Stage<KK, EL>;             // A
+  using SB = Stage<KV, EL>;             // B (forward) / dy (backward)
+  using SH = Stage<KV, EL>;             // h (backward)
+  constexpr int HALO = BWD ? (KK + KV + 3) / 4 * 4 : 0;  // whole 16-byte units
+  constexpr int WFLOATS = SA::FLOATS + SB::FLOATS + (BWD ? SH::FLOATS : 0) + HALO;
 
-  __shared__ float s_agg[2][WAVES][NS];
+  __shared__ __attribute__((aligned(16))) float s_stage[WAVES][WFLOATS];
+  __shared__ float s_agg[WAVES][NS];
   __shared__ float s_carry[NC];
   __shared__ int32_t s_cu[VARLEN ? kMatCuLds : 1];
 
   const int l = lane_id();
   const int w = (int)(threadIdx.x >> 6);
+  // one tile per workgroup: the row's only tile, or tile c of a chained row
   int64_t r;
-  int c_first, c_last;
-  if constexpr (MODE == kMatRowLoop) {
+  int c;
+  if constexpr (MODE == kMatSingle) {
     r = blockIdx.x;
-    c_first = 0;
-    c_last = a.ntiles - 1;
+    c = 0;
   } else {
-    r = blockIdx.x / (uint32_t)a.ntiles;
-    c_first = c_last = (int)(blockIdx.x - (uint32_t)r * (uint32_t)a.ntiles);
+    // tile-major numbering (see tile_of_block)
+    tile_of_block(a.rows, r, c);
   }
   const int64_t T = a.T;
   const int64_t row0 = r * a.stride;  // first step of the row
   const bool has_h0 = a.h0 != nullptr;
+  // the k x v arrays of this row start 16-byte aligned (the k x k ones always do)
+  const bool vecB = ((row0 * KV) & 3) == 0;
+
+  float* stA = s_stage[w];
+  float* stB = stA + SA::FLOATS;
+  float* stH = stB + SB::FLOATS;
+  float* halo = stB + SB::FLOATS + (BWD ? SH::FLOATS : 0);  // bwd: A before, h after the window
 
   Workspace ws{};
   if constexpr (MODE == kMatLookback) ws = ws_view(a.ws);
 
-  // sequence table: cached whole in LDS when it fits, else read from memory
-  const int32_t* cuv = a.cu;
-  const int ncu = a.nseg + 1;
-  if constexpr (VARLEN) {
-    if (ncu <= kMatCuLds) {
-      for (int i = threadIdx.x; i < ncu; i += WAVES * 64) s_cu[i] = a.cu[i];
-      __syncthreads();
-      cuv = s_cu;
-    }
-  }
   // h0 of sequence k for this row (zero when absent)
   auto load_h0 = [&](int k, float* o) {
-    if (has_h0) vload<KV>(a.h0 + ((int64_t)k * a.rows + r) * KV, o);
+    if (has_h0) gload<KV>(a.h0 + ((int64_t)k * a.rows + r) * KV, o);
     else {
 #pragma unroll
       for (int i = 0; i < KV; ++i) o[i] = 0.f;
     }
   };
 
-  C carry = Ops::cident();
-  for (int c = c_first; c <= c_last; ++c) {
-    const int64_t j0 = (int64_t)c * TILE + (int64_t)w * WSTEPS + (int64_t)l * EL;  // processing index of step 0
-    auto phys = [&](int64_t j) -> int64_t { return REV ? T - 1 - j : j; };
+  const int32_t* cuv = a.cu;
+  const int ncu = a.nseg + 1;
 
-    // ---- load ---------------------------------------------------------------
-    // fwd: Am = A_t, Bm = B_t. bwd: Am = A_t (own), Bm = dy_t, Hm = h_t.
-    float Am[EL][KK], Bm[EL][KV], Hm[BWD ? EL : 1][KV];
-    // a tile wholly inside the row issues every load unconditionally, so all
-    // of them are in flight together; only a row's last tile checks steps
-    const bool interior = (int64_t)(c + 1) * TILE <= T;
-    if (interior) {
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        const int64_t t = phys(j0 + e);
-        vload<KK>(a.A + (row0 + t) * KK, Am[e]);
-        vload<KV>(a.B + (row0 + t) * KV, Bm[e]);
-        if constexpr (BWD) vload<KV>(a.hs + (row0 + t) * KV, Hm[e]);
-      }
-    } else {
-#pragma unroll
-    for (int e = 0; e < EL; ++e) {
-      const int64_t t = phys(j0 + e);
-      if (t >= 0 && t < T) {
-        vload<KK>(a.A + (row0 + t) * KK, Am[e]);
-        vload<KV>(a.B + (row0 + t) * KV, Bm[e]);
-        if constexpr (BWD) vload<KV>(a.hs + (row0 + t) * KV, Hm[e]);
-      } else {
-        // identity step for positions outside the row
-#pragma unroll
-        for (int i = 0; i < KK; ++i) Am[e][i] = (i % (K + 1) == 0) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 0; i < KV; ++i) Bm[e][i] = 0.f;
-        if constexpr (BWD) {
-#pragma unroll
-          for (int i = 0; i < KV; ++i) Hm[e][i] = 0.f;
-        }
+  C carry = Ops::cident();  // state entering the tile
+  {
+    // physical window of this wave: tile pc, window pw (mirrored for reverse)
+    const int pc = REV ? a.ntiles - 1 - c : c;
+    const int pw = REV ? WAVES - 1 - w : w;
+    const int64_t wlo = (int64_t)pc * TILE + (int64_t)pw * WSTEPS;  // first step of the window
+    const int nv = (int)max((int64_t)0, min((int64_t)WSTEPS, T - wlo));  // valid steps
+
+    // ---- stage the window ------------------------------------------------
+    if (nv > 0) {
+      SA::load(a.A + (row0 + wlo) * KK, stA, nv * KK, true);
+      SB::load(a.B + (row0 + wlo) * KV, stB, nv * KV, vecB);
+      if constexpr (BWD) SH::load(a.hs + (row0 + wlo) * KV, stH, nv * KV, vecB);
+    }
+    if constexpr (BWD) {
+      // A of the step before the window and h of the step after it, in
+      // processing order (zero outside the row)
+      const int64_t tA = REV ? wlo + WSTEPS : wlo - 1;
+      const int64_t tH = REV ? wlo - 1 : wlo + WSTEPS;
+      if (l < KK) halo[l] = (tA >= 0 && tA < T) ? a.A[(row0 + tA) * KK + l] : 0.f;
+      if (l < KV) halo[KK + l] = (tH >= 0 && tH < T) ? a.hs[(row0 + tH) * KV + l] : 0.f;
+    }
+    // the sequence table, once per workgroup (after the window loads are in
+    // flight, so its latency overlaps theirs)
+    if constexpr (VARLEN) {
+      if (ncu <= kMatCuLds) {
+        for (int i = threadIdx.x; i < ncu; i += WAVES * 64) s_cu[i] = a.cu[i];
+        __syncthreads();
+        cuv = s_cu;
       }
     }
-    }
+    wait_stage_loads();
 
-    // ---- sequence boundaries ----------------------------------------------------
+    // lane-owned steps: processing element e <-> window step sidx(e)
+    auto sidx = [&](int e) -> int { return REV ? (63 - l) * EL + (EL - 1 - e) : l * EL + e; };
+    const int64_t tlane = wlo + (REV ? (63 - l) * EL : l * EL);  // lowest step of the lane
+
+    // ---- sequence boundaries ------------------------------------------------
     // first: a sequence's first step in processing order; last: its last one
     uint32_t firstm = 0, lastm = 0;
     int segk[EL];
 #pragma unroll
     for (int e = 0; e < EL; ++e) segk[e] = 0;
     if constexpr (!VARLEN) {
+      const int64_t tf = REV ? T - 1 : 0, tl = REV ? 0 : T - 1;
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        const int64_t j = j0 + e;
-        if (j == 0) firstm |= 1u << e;
-        if (j == T - 1) lastm |= 1u << e;
+        const int64_t t = wlo + sidx(e);
+        if (t == tf) firstm |= 1u << e;
+        if (t == tl) lastm |= 1u << e;
       }
     } else {
-      // physical range of the lane's steps, walked upward
-      const int64_t tlo = REV ? T - (j0 + EL) : j0;
-      int k = seg_find(cuv, ncu, max(tlo, (int64_t)0));
+      int k = seg_find(cuv, ncu, max(tlane, (int64_t)0));
 #pragma unroll
       for (int ep = 0; ep < EL; ++ep) {
-        const int64_t q = tlo + ep;
-        if (q < 0 || q >= T) continue;
+        const int64_t q = tlane + ep;
+        if (q >= T) continue;
         while (k + 1 < ncu && (int64_t)cuv[k + 1] <= q) ++k;
         const bool is_start = (int64_t)cuv[k] == q;
         const bool is_end = (k + 1 < ncu) && ((int64_t)cuv[k + 1] - 1 == q);
@@ -281,82 +398,79 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
         if (REV ? is_start : is_end) lastm |= 1u << e;
       }
     }
+    auto valid = [&](int e) -> bool { return wlo + sidx(e) < T; };
 
-    // ---- elements (X, Y) of the scan in processing order -------------------------
-    // fwd: X = A_t, Y = B_t (sequence start: X = 0, Y = A h0 + B)
-    // bwd: X = (A of the previous step in processing order)^T, Y = dy_t
-    //      (sequence start: X = 0), N = forward state before t (h0 at the
-    //      sequence's forward-first step)
-    // (the forward keeps X in Am itself; the backward needs A_t for dh0)
-    float Xb[BWD ? EL : 1][KK], N[BWD ? EL : 1][KV];
-    auto X = [&](int e) -> float* {
-      if constexpr (BWD) return Xb[e];
-      else return Am[e];
-    };
-    if constexpr (!BWD) {
+    // ---- element e of the scan, in processing order ------------------------------
+    // fwd: X = A_t, Y = B_t; a sequence start becomes (0, A h0 + B).
+    // bwd: X = (A of the previous step in processing order)^T, Y = dy_t; a
+    //      sequence start becomes (0, dy).
+    // A of processing element e - 1 (bwd): window step sidx(e) -/+ 1, or the halo
+    auto prevA = [&](int e, float* o) {
+      const int s = REV ? sidx(e) + 1 : sidx(e) - 1;
+      if (s < 0 || s >= WSTEPS) {
 #pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        if (firstm & (1u << e)) {
+        for (int i = 0; i < KK; ++i) o[i] = halo[i];
+      } else {
+        SA::get(stA, s, o);
+      }
+    };
+    // h of processing element e + 1 (bwd): the forward state before step t
+    auto nextH = [&](int e, float* o) {
+      const int sn = REV ? sidx(e) - 1 : sidx(e) + 1;
+      if (sn < 0 || sn >= WSTEPS) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) o[i] = halo[KK + i];
+      } else {
+        SH::get(stH, sn, o);
+      }
+    };
+    // (X, Y) of element e; false for a step outside the row (identity)
+    auto element = [&](int e, float* X, float* Y) -> bool {
+      if (!valid(e)) return false;
+      const int s = sidx(e);
+      const bool first = firstm & (1u << e);
+      if constexpr (!BWD) {
+        SA::get(stA, s, X);
+        SB::get(stB, s, Y);
+        if (first) {
           float h0v[KV], y[KV];
           load_h0(segk[e], h0v);
-          Ops::template mul<V>(Am[e], h0v, Bm[e], y);
+          Ops::template mul<V>(X, h0v, Y, y);
 #pragma unroll
-          for (int i = 0; i < KV; ++i) Bm[e][i] = y[i];
+          for (int i = 0; i < KV; ++i) Y[i] = y[i];
 #pragma unroll
-          for (int i = 0; i < KK; ++i) Am[e][i] = 0.f;
+          for (int i = 0; i < KK; ++i) X[i] = 0.f;
         }
-      }
-    } else {
-      // previous step's A (lane before / wave before) and next step's h
-      float Ap[KK], Hn[KV];
+      } else {
+        SB::get(stB, s, Y);
+        if (first) {
 #pragma unroll
-      for (int i = 0; i < KK; ++i) Ap[i] = __shfl_up(Am[EL - 1][i], 1, 64);
-#pragma unroll
-      for (int i = 0; i < KV; ++i) Hn[i] = __shfl_down(Hm[0][i], 1, 64);
-      if (l == 0) {
-        const int64_t t = phys(j0 - 1);
-        if (j0 - 1 >= 0 && t >= 0 && t < T) vload<KK>(a.A + (row0 + t) * KK, Ap);
-      }
-      if (l == 63) {
-        const int64_t t = phys(j0 + EL);
-        if (t >= 0 && t < T) vload<KV>(a.hs + (row0 + t) * KV, Hn);
-        else {
-#pragma unroll
-          for (int i = 0; i < KV; ++i) Hn[i] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        const float* src = (e == 0) ? Ap : Am[e - 1];
-        const bool first = firstm & (1u << e);
-#pragma unroll
-        for (int p = 0; p < K; ++p)
-#pragma unroll
-          for (int q = 0; q < K; ++q) Xb[e][p * K + q] = first ? 0.f : src[q * K + p];
-        const float* hn = (e == EL - 1) ? Hn : Hm[e + 1];
-        if (lastm & (1u << e)) {
-          load_h0(segk[e], N[e]);
+          for (int i = 0; i < KK; ++i) X[i] = 0.f;
         } else {
+          float Ap[KK];
+          prevA(e, Ap);
 #pragma unroll
-          for (int i = 0; i < KV; ++i) N[e][i] = hn[i];
+          for (int p = 0; p < K; ++p)
+#pragma unroll
+            for (int q = 0; q < K; ++q) X[p * K + q] = Ap[q * K + p];
         }
       }
-    }
+      return true;
+    };
 
     // ---- lane-serial summary ------------------------------------------------------
     S sum = Ops::ident();
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
-      if (Ops::zero_k(X(e))) {
+      float X[KK], Y[KV];
+      if (!element(e, X, Y)) continue;
+      if (Ops::zero_k(X)) {
 #pragma unroll
         for (int i = 0; i < KK; ++i) sum.v[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < KV; ++i) sum.v[KK + i] = Bm[e][i];
+        for (int i = 0; i < KV; ++i) sum.v[KK + i] = Y[i];
       } else {
-        S nx;
-        Ops::template mul<K>(X(e), sum.v, nullptr, nx.v);
-        Ops::template mul<V>(X(e), sum.v + KK, Bm[e], nx.v + KK);
-        sum = nx;
+        Ops::premul(X, sum, Y);
       }
     }
     // ---- wave scan --------------------------------------------------------------
@@ -371,24 +485,40 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     for (int i = 0; i < NS; ++i) wagg.v[i] = readlane_f(sum.v[i], 63);
 
     // ---- across waves ---------------------------------------------------------------
-    S ex = Ops::ident(), tagg = wagg;
-    if constexpr (WAVES > 1) {
-      const int buf = c & 1;
-      if (l == 0) {
-#pragma unroll
-        for (int i = 0; i < NS; ++i) s_agg[buf][w][i] = wagg.v[i];
-      }
-      __syncthreads();
-      tagg = Ops::ident();
+    // tile aggregate = the waves' aggregates in order; a wave's lanes prepend
+    // the waves before it to their own summaries (so only `sum` stays live
+    // through the look-back)
+    auto tile_agg = [&]() -> S {
+      S t = Ops::ident();
 #pragma unroll
       for (int q = 0; q < WAVES; ++q) {
-        if (q == w) ex = tagg;
         S x;
 #pragma unroll
-        for (int i = 0; i < NS; ++i) x.v[i] = s_agg[buf][q][i];
-        Ops::compose(tagg, x);
-        tagg = x;
+        for (int i = 0; i < NS; ++i) x.v[i] = s_agg[q][i];
+        Ops::compose(t, x);
+        t = x;
       }
+      return t;
+    };
+    // composition of the waves before this one
+    auto waves_before = [&]() -> S {
+      S ex = Ops::ident();
+      for (int q = 0; q < w; ++q) {
+        S x;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) x.v[i] = s_agg[q][i];
+        Ops::compose(ex, x);
+        ex = x;
+      }
+      return ex;
+    };
+    if constexpr (WAVES > 1) {
+      if (l == 0) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) s_agg[w][i] = wagg.v[i];
+      }
+      __syncthreads();
+      if (w > 0) Ops::compose(waves_before(), sum);
     }
 
     // ---- across tiles: decoupled look-back ------------------------------------------
@@ -397,20 +527,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
       uint64_t* my = rd + (int64_t)ND * c;
       if (w == 0) {
         const uint32_t tagA = kTagAgg, tagI = kTagIncl;
-        const bool hard = Ops::hard(tagg);
-        if (l == 0) {
-          if (!hard) {
+        bool hard;
+        {
+          const S tagg = (WAVES > 1) ? tile_agg() : wagg;
+          hard = Ops::hard(tagg);
+          if (l == 0) {
+            if (!hard) {
 #pragma unroll
-            for (int i = 0; i < NS; ++i) st_u64(my + i, pack_word(tagA, tagg.v[i]));
-          } else {
-            const C inc = Ops::carry_of_hard(tagg);
+              for (int i = 0; i < NS; ++i) st_u64(my + i, pack_word(tagA, tagg.v[i]));
+            } else {
+              const C inc = Ops::carry_of_hard(tagg);
 #pragma unroll
-            for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
+              for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
+            }
           }
         }
         if (c > 0) carry = lookback<Ops>(ws, rd, c);
         if (l == 0) {
           if (!hard) {
+            const S tagg = (WAVES > 1) ? tile_agg() : wagg;
             const C inc = Ops::apply(tagg, carry);
 #pragma unroll
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
@@ -424,63 +559,103 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
       for (int i = 0; i < NC; ++i) carry.v[i] = s_carry[i];
     }
 
-    // ---- apply and store ---------------------------------------------------------
+    // ---- apply: each step from its exact carry-in, outputs into the staging slots
     {
-      const C hw = Ops::apply(ex, carry);  // state entering this wave's span
-      const C v = Ops::apply(sum, hw);     // state after this lane
+      // state entering this wave's window (lane 0) and after this lane
+      C hw = carry;
+      if constexpr (WAVES > 1) {
+        if (w > 0) hw = Ops::apply(waves_before(), carry);
+      }
+      const C v = Ops::apply(sum, carry);
       C st;
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         st.v[i] = __shfl_up(v.v[i], 1, 64);
         if (l == 0) st.v[i] = hw.v[i];
       }
+      // bwd: the lane's first A_prev is read before any lane overwrites its A
+      // slots with dA (all lanes run this code in step)
+      float Aown[BWD ? KK : 1];
+      if constexpr (BWD) prevA(0, Aown);
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        if (Ops::zero_k(X(e))) {
+        if (!valid(e)) continue;
+        const int s = sidx(e);
+        const bool first = firstm & (1u << e);
+        float Y[KV];
+        SB::get(stB, s, Y);
+        if constexpr (!BWD) {
+          float X[KK];
+          SA::get(stA, s, X);
+          if (first) {
+            float h0v[KV], y[KV];
+            load_h0(segk[e], h0v);
+            Ops::template mul<V>(X, h0v, Y, y);
 #pragma unroll
-          for (int i = 0; i < KV; ++i) st.v[i] = Bm[e][i];
+            for (int i = 0; i < KV; ++i) st.v[i] = y[i];
+          } else if (Ops::zero_k(X)) {
+#pragma unroll
+            for (int i = 0; i < KV; ++i) st.v[i] = Y[i];
+          } else {
+            C nx;
+            Ops::template mul<V>(X, st.v, Y, nx.v);
+            st = nx;
+          }
+          SB::put(stB, s, st.v);  // h over B
         } else {
-          C nx;
-          Ops::template mul<V>(X(e), st.v, Bm[e], nx.v);
-          st = nx;
-        }
-        const int64_t t = phys(j0 + e);
-        if (t >= 0 && t < T) {
-          vstore<KV>(a.out0 + (row0 + t) * KV, st.v);
-          if constexpr (BWD) {
-            // dA_t = lam_t h_prev^T (k x k)
-            float dA[KK];
+          // Aown holds A of the previous processing step; X = its transpose
+          float X[KK];
+#pragma unroll
+          for (int p = 0; p < K; ++p)
+#pragma unroll
+            for (int q = 0; q < K; ++q) X[p * K + q] = first ? 0.f : Aown[q * K + p];
+          if (first || Ops::zero_k(X)) {
+#pragma unroll
+            for (int i = 0; i < KV; ++i) st.v[i] = Y[i];
+          } else {
+            C nx;
+            Ops::template mul<V>(X, st.v, Y, nx.v);
+            st = nx;
+          }
+          SA::get(stA, s, Aown);  // own A: dh0 below, and the next element's X
+          float N[KV];
+          if (lastm & (1u << e)) load_h0(segk[e], N);
+          else nextH(e, N);
+          // dA_t = lam_t h_prev^T (k x k)
+          float dA[KK];
+#pragma unroll
+          for (int p = 0; p < K; ++p)
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+              float acc = 0.f;
+#pragma unroll
+              for (int u = 0; u < V; ++u) acc = __builtin_fmaf(st.v[p * V + u], N[q * V + u], acc);
+              dA[p * K + q] = acc;
+            }
+          SB::put(stB, s, st.v);  // dB = lam over dy
+          SA::put(stA, s, dA);    // dA over A
+          if (a.dh0 && (lastm & (1u << e))) {
+            // dh0 = A_s^T lam_s
+            float* dst = a.dh0 + ((int64_t)segk[e] * a.rows + r) * KV;
 #pragma unroll
             for (int p = 0; p < K; ++p)
 #pragma unroll
-              for (int q = 0; q < K; ++q) {
+              for (int u = 0; u < V; ++u) {
                 float acc = 0.f;
 #pragma unroll
-                for (int u = 0; u < V; ++u) acc = __builtin_fmaf(st.v[p * V + u], N[e][q * V + u], acc);
-                dA[p * K + q] = acc;
+                for (int q = 0; q < K; ++q) acc = __builtin_fmaf(Aown[q * K + p], st.v[q * V + u], acc);
+                dst[p * V + u] = acc;
               }
-            vstore<KK>(a.out1 + (row0 + t) * KK, dA);
-            if (a.dh0 && (lastm & (1u << e))) {
-              // dh0 = A_s^T lam_s
-              float d[KV];
-#pragma unroll
-              for (int p = 0; p < K; ++p)
-#pragma unroll
-                for (int u = 0; u < V; ++u) {
-                  float acc = 0.f;
-#pragma unroll
-                  for (int q = 0; q < K; ++q) acc = __builtin_fmaf(Am[e][q * K + p], st.v[q * V + u], acc);
-                  d[p * V + u] = acc;
-                }
-              float* dst = a.dh0 + ((int64_t)segk[e] * a.rows + r) * KV;
-#pragma unroll
-              for (int i = 0; i < KV; ++i) dst[i] = d[i];
-            }
           }
         }
       }
     }
-    carry = Ops::apply(tagg, carry);  // state at the end of the tile
+    // ---- store ----------------------------------------------------------------------
+    wave_lds_sync();
+    if (nv > 0) {
+      SB::store(a.out0 + (row0 + wlo) * KV, stB, nv * KV, vecB);
+      if constexpr (BWD) SA::store(a.out1 + (row0 + wlo) * KK, stA, nv * KK, true);
+    }
   }
 }
 
@@ -490,10 +665,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
 template <int K, int V>
 struct MatCfg;
 // (waves per workgroup, steps per lane) for forward / backward
-template <> struct MatCfg<2, 1> { static constexpr int W = 4, EF = 8, EB = 4; };
-template <> struct MatCfg<2, 2> { static constexpr int W = 4, EF = 4, EB = 4; };
-template <> struct MatCfg<4, 1> { static constexpr int W = 4, EF = 4, EB = 2; };
-template <> struct MatCfg<4, 4> { static constexpr int W = 4, EF = 4, EB = 2; };
+template <> struct MatCfg<2, 1> { static constexpr int W = 2, EF = 8, EB = 8; };
+template <> struct MatCfg<2, 2> { static constexpr int W = 2, EF = 4, EB = 4; };
+template <> struct MatCfg<4, 1> { static constexpr int W = 2, EF = 4, EB = 4; };
+template <> struct MatCfg<4, 4> { static constexpr int W = 2, EF = 2, EB = 2; };
 
 template <int K, int V>
 int64_t matrix_tile_steps(bool bwd) {
@@ -510,8 +685,8 @@ static hipError_t launch_mat(const MatArgs& a0, hipStream_t st) {
   const dim3 block(W * 64);
   if (!lookback) {
     const dim3 grid((unsigned)a.rows);
-    if (varlen) hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, true, kMatRowLoop, W, E>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, false, kMatRowLoop, W, E>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, true, kMatSingle, W, E>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, false, kMatSingle, W, E>), grid, block, 0, st, a);
   } else {
     // fresh descriptors for this call (zero tag = not published)
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(MatOps<K, V>::NS + MatOps<K, V>::NC);

@@ -161,8 +161,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     c_first = 0;
     c_last = a.ntiles - 1;
   } else {
-    r = blockIdx.x / (uint32_t)a.ntiles;
-    c_first = c_last = (int)(blockIdx.x - (uint32_t)r * (uint32_t)a.ntiles);
+    int c;
+    tile_of_block(a.rows, r, c);
+    c_first = c_last = c;
   }
   const int64_t T = a.T;
   const int64_t rowoff = r * a.stride;

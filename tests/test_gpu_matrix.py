@@ -153,3 +153,107 @@ def test_orthogonal_4x4_full_sampled(m, oracle_lib):
     close(dB[idx], rB, TAU_BWD, "dB")
     close(dA[idx], rA, TAU_BWD, "dA")
     assert torch.isfinite(h).all() and torch.isfinite(dA).all()
+
+
+# ---------------------------------------------------------------------------
+# exact mode, strided rows, non-finite containment
+# ---------------------------------------------------------------------------
+def _signed_perm_case(r, k, v, rows, T, max_run=2048, p_zero=0.02):
+    """Integer data whose matrix scan is exact in fp32 in every association order:
+    A_t a signed permutation matrix or 0 (a zero at least every max_run steps),
+    B, dy in {-1, 0, 1}. Every product has one nonzero term per entry, so
+    |h|, |lam| <= max_run and |dA| <= max_run^2 < 2^24."""
+    A = np.zeros((rows, T, k, k), np.float32)
+    perm = np.argsort(r.random((rows, T, k)), axis=-1)
+    sign = r.choice(np.array([-1.0, 1.0], np.float32), size=(rows, T, k))
+    for i in range(k):
+        np.put_along_axis(A[:, :, i, :], perm[:, :, i:i + 1], sign[:, :, i:i + 1], axis=-1)
+    zero = r.random((rows, T)) < p_zero
+    zero[:, max_run - 1::max_run] = True
+    A[zero] = 0.0
+    B = r.integers(-1, 2, size=(rows, T, k, v)).astype(np.float32)
+    dy = r.integers(-1, 2, size=(rows, T, k, v)).astype(np.float32)
+    return A, B, dy
+
+
+@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
+    """Integer data: the GPU must equal the oracle bit for bit (segments, resets,
+    h0 injection, tile and look-back boundaries, reverse, adjoint)."""
+    k, v = kv
+    r = np.random.default_rng(300 + 10 * k + v + reverse)
+    rows, T = 3, 9001
+    A, B, dy = _signed_perm_case(r, k, v, rows, T)
+    cu = gen.segments_random(r, T, 9)
+    h0 = r.integers(-1, 2, size=(len(cu) - 1, rows, k, v)).astype(np.float32)
+    cu_t, h0_t, Ad = _t(cu, torch.int32), _t(h0), _t(A)
+    h = m.matrix_affine_scan_fwd(Ad, _t(B), h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    href = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(h.cpu().double().numpy(), href)
+    dA, dB, dh0 = m.matrix_affine_scan_bwd(Ad, h, _t(dy), h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    rA, rB, rh0 = oracle_lib.matrix_affine_scan_bwd(A, href, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(dB.cpu().double().numpy(), rB)
+    assert np.array_equal(dA.cpu().double().numpy(), rA)
+    assert np.array_equal(dh0.cpu().double().numpy(), rh0)
+
+
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+@pytest.mark.parametrize("T", [700, 5001])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_odd_row_stride(m, oracle_lib, kv, T, reverse):
+    """row_stride = T + 1 through the C ABI: with k x v = 2, every other row starts
+    8 bytes off a 16-byte boundary (the unaligned staging path)."""
+    import ctypes
+    k, v = kv
+    r = np.random.default_rng(400 + T + k + reverse)
+    rows, stride = 5, T + 1
+    A, B, dy = _random_case(r, k, v, rows, stride)
+    h0 = r.standard_normal((1, rows, k, v)).astype(np.float32)
+    Ad, Bd, dyd, h0d = _t(A), _t(B), _t(dy), _t(h0)
+    h = torch.full((rows, stride, k, v), 7.0, device=DEV)
+    prob = m.Problem(rows, T, stride, None, 1, int(reverse))
+    ws = torch.zeros(m.workspace_bytes(prob, m.OP_MATRIX_BWD, k, v) + m.workspace_bytes(prob, m.OP_MATRIX_FWD, k, v),
+                     dtype=torch.uint8, device=DEV)
+    sh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(prob), k, v, p(Ad), p(Bd), p(h0d), p(h), p(ws), ws.numel(), sh) == 0
+    href = oracle_lib.matrix_affine_scan_fwd(A[:, :T], B[:, :T], h0=h0, reverse=reverse)
+    close(h[:, :T], href, TAU_FWD, "h")
+    assert torch.all(h[:, T:] == 7.0), "wrote past the row"
+    dA = torch.full((rows, stride, k, k), 7.0, device=DEV)
+    dB = torch.full((rows, stride, k, v), 7.0, device=DEV)
+    dh0 = torch.empty((1, rows, k, v), device=DEV)
+    hin = h.clone()
+    assert m.lib.matrix_affine_scan_bwd(ctypes.byref(prob), k, v, p(Ad), p(hin), p(dyd), p(h0d), p(dA), p(dB),
+                                        p(dh0), p(ws), ws.numel(), sh) == 0
+    rA, rB, rh0 = oracle_lib.matrix_affine_scan_bwd(A[:, :T], href, dy[:, :T], h0=h0, reverse=reverse)
+    close(dB[:, :T], rB, TAU_BWD, "dB")
+    close(dA[:, :T], rA, TAU_BWD, "dA")
+    close(dh0, rh0, TAU_BWD, "dh0")
+    assert torch.all(dA[:, T:] == 7.0) and torch.all(dB[:, T:] == 7.0), "wrote past the row"
+
+
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+def test_matrix_nan_poison_stays_in_its_sequence(m, oracle_lib, kv):
+    """A sequence full of NaN/Inf changes nothing in any other sequence (bitwise)."""
+    k, v = kv
+    r = np.random.default_rng(500 + k)
+    T = 7000
+    A, B, dy = _random_case(r, k, v, 2, T)
+    cu = np.array([0, 1500, 4000, 4001, 7000], dtype=np.int32)
+    Ap, Bp = A.copy(), B.copy()
+    Ap[:, 1500:4000] = np.nan
+    Bp[:, 1500:3000] = np.inf
+    cu_t = _t(cu, torch.int32)
+    keep = np.r_[0:1500, 4000:7000]
+    for rev in (False, True):
+        h = m.matrix_affine_scan_fwd(_t(A), _t(B), cu_seqlens=cu_t, reverse=rev)
+        hp = m.matrix_affine_scan_fwd(_t(Ap), _t(Bp), cu_seqlens=cu_t, reverse=rev)
+        assert torch.equal(h[:, keep], hp[:, keep])
+        d1 = m.matrix_affine_scan_bwd(_t(A), h, _t(dy), cu_seqlens=cu_t, reverse=rev)
+        d2 = m.matrix_affine_scan_bwd(_t(Ap), hp, _t(dy), cu_seqlens=cu_t, reverse=rev)
+        for a, b in zip(d1[:2], d2[:2]):
+            assert torch.equal(a[:, keep], b[:, keep])
+        assert torch.equal(d1[2][[0, 2, 3]], d2[2][[0, 2, 3]])
+        close(h[:, keep], oracle_lib.matrix_affine_scan_fwd(A, B, cu_seqlens=cu, reverse=rev)[:, keep], TAU_FWD, "h")

@@ -28,6 +28,11 @@ FLAGS = [
 ]
 
 
+# Every source compiles in well under a minute; a compile that runs past this
+# is a compiler problem and fails the build instead of stalling it.
+COMPILE_TIMEOUT_S = 900
+
+
 def _hipcc() -> str:
     h = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(h):
@@ -42,7 +47,10 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
+    except subprocess.TimeoutExpired as e:
+        raise RuntimeError(f"hipcc did not finish {src} within {COMPILE_TIMEOUT_S} s") from e
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (r.stderr or "").splitlines() if noise not in ln and "(ignoring feature)" not in ln)
     if r.returncode != 0:

@@ -38,6 +38,14 @@ __device__ __forceinline__ float dpp_f(float old, float src) {
                                                     ROW_MASK, 0xf, false));
 }
 
+// DPP move whose value is only used in lanes where the source lane is valid
+// (out-of-range sources read zero, lanes outside ROW_MASK are left undefined):
+// no register has to be initialised first.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_mov_f(float src) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(src), CTRL, ROW_MASK, 0xf, true));
+}
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -213,13 +221,14 @@ struct LogOps {
 };
 
 // One DPP scan step on a summary: lanes whose mask bit is set compose the
-// summary DPP brings in (earlier) in front of their own.
+// summary DPP brings in (earlier) in front of their own. `valid` holds exactly
+// in the lanes whose DPP source lies in the wave and inside ROW_MASK, so the
+// moved value is never read elsewhere.
 template <class Ops, int CTRL, int ROW_MASK>
 __device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
   typename Ops::S e;
-  const typename Ops::S id = Ops::ident();
 #pragma unroll
-  for (int i = 0; i < Ops::NS; ++i) e.v[i] = dpp_f<CTRL, ROW_MASK>(id.v[i], x.v[i]);
+  for (int i = 0; i < Ops::NS; ++i) e.v[i] = dpp_mov_f<CTRL, ROW_MASK>(x.v[i]);
   if (valid) Ops::compose(e, x);
 }
 

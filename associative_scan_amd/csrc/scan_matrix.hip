@@ -664,11 +664,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
 // ---------------------------------------------------------------------------
 template <int K, int V>
 struct MatCfg;
-// (waves per workgroup, steps per lane) for forward / backward
-template <> struct MatCfg<2, 1> { static constexpr int W = 2, EF = 8, EB = 8; };
-template <> struct MatCfg<2, 2> { static constexpr int W = 2, EF = 4, EB = 4; };
+// (waves per workgroup, steps per lane) for forward / backward, from timing
+// sweeps at 4096 rows x T = 8192 (the 4x4 kernels are bound by VALU work and
+// LDS occupancy, so they run one small wave window per workgroup)
+template <> struct MatCfg<2, 1> { static constexpr int W = 4, EF = 4, EB = 4; };
+template <> struct MatCfg<2, 2> { static constexpr int W = 4, EF = 4, EB = 4; };
 template <> struct MatCfg<4, 1> { static constexpr int W = 2, EF = 4, EB = 4; };
-template <> struct MatCfg<4, 4> { static constexpr int W = 2, EF = 2, EB = 2; };
+template <> struct MatCfg<4, 4> { static constexpr int W = 1, EF = 2, EB = 2; };
 
 template <int K, int V>
 int64_t matrix_tile_steps(bool bwd) {

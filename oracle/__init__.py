@@ -33,7 +33,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "scan_fwd", "scan_bwd", "scan_log_fwd", "matrix_affine_scan_fwd",
+__all__ = ["build", "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd",
            "matrix_affine_scan_bwd", "num_threads"]
 
 
@@ -60,6 +60,7 @@ def _load():
         lib.oracle_scan_fwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p]
         lib.oracle_scan_bwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p, p, p, p]
         lib.oracle_scan_log_fwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p]
+        lib.oracle_scan_log_bwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p, p, p, p, p]
         lib.oracle_matrix_fwd.argtypes = [i64, i64, i64, p, i32, i32, i32, i32, p, p, p, p]
         lib.oracle_matrix_bwd.argtypes = [i64, i64, i64, p, i32, i32, i32, i32, p, p, p, p, p, p, p]
         for f in (lib.oracle_scan_fwd, lib.oracle_scan_bwd, lib.oracle_scan_log_fwd,
@@ -140,6 +141,22 @@ def scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
     h = np.zeros_like(la)
     _load().oracle_scan_log_fwd(rows, T, T, _ptr(cu), nseg, int(bool(reverse)), _ptr(la), _ptr(lb), _ptr(lh0), _ptr(h))
     return h
+
+
+def scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False):
+    """Adjoint of scan_log_fwd for L = <dy, h>: returns (dlog_a, dlog_b, dlog_h0[nseg, rows]);
+    see oracle_scan_log_bwd."""
+    la, lb, h, dy = _f64(log_a), _f64(log_b), _f64(h), _f64(dy)
+    assert la.shape == lb.shape == h.shape == dy.shape
+    T = la.shape[-1]
+    rows = int(np.prod(la.shape[:-1], dtype=np.int64))
+    cu, nseg = _segments(cu_seqlens, T)
+    lh0 = _h0(log_h0, nseg, rows)
+    dla, dlb = np.zeros_like(la), np.zeros_like(la)
+    dlh0 = np.zeros((nseg, rows))
+    _load().oracle_scan_log_bwd(rows, T, T, _ptr(cu), nseg, int(bool(reverse)), _ptr(la), _ptr(lb), _ptr(h),
+                                _ptr(dy), _ptr(lh0), _ptr(dla), _ptr(dlb), _ptr(dlh0))
+    return dla, dlb, dlh0
 
 
 def _mat_shapes(A, B_or_h):

@@ -166,6 +166,52 @@ API void oracle_scan_log_fwd(int64_t rows, int64_t T, int64_t row_stride, const 
 }
 
 /* ---------------------------------------------------------------------------
+ * Log-space backward: the adjoint of oracle_scan_log_fwd with respect to its
+ * log inputs, for L = <dy, h> with h the forward's (linear) output. With
+ * a_t = exp(log_a_t), b_t = exp(log_b_t), h0 = exp(log_h0) (0 if NULL), the
+ * recurrence is h_t = a_t h_{t-1} + b_t ("Triton scan kernels", "One
+ * associative-scan family"), so the chain rule through exp gives, walking
+ * each segment against the forward's direction:
+ *   lam_t      = dy_t + a_{t+1} lam_{t+1}      (a of the next forward step; 0 past the end)
+ *   dlog_b_t   = lam_t * b_t
+ *   dlog_a_t   = lam_t * a_t * h_{t-1}         (h_{b-1} := h0)
+ *   dlog_h0    = lam_b * a_b * h0              (b = the segment's forward-first step)
+ * reverse mirrors the neighbours as in oracle_scan_bwd. dlog_h0 may be NULL;
+ * an empty segment writes 0.
+ * ------------------------------------------------------------------------- */
+API void oracle_scan_log_bwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
+                             int32_t reverse, const double* log_a, const double* log_b, const double* h,
+                             const double* dy, const double* log_h0, double* dlog_a, double* dlog_b,
+                             double* dlog_h0) {
+  if (!cu) nseg = 1;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t s = 0; s < nseg; ++s) {
+      const int64_t b = seg_begin(cu, s, T), e = seg_end(cu, s, T), n = e - b;
+      const int64_t o = r * row_stride;
+      const double h0 = log_h0 ? exp(log_h0[(int64_t)s * rows + r]) : 0.0;
+      double lam = 0.0, anext = 0.0;
+      if (n <= 0) {
+        if (dlog_h0) dlog_h0[(int64_t)s * rows + r] = 0.0;
+        continue;
+      }
+      int64_t tfirst = b;
+      for (int64_t i = n - 1; i >= 0; --i) {
+        const int64_t t = reverse ? e - 1 - i : b + i; /* walk opposite to the forward */
+        const double at = exp(log_a[o + t]);
+        lam = dy[o + t] + anext * lam;
+        dlog_b[o + t] = lam * exp(log_b[o + t]);
+        const double hprev = (i == 0) ? h0 : h[o + (reverse ? t + 1 : t - 1)];
+        dlog_a[o + t] = lam * at * hprev;
+        anext = at;
+        tfirst = t;
+      }
+      if (dlog_h0) dlog_h0[(int64_t)s * rows + r] = lam * exp(log_a[o + tfirst]) * h0;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------
  * Matrix-affine forward: h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t
  * k x v (left multiplication, row-major blocks). Same segment / h0 / reverse
  * rules as the scalar scan; h0 is [nseg][rows][k][v].

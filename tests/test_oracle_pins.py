@@ -344,6 +344,132 @@ def test_log_zero_gate_restarts(oracle_lib):
     np.testing.assert_allclose(h[:, 21:], h_tail, rtol=1e-13)
 
 
+def _tangent_log(la, lb, lh0, lad, lbd, lh0d, cu, reverse):
+    """Forward-mode derivative of h_t = a_t h_{t-1} + b_t with a = e^{log_a},
+    b = e^{log_b}, h0 = e^{log_h0}, for perturbations of the log inputs:
+    hd_t = a_t lad_t h_{t-1} + a_t hd_{t-1} + b_t lbd_t, hd before a segment = h0 lh0d."""
+    a, b = np.exp(la), np.exp(lb)
+    h, hd = np.zeros_like(la), np.zeros_like(la)
+    for s in range(len(cu) - 1):
+        idx = list(range(cu[s], cu[s + 1]))
+        if reverse:
+            idx = idx[::-1]
+        st = np.exp(lh0[s])
+        std = st * lh0d[s]
+        for t in idx:
+            std = a[:, t] * lad[:, t] * st + a[:, t] * std + b[:, t] * lbd[:, t]
+            st = a[:, t] * st + b[:, t]
+            h[:, t], hd[:, t] = st, std
+    return h, hd
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_bwd_adjoint_dot_product(oracle_lib, reverse):
+    """<dy, J v> = <J^T dy, v> for the log-space adjoint, J v from the tangent-linear
+    recurrence written in linear space."""
+    r = _rng(14)
+    T = 301
+    la = -np.log1p(np.exp(r.standard_normal((4, T))))
+    lb = r.standard_normal((4, T))
+    cu = gen.segments_random(r, T, 5)
+    lh0 = r.standard_normal((5, 4))
+    lad, lbd, lh0d = r.standard_normal(la.shape), r.standard_normal(la.shape), r.standard_normal(lh0.shape)
+    dy = r.standard_normal(la.shape)
+    href, hd = _tangent_log(la, lb, lh0, lad, lbd, lh0d, cu, reverse)
+    h = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    np.testing.assert_allclose(h, href, rtol=1e-12)
+    dla, dlb, dlh0 = oracle_lib.scan_log_bwd(la, lb, h, dy, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    lhs = np.sum(dy * hd)
+    rhs = np.sum(dla * lad) + np.sum(dlb * lbd) + np.sum(dlh0 * lh0d)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_log_bwd_finite_differences(oracle_lib):
+    """Central differences of <dy, scan_log_fwd(.)> in every kind of log input."""
+    r = _rng(15)
+    T = 30
+    la = -np.log1p(np.exp(r.standard_normal((2, T))))
+    lb = r.standard_normal((2, T))
+    cu = np.array([0, 11, 11, 30], dtype=np.int32)
+    lh0 = r.standard_normal((3, 2))
+    dy = r.standard_normal(la.shape)
+    eps = 1e-6
+    for reverse in (False, True):
+        L = lambda a_, b_, h0_: np.sum(dy * oracle_lib.scan_log_fwd(a_, b_, log_h0=h0_, cu_seqlens=cu, reverse=reverse))
+        h = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+        dla, dlb, dlh0 = oracle_lib.scan_log_bwd(la, lb, h, dy, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+        for (i, t) in [(0, 0), (0, 10), (1, 11), (1, 29), (0, 17), (1, 5)]:
+            for which in ("a", "b"):
+                arr, grad = (la, dla) if which == "a" else (lb, dlb)
+                p, m = arr.copy(), arr.copy()
+                p[i, t] += eps
+                m[i, t] -= eps
+                fd = (L(p, lb, lh0) - L(m, lb, lh0)) / (2 * eps) if which == "a" else \
+                     (L(la, p, lh0) - L(la, m, lh0)) / (2 * eps)
+                assert abs(fd - grad[i, t]) < 1e-6 * max(1, abs(fd)), (reverse, which, i, t, fd, grad[i, t])
+        for s in (0, 2):  # segment 1 is empty: its h0 touches nothing
+            for i in range(2):
+                p, m = lh0.copy(), lh0.copy()
+                p[s, i] += eps
+                m[s, i] -= eps
+                fd = (L(la, lb, p) - L(la, lb, m)) / (2 * eps)
+                assert abs(fd - dlh0[s, i]) < 1e-6 * max(1, abs(fd))
+        assert np.all(dlh0[1] == 0.0)
+
+
+def test_log_bwd_shift_scales_gradients(oracle_lib):
+    """log_b + c and log_h0 + c scale h by e^c and leave the adjoint state alone,
+    so every log-input gradient of <dy, h> scales by e^c."""
+    r = _rng(16)
+    la = -np.log1p(np.exp(r.standard_normal((3, 400))))
+    lb = r.standard_normal((3, 400))
+    lh0 = r.standard_normal(3)
+    dy = r.standard_normal(la.shape)
+    c = -3.25
+    h1 = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0)
+    h2 = oracle_lib.scan_log_fwd(la, lb + c, log_h0=lh0 + c)
+    g1 = oracle_lib.scan_log_bwd(la, lb, h1, dy, log_h0=lh0)
+    g2 = oracle_lib.scan_log_bwd(la, lb + c, h2, dy, log_h0=lh0 + c)
+    for x1, x2 in zip(g1, g2):
+        np.testing.assert_allclose(x2, x1 * np.exp(c), rtol=1e-12, atol=1e-300)
+
+
+def test_log_bwd_zero_gate(oracle_lib):
+    """log_a = -inf (a = 0) at t: no gradient reaches log_a_t, and nothing after t
+    reaches the log inputs before t."""
+    r = _rng(17)
+    la = -np.log1p(np.exp(r.standard_normal((2, 80))))
+    lb = r.standard_normal((2, 80))
+    la[:, 30] = -np.inf
+    dy = r.standard_normal(la.shape)
+    h = oracle_lib.scan_log_fwd(la, lb)
+    dla, dlb, _ = oracle_lib.scan_log_bwd(la, lb, h, dy)
+    assert np.all(dla[:, 30] == 0.0)
+    dy2 = dy.copy()
+    dy2[:, 30:] = r.standard_normal((2, 50))
+    dla2, dlb2, _ = oracle_lib.scan_log_bwd(la, lb, h, dy2)
+    assert np.array_equal(dla[:, :30], dla2[:, :30]) and np.array_equal(dlb[:, :30], dlb2[:, :30])
+
+
+def test_log_bwd_is_linear_adjoint_through_exp(oracle_lib):
+    """Chain rule through exp against the independently pinned linear adjoint:
+    dlog_b = dx * b, dlog_a = dg * a, dlog_h0 = dh0 * h0 (to rounding: the two sides
+    take exp in different libraries)."""
+    d = gen.logspace(B=2, D=4, T=1500)
+    la, lb = d["log_a"].astype(np.float64), d["log_b"].astype(np.float64)
+    r = _rng(18)
+    cu = np.array([0, 600, 1500], dtype=np.int32)
+    lh0 = r.standard_normal((2, 8))
+    dy = r.standard_normal(la.shape)
+    for reverse in (False, True):
+        h = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+        dla, dlb, dlh0 = oracle_lib.scan_log_bwd(la, lb, h, dy, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+        dx, dg, dh0 = oracle_lib.scan_bwd(np.exp(la), h, dy, h0=np.exp(lh0), cu_seqlens=cu, reverse=reverse)
+        np.testing.assert_allclose(dlb, dx * np.exp(lb), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dla, dg * np.exp(la), rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dlh0, dh0 * np.exp(lh0), rtol=1e-11, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # matrix-affine
 # ---------------------------------------------------------------------------

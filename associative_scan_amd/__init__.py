@@ -9,6 +9,7 @@ Entry points (same names as the C ABI):
     scan_fwd(g, x, h0=None, cu_seqlens=None, reverse=False) -> h
     scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dx, dg, dh0)
     scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False) -> h
+    scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False) -> (dlog_a, dlog_b, dlog_h0)
     matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False) -> h
     matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dA, dB, dh0)
 
@@ -29,15 +30,16 @@ import torch
 
 __all__ = [
     "lib", "library_path", "Problem", "MscanError",
-    "scan_fwd", "scan_bwd", "scan_log_fwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
-    "scan_causal", "scan_bidirectional_branched",
+    "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
+    "scan_causal", "scan_bidirectional_branched", "scan_log",
     "workspace_bytes", "OP_SCAN_FWD", "OP_SCAN_BWD", "OP_SCAN_LOG_FWD", "OP_MATRIX_FWD", "OP_MATRIX_BWD",
+    "OP_SCAN_LOG_BWD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmscan.so")
 
-OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD = range(5)
+OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD, OP_SCAN_LOG_BWD = range(6)
 _F32, _BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error"}
 
@@ -70,6 +72,7 @@ def _load():
         "scan_fwd": (i32, [P, i32, p, p, p, p, p, sz, p]),
         "scan_bwd": (i32, [P, i32, p, p, p, p, p, p, p, p, sz, p]),
         "scan_log_fwd": (i32, [P, p, p, p, p, p, sz, p]),
+        "scan_log_bwd": (i32, [P, p, p, p, p, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_fwd": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_bwd": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
         "mscan_status_string": (ctypes.c_char_p, [i32]),
@@ -288,6 +291,36 @@ def scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
     return h
 
 
+def scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
+    """Adjoint of scan_log_fwd for dL/dh = dy: (dlog_a, dlog_b, dlog_h0)."""
+    for t, n in ((log_a, "log_a"), (log_b, "log_b"), (h, "h"), (dy, "dy")):
+        if t.dtype != torch.float32 or t.shape != log_a.shape:
+            raise ValueError(f"{n} must be a float32 tensor of log_a's shape")
+    rows, T, stride = _rows_view(log_a, "log_a")
+    for t, n in ((log_b, "log_b"), (h, "h"), (dy, "dy")):
+        if _rows_view(t, n)[2] != stride:
+            raise ValueError("log_a, log_b, h and dy must share the row stride")
+    if stride != T:
+        raise ValueError("scan_log_bwd takes contiguous rows")
+    dev = log_a.device
+    cu, nseg = _segments(cu_seqlens, dev, T)
+    log_h0 = _h0(log_h0, nseg, rows, (), "log_h0")
+    dla = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
+    dlb = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
+    dlh0 = torch.empty((nseg, rows), dtype=torch.float32, device=dev) if need_dh0 else None
+    if rows == 0 or T == 0:
+        if dlh0 is not None:
+            dlh0.zero_()
+        return dla, dlb, dlh0
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_BWD))
+    _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
+                                            _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), _ptr(ws), ws.numel(),
+                                            ctypes.c_void_p(sh)))
+    return dla, dlb, dlh0
+
+
 def _mat_dims(A, Bh, nameB):
     if A.dtype != torch.float32 or Bh.dtype != torch.float32:
         raise ValueError("matrix scan inputs must be float32")
@@ -363,6 +396,30 @@ class _ScanFn(torch.autograd.Function):
         if dh0 is not None and h0 is not None:
             dh0 = dh0.view(h0.shape)
         return dg.to(g.dtype), dx.to(ctx.x_dtype), dh0, None, None
+
+
+class _LogScanFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, log_a, log_b, log_h0, cu_seqlens, reverse):
+        h = scan_log_fwd(log_a, log_b, log_h0=log_h0, cu_seqlens=cu_seqlens, reverse=reverse)
+        ctx.save_for_backward(log_a, log_b, h, log_h0, cu_seqlens)
+        ctx.reverse = reverse
+        return h
+
+    @staticmethod
+    def backward(ctx, dy):
+        log_a, log_b, h, log_h0, cu = ctx.saved_tensors
+        dla, dlb, dlh0 = scan_log_bwd(log_a, log_b, h, dy.contiguous().float(), log_h0=log_h0, cu_seqlens=cu,
+                                      reverse=ctx.reverse, need_dh0=log_h0 is not None and ctx.needs_input_grad[2])
+        if dlh0 is not None and log_h0 is not None:
+            dlh0 = dlh0.view(log_h0.shape)
+        return dla, dlb, dlh0, None, None
+
+
+def scan_log(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
+    """Differentiable log-space scan: h = exp of h_t = a_t h_{t-1} + b_t carried
+    in log space, with the native adjoint kernel for the backward."""
+    return _LogScanFn.apply(log_a, log_b, log_h0, cu_seqlens, reverse)
 
 
 def scan_causal(gates, tokens, cu_seqlens=None, h0=None):

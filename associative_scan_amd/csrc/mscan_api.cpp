@@ -86,6 +86,8 @@ size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
       return scalar_ws_bytes(prob, 3, false);
     case MSCAN_OP_SCAN_LOG_FWD:
       return scalar_ws_bytes(prob, 5, true);
+    case MSCAN_OP_SCAN_LOG_BWD:
+      return scalar_ws_bytes(prob, 3, true);
     case MSCAN_OP_MATRIX_FWD:
     case MSCAN_OP_MATRIX_BWD:
       if (!matrix_shape_ok(k, v)) return 0;
@@ -189,6 +191,45 @@ mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const f
   a.stride = prob->row_stride;
   a.ws = ws;
   return hip_status(mscan::launch_log(a, (hipStream_t)stream));
+}
+
+mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const float* log_b, const float* h,
+                          const float* dy, const float* log_h0, float* dlog_a, float* dlog_b, float* dlog_h0,
+                          void* ws, size_t ws_bytes, void* stream) {
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (!log_a || !log_b || !h || !dy || !dlog_a || !dlog_b) return MSCAN_ERR_INVALID;
+  if (!aligned16(log_a) || !aligned16(log_b) || !aligned16(h) || !aligned16(dy) || !aligned16(dlog_a) ||
+      !aligned16(dlog_b))
+    return MSCAN_ERR_INVALID;
+  if ((log_h0 && ((uintptr_t)log_h0 & 3u)) || (dlog_h0 && ((uintptr_t)dlog_h0 & 3u))) return MSCAN_ERR_INVALID;
+  const int64_t nt = scalar_tiles_for(prob, MSCAN_F32);
+  if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, true)))
+    return MSCAN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (dlog_h0 && prob->cu_seqlens) {
+    // empty sequences have no element to write their (zero) gradient
+    const mscan_status z = hip_status(mscan::launch_zero(dlog_h0, (size_t)prob->nseg * (size_t)prob->rows * 4u, st));
+    if (z != MSCAN_OK) return z;
+  }
+  mscan::ScalarArgs a{};
+  a.g = log_a;
+  a.lb = log_b;
+  a.b = dy;
+  a.hs = h;
+  a.h0 = log_h0;
+  a.out0 = dlog_b;
+  a.out1 = dlog_a;
+  a.dh0 = dlog_h0;
+  a.cu = prob->cu_seqlens;
+  a.nseg = prob->nseg;
+  a.rev = prob->reverse ? 0 : 1;  // the adjoint runs against the forward's order
+  a.rows = prob->rows;
+  a.T = prob->T;
+  a.stride = prob->row_stride;
+  a.ws = ws;
+  return hip_status(mscan::launch_log_bwd(a, st));
 }
 
 mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

@@ -10,6 +10,7 @@ namespace mscan {
 struct ScalarArgs {
   const void* g;        // gates, fp32 or bf16
   const void* b;        // forward: x (same type as g); backward: dy (fp32)
+  const float* lb;      // log-space backward: log b (the gate g is log a)
   const float* hs;      // backward: forward states h
   const float* h0;      // [nseg][rows] or null
   float* out0;          // forward: h; backward: dx
@@ -32,6 +33,9 @@ bool scalar_uses_lookback(int64_t rows, int64_t ntiles);
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
 // Log-space forward (g = log a, b = log b, h0 = log h0; fp32).
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st);
+// Log-space backward (g = log a, lb = log b, b = dy, hs = h, h0 = log h0;
+// out0 = dlog_b, out1 = dlog_a, dh0 = dlog_h0; fp32).
+hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st);
 
 // Arguments of the matrix-affine kernels (see scan_matrix.hip). Strides and
 // offsets count time steps; a step holds a k x k block of A and k x v blocks

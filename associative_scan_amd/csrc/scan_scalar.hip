@@ -8,6 +8,12 @@
 // only the forward's inputs and outputs ("Triton scan kernels", "Autograd
 // integration and the reversed-scan backward").
 //
+// Log-space backward ("Triton scan kernels": parallel_scan_log carries the
+// same recurrence with a = e^{log a}, b = e^{log b}): the same adjoint scan with
+// the gate exponentiated as it is loaded, and the outputs taken through exp by
+// the chain rule: dlog_b = lam * b, dlog_a = lam * a * h_prev,
+// dlog_h0 = lam * a * h0 (template flag LOGB).
+//
 // Both directions are the same affine scan run along a "processing order":
 //   forward : element (a, b) = (g_t, x_t), order = time (reversed if reverse),
 //             a sequence's first element becomes (0, g h0 + x);
@@ -135,8 +141,10 @@ enum : int { kRowLoop = 0, kLookback = 1 };
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <class Ops, typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL>
+template <class Ops, typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL,
+          bool LOGB = false>
 __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
+  static_assert(!LOGB || (BWD && sizeof(Tin) == 4), "the log-space adjoint is an fp32 backward");
   using S = typename Ops::S;
   using C = typename Ops::C;
   constexpr int NS = Ops::NS, NC = Ops::NC, ND = NS + NC;
@@ -173,7 +181,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   const Tin* gp = (const Tin*)a.g;
   const float* h0p = a.h0;
   const bool has_h0 = h0p != nullptr;
-  const float h0row = (!VARLEN && has_h0) ? h0p[r] : 0.f;
+  // initial state as the backward uses it (h_prev of a sequence's first step)
+  auto h0val = [&](int64_t i) -> float { return LOGB ? __expf(h0p[i]) : h0p[i]; };
+  const float h0row = (!VARLEN && has_h0) ? h0val(r) : 0.f;
 
   Workspace ws{};
   if constexpr (MODE == kLookback) ws = ws_view(a.ws);
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     };
 
     // ---- load: every vector of the tile is in flight before the first use
-    float Lg[SUBS][EL], Lb[SUBS][EL], Lh[BWD ? SUBS : 1][EL];
+    float Lg[SUBS][EL], Lb[SUBS][EL], Lh[BWD ? SUBS : 1][EL], Lx[LOGB ? SUBS : 1][EL];
     if (interior) {
 #pragma unroll
       for (int s = 0; s < SUBS; ++s) {
@@ -240,6 +250,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         } else {
           load_span<float, EL>((const float*)a.b + base + u0, Lb[s]);
           load_span<float, EL>(a.hs + base + u0, Lh[s]);
+          if constexpr (LOGB) load_span<float, EL>(a.lb + base + u0, Lx[s]);
         }
       }
     } else {
@@ -256,9 +267,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           } else {
             Lb[s][e] = ok ? ((const float*)a.b)[rowoff + t] : 0.f;
             Lh[s][e] = ok ? a.hs[rowoff + t] : 0.f;
+            if constexpr (LOGB) Lx[s][e] = ok ? a.lb[rowoff + t] : 0.f;
           }
         }
       }
+    }
+    if constexpr (LOGB) {
+      // a = e^{log a} (0 for log a = -inf), b = e^{log b}
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s)
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          Lg[s][e] = __expf(Lg[s][e]);
+          Lx[s][e] = __expf(Lx[s][e]);
+        }
     }
     // processing order: element e of a lane is physical component P_(e)
     auto P_ = [](int e) { return REV ? EL - 1 - e : e; };
@@ -293,6 +315,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
           const int64_t t = u_of(j) - lead;
           gprev = (j >= 0 && t >= 0 && t < T) ? InTraits<Tin>::load1(gp + rowoff + t) : 0.f;
+          if constexpr (LOGB) gprev = (j >= 0 && t >= 0 && t < T) ? __expf(gprev) : 0.f;
         }
         if (s + 1 < SUBS) {
           const float hn = readlane_f(N[s + 1][0], 0);
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             const bool last = REV ? is_start : is_end;
             if (first || last) {
               const int sk = min(max(seg.k0 + k, 0), a.nseg - 1);
-              const float hv = has_h0 ? h0p[(int64_t)sk * a.rows + r] : 0.f;
+              const float hv = has_h0 ? h0val((int64_t)sk * a.rows + r) : 0.f;
               if (first) {
                 if constexpr (!BWD) Ops::first_ab(A[s][e], B[s][e], hv, has_h0);
                 else A[s][e] = 0.f;
@@ -502,8 +525,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       float o0[EL], o1[EL];
 #pragma unroll
       for (int e = 0; e < EL; ++e) {
-        o0[P_(e)] = O[s][e];
-        if constexpr (BWD) o1[P_(e)] = O[s][e] * N[s][e];
+        if constexpr (!LOGB) {
+          o0[P_(e)] = O[s][e];
+          if constexpr (BWD) o1[P_(e)] = O[s][e] * N[s][e];
+        } else {
+          o0[P_(e)] = O[s][e] * Lx[s][P_(e)];             // dlog_b = lam * b
+          o1[P_(e)] = (O[s][e] * N[s][e]) * G[s][e];      // dlog_a = lam * h_prev * a
+        }
       }
       if (interior) {
         store_span<EL>(a.out0 + base + u0, o0);
@@ -527,7 +555,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             const int64_t t = u0 + P_(e) - lead;
             int sk = 0;
             if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
-            a.dh0[(int64_t)sk * a.rows + r] = G[s][e] * O[s][e];
+            // dh0 = g * lam; log space: dlog_h0 = a * lam * h0 (N holds h0 there)
+            a.dh0[(int64_t)sk * a.rows + r] = LOGB ? (G[s][e] * O[s][e]) * N[s][e] : G[s][e] * O[s][e];
           }
         }
       }
@@ -539,7 +568,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 // host launch
 // ---------------------------------------------------------------------------
 
-template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL>
+template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL, bool LOGB = false>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
   ScalarArgs a = a0;
@@ -549,16 +578,16 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   const dim3 block(WAVES * 64);
   if (!lookback) {
     const dim3 grid((unsigned)a.rows);
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
   } else {
     // fresh descriptors for this call (zero tag = not published)
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(Ops::NS + Ops::NC);
     const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
     if (z != hipSuccess) return z;
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -595,6 +624,12 @@ hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_
 // Log-space forward: fp32 (log a, log b), same tiles as the fp32 scalar scan.
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
   return a.rev ? launch_cfg<LogOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LogOps, float, false, false, 4, 4, 1>(a, st);
+}
+
+// Log-space backward: the fp32 adjoint scan with exponentiated gates.
+hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
+  return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true>(a, st)
+               : launch_cfg<LinOps, float, true, false, 4, 4, 1, true>(a, st);
 }
 
 }  // namespace mscan

@@ -317,9 +317,19 @@ def other_workloads(m, gen, torch, dev, stream, np):
     la = -torch.nn.functional.softplus(torch.randn((B, D, T), device=dev, generator=gt))
     lb = torch.randn((B, D, T), device=dev, generator=gt)
     n = B * D * T
-    out["logspace"] = {"workload": "B=8 D=1024 T=8192 fp32, log_a = -softplus(N(0,1)), log_b ~ N(0,1)",
-                       "fwd": _entry(12 * n, _time(torch, stream, lambda: m.scan_log_fwd(la, lb), 10), n, "elements")}
-    del la, lb
+    dyl = torch.randn((B, D, T), device=dev, generator=gt)
+    hl = m.scan_log_fwd(la, lb)
+
+    def lfb():
+        h_ = m.scan_log_fwd(la, lb)
+        m.scan_log_bwd(la, lb, h_, dyl, need_dh0=False)
+
+    out["logspace"] = {"workload": "B=8 D=1024 T=8192 fp32, log_a = -softplus(N(0,1)), log_b ~ N(0,1), dy ~ N(0,1)",
+                       "fwd": _entry(12 * n, _time(torch, stream, lambda: m.scan_log_fwd(la, lb), 10), n, "elements"),
+                       "bwd": _entry(24 * n, _time(torch, stream, lambda: m.scan_log_bwd(la, lb, hl, dyl, need_dh0=False), 10),
+                                     n, "elements"),
+                       "fwd_bwd": _entry(36 * n, _time(torch, stream, lfb, 10), n, "elements")}
+    del la, lb, dyl, hl
     torch.cuda.empty_cache()
 
     # matrix-affine: rotations (k=2, v=1) and scaled orthogonal blocks (k=4, v=4)

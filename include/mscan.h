@@ -92,7 +92,8 @@ typedef enum {
   MSCAN_OP_SCAN_BWD = 1,
   MSCAN_OP_SCAN_LOG_FWD = 2,
   MSCAN_OP_MATRIX_FWD = 3,
-  MSCAN_OP_MATRIX_BWD = 4
+  MSCAN_OP_MATRIX_BWD = 4,
+  MSCAN_OP_SCAN_LOG_BWD = 5
 } mscan_op;
 
 typedef struct {
@@ -144,6 +145,26 @@ MSCAN_API mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const v
  *   h : fp32 [rows][T] = exp(log h_t), written.                               */
 MSCAN_API mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
                           const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream);
+
+/* Log-space backward: the adjoint of scan_log_fwd with respect to its log
+ * inputs, for a loss L with dL/dh = dy ("Triton scan kernels", "One
+ * associative-scan family": the log-space member is h_t = a_t h_{t-1} + b_t
+ * with a = e^{log a}, b = e^{log b}; the page's own backward for it recomputes
+ * through autograd, "Measured results"). Walking each sequence against the
+ * forward's direction:
+ *   lam_t    = dy_t + a_{t+1} lam_{t+1}  (no a past a sequence end)
+ *   dlog_b_t = lam_t * b_t
+ *   dlog_a_t = lam_t * a_t * h_{t-1}     (h0 = e^{log_h0} before a sequence start)
+ *   dlog_h0  = lam_s * a_s * h0          at each sequence's first step s
+ * (reverse: the mirror image, as for scan_bwd).
+ *   log_a, log_b : fp32 [rows][T] (the forward's inputs);
+ *   h : fp32 [rows][T], the forward's output; dy : fp32 [rows][T];
+ *   log_h0 : fp32 [nseg][rows] or NULL.
+ *   dlog_a, dlog_b : fp32 [rows][T], written. dlog_h0 : fp32 [nseg][rows] or
+ *   NULL; an empty sequence gets 0.                                          */
+MSCAN_API mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const float* log_b,
+                          const float* h, const float* dy, const float* log_h0, float* dlog_a,
+                          float* dlog_b, float* dlog_h0, void* ws, size_t ws_bytes, void* stream);
 
 /* Matrix-affine forward ("Triton scan kernels", "One associative-scan family":
  * h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t k x v; matrix_scan is

@@ -106,3 +106,82 @@ def test_log_matches_linear_scan_on_exp_inputs(m):
     h_lin = m.scan_fwd(_t(np.exp(la)), _t(np.exp(lb)))
     err = ((h_log - h_lin).abs() / (1 + h_lin.abs())).max().item()
     assert err <= 1e-4, err
+
+
+# ---------------------------------------------------------------------------
+# log-space backward (scan_log_bwd): tolerance 1e-4 * (1 + |ref|) per element
+# ---------------------------------------------------------------------------
+TAU_GRAD = 1e-4
+
+
+def _log_bwd_case(m, o, la, lb, dy, lh0=None, cu=None, reverse=False):
+    cu_t = None if cu is None else _t(cu, torch.int32)
+    lh0_t = None if lh0 is None else _t(lh0)
+    la_t, lb_t = _t(la), _t(lb)
+    h = m.scan_log_fwd(la_t, lb_t, log_h0=lh0_t, cu_seqlens=cu_t, reverse=reverse)
+    dla, dlb, dlh0 = m.scan_log_bwd(la_t, lb_t, h, _t(dy), log_h0=lh0_t, cu_seqlens=cu_t, reverse=reverse)
+    href = o.scan_log_fwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    ra, rb, rh0 = o.scan_log_bwd(la, lb, href, dy, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    close(dlb, rb, TAU_GRAD, "dlog_b")
+    close(dla, ra, TAU_GRAD, "dlog_a")
+    if lh0 is not None:
+        close(dlh0.reshape(rh0.shape), rh0, TAU_GRAD, "dlog_h0")
+    return dla, dlb, dlh0
+
+
+@pytest.mark.timeout(400)
+def test_log_bwd_workload_full(m, oracle_lib):
+    """B=8, D=1024, T=8192, log_a = -softplus(N(0,1)), log_b ~ N(0,1), dy ~ N(0,1):
+    every element of both gradients."""
+    d = gen.logspace()
+    dy = np.random.default_rng(41).standard_normal(d["log_a"].shape).astype(np.float32)
+    _log_bwd_case(m, oracle_lib, d["log_a"], d["log_b"], dy)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 4095, 4096, 4097, 20000])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_bwd_lengths_with_h0(m, oracle_lib, T, reverse):
+    r = np.random.default_rng(100 + T + reverse)
+    la, lb = _inputs(r, 5, T)
+    dy = r.standard_normal((5, T)).astype(np.float32)
+    lh0 = r.standard_normal(5).astype(np.float32)
+    _log_bwd_case(m, oracle_lib, la, lb, dy, lh0=lh0, reverse=reverse)
+
+
+@pytest.mark.parametrize("rows", [3, 1024])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_bwd_varlen(m, oracle_lib, rows, reverse):
+    r = np.random.default_rng(200 + rows + reverse)
+    T = 15000
+    la, lb = _inputs(r, rows, T)
+    dy = r.standard_normal((rows, T)).astype(np.float32)
+    cu = np.concatenate([[0, 0], gen.segments_random(r, T, 9)[1:], [T]]).astype(np.int32)
+    lh0 = r.standard_normal((len(cu) - 1, rows)).astype(np.float32)
+    _, _, dlh0 = _log_bwd_case(m, oracle_lib, la, lb, dy, lh0=lh0, cu=cu, reverse=reverse)
+    assert torch.all(dlh0[0] == 0) and torch.all(dlh0[-1] == 0), "empty sequences get a zero gradient"
+
+
+def test_log_bwd_zero_gates(m, oracle_lib):
+    """log a = -inf: no gradient reaches log a there, and nothing crosses it."""
+    r = np.random.default_rng(6)
+    la, lb = _inputs(r, 4, 9000)
+    la[:, ::97] = -np.inf
+    dy = r.standard_normal((4, 9000)).astype(np.float32)
+    dla, _, _ = _log_bwd_case(m, oracle_lib, la, lb, dy, lh0=np.zeros(4, np.float32))
+    assert torch.all(dla[:, ::97] == 0)
+
+
+def test_log_autograd_wrapper(m, oracle_lib):
+    """scan_log's autograd backward is the native adjoint kernel."""
+    r = np.random.default_rng(7)
+    la, lb = _inputs(r, 6, 5000)
+    lh0 = r.standard_normal(6).astype(np.float32)
+    dy = r.standard_normal((6, 5000)).astype(np.float32)
+    la_t, lb_t, lh0_t = (_t(x).requires_grad_() for x in (la, lb, lh0))
+    h = m.scan_log(la_t, lb_t, log_h0=lh0_t)
+    (h * _t(dy)).sum().backward()
+    href = oracle_lib.scan_log_fwd(la, lb, log_h0=lh0)
+    ra, rb, rh0 = oracle_lib.scan_log_bwd(la, lb, href, dy, log_h0=lh0)
+    close(la_t.grad, ra, TAU_GRAD, "dlog_a")
+    close(lb_t.grad, rb, TAU_GRAD, "dlog_b")
+    close(lh0_t.grad, rh0.reshape(-1), TAU_GRAD, "dlog_h0")

@@ -105,3 +105,16 @@ def test_scan_bwd_validation(m):
 def test_null_problem(m):
     st = m.lib.scan_fwd(None, 0, FAKE, FAKE, None, FAKE, None, 0, None)
     assert st == 1
+
+
+def test_scan_log_bwd_validation(m):
+    p = _prob(m)
+    # args: prob, log_a, log_b, h, dy, log_h0, dlog_a, dlog_b, dlog_h0, ws, ws_bytes, stream
+    assert m.lib.scan_log_bwd(ctypes.byref(p), FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert m.lib.scan_log_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 8, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert m.lib.scan_log_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, FAKE, None, None, 0, None) == 1
+    long = _prob(m, rows=4, T=20000)
+    need = m.workspace_bytes(long, m.OP_SCAN_LOG_BWD)
+    assert need == 128 + 4 * 5 * 24  # 3 words per 4096-element tile, 5 tiles per row
+    assert m.lib.scan_log_bwd(ctypes.byref(long), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need - 8,
+                              None) == 3

@@ -33,7 +33,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-__all__ = ["build", "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd",
+__all__ = ["build", "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "gate", "gate_grad",
+           "scan_fwd_gated", "scan_bwd_gated", "scan_log_fwd_gated", "scan_log_bwd_gated", "matrix_affine_scan_fwd",
            "matrix_affine_scan_bwd", "num_threads"]
 
 
@@ -61,6 +62,8 @@ def _load():
         lib.oracle_scan_bwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p, p, p, p]
         lib.oracle_scan_log_fwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p]
         lib.oracle_scan_log_bwd.argtypes = [i64, i64, i64, p, i32, i32, p, p, p, p, p, p, p, p]
+        lib.oracle_gate.argtypes = [i32, i64, p, p]
+        lib.oracle_gate_grad.argtypes = [i32, i64, p, p, p]
         lib.oracle_matrix_fwd.argtypes = [i64, i64, i64, p, i32, i32, i32, i32, p, p, p, p]
         lib.oracle_matrix_bwd.argtypes = [i64, i64, i64, p, i32, i32, i32, i32, p, p, p, p, p, p, p]
         for f in (lib.oracle_scan_fwd, lib.oracle_scan_bwd, lib.oracle_scan_log_fwd,
@@ -157,6 +160,50 @@ def scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=Fals
     _load().oracle_scan_log_bwd(rows, T, T, _ptr(cu), nseg, int(bool(reverse)), _ptr(la), _ptr(lb), _ptr(h),
                                 _ptr(dy), _ptr(lh0), _ptr(dla), _ptr(dlb), _ptr(dlh0))
     return dla, dlb, dlh0
+
+
+SIGMOID, NEG_SOFTPLUS = 1, 2
+
+
+def gate(kind, z):
+    """f(z): sigmoid (kind 1) or -softplus (kind 2); see oracle_gate."""
+    z = _f64(z)
+    out = np.zeros_like(z)
+    _load().oracle_gate(int(kind), z.size, _ptr(z), _ptr(out))
+    return out
+
+
+def gate_grad(kind, z, dact):
+    """dz = dact * f'(z); see oracle_gate_grad."""
+    z, dact = _f64(z), _f64(dact)
+    assert z.shape == dact.shape
+    dz = np.zeros_like(z)
+    _load().oracle_gate_grad(int(kind), z.size, _ptr(z), _ptr(dact), _ptr(dz))
+    return dz
+
+
+def scan_fwd_gated(z, x, h0=None, cu_seqlens=None, reverse=False):
+    """Scalar scan with gates g = sigmoid(z): the activation, then the scan."""
+    return scan_fwd(gate(SIGMOID, z), x, h0=h0, cu_seqlens=cu_seqlens, reverse=reverse)
+
+
+def scan_bwd_gated(z, h, dy, h0=None, cu_seqlens=None, reverse=False):
+    """Adjoint of scan_fwd_gated: (dx, dz, dh0), dz = dg * g (1 - g) by the chain rule."""
+    g = gate(SIGMOID, z)
+    dx, dg, dh0 = scan_bwd(g, h, dy, h0=h0, cu_seqlens=cu_seqlens, reverse=reverse)
+    return dx, gate_grad(SIGMOID, z, dg), dh0
+
+
+def scan_log_fwd_gated(z, log_b, log_h0=None, cu_seqlens=None, reverse=False):
+    """Log-space scan with log_a = -softplus(z): the activation, then the scan."""
+    return scan_log_fwd(gate(NEG_SOFTPLUS, z), log_b, log_h0=log_h0, cu_seqlens=cu_seqlens, reverse=reverse)
+
+
+def scan_log_bwd_gated(z, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False):
+    """Adjoint of scan_log_fwd_gated: (dz, dlog_b, dlog_h0), dz = dlog_a * (-sigmoid(z))."""
+    la = gate(NEG_SOFTPLUS, z)
+    dla, dlb, dlh0 = scan_log_bwd(la, log_b, h, dy, log_h0=log_h0, cu_seqlens=cu_seqlens, reverse=reverse)
+    return gate_grad(NEG_SOFTPLUS, z, dla), dlb, dlh0
 
 
 def _mat_shapes(A, B_or_h):

@@ -311,6 +311,38 @@ API void oracle_matrix_bwd(int64_t rows, int64_t T, int64_t row_stride, const in
   }
 }
 
+/* ---------------------------------------------------------------------------
+ * Gate activations for scans that take gate logits z instead of gates.
+ * The workloads on the pages draw their gates this way: the packed scan's
+ * g = sigmoid(z) (README benchmark inputs), and the log-space scan's
+ * log_a = -softplus(z) (minGRU, "One associative-scan family": the base
+ * log-space MinGRU's coefficient is a positive scalar in (0, 1)).
+ *   kind 1: f(z) = sigmoid(z) = 1 / (1 + exp(-z)),  f'(z) = f(z) (1 - f(z))
+ *   kind 2: f(z) = -softplus(z) = -log(1 + exp(z)),  f'(z) = -sigmoid(z)
+ * oracle_gate writes f(z); oracle_gate_grad writes dz = dact * f'(z).
+ * softplus is evaluated as max(z, 0) + log1p(exp(-|z|)) so it neither
+ * overflows nor loses its tail for large |z|.
+ * ------------------------------------------------------------------------- */
+static double sigmoid_d(double z) {
+  if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+  const double e = exp(z);
+  return e / (1.0 + e);
+}
+static double softplus_d(double z) { return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z))); }
+
+API void oracle_gate(int32_t kind, int64_t n, const double* z, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (kind == 1) ? sigmoid_d(z[i]) : -softplus_d(z[i]);
+}
+
+API void oracle_gate_grad(int32_t kind, int64_t n, const double* z, const double* dact, double* dz) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const double s = sigmoid_d(z[i]);
+    dz[i] = dact[i] * ((kind == 1) ? s * (1.0 - s) : -s);
+  }
+}
+
 API int oracle_abi_version(void) { return 1; }
 
 /* Number of threads the parallel loops above use (OpenMP's current team size). */

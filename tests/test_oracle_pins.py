@@ -18,6 +18,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 import scipy.signal
+import scipy.special
 
 import gen
 
@@ -468,6 +469,67 @@ def test_log_bwd_is_linear_adjoint_through_exp(oracle_lib):
         np.testing.assert_allclose(dlb, dx * np.exp(lb), rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(dla, dg * np.exp(la), rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(dlh0, dh0 * np.exp(lh0), rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# gate activations (scans that take gate logits)
+# ---------------------------------------------------------------------------
+def test_gate_sigmoid_against_library(oracle_lib):
+    z = np.concatenate([np.linspace(-40, 40, 2001), [-750.0, 750.0, 0.0]])
+    g = oracle_lib.gate(1, z)
+    np.testing.assert_allclose(g, scipy.special.expit(z), rtol=1e-15, atol=0)
+    assert g[-1] == 0.5 and g[-3] == 0.0 and g[-2] == 1.0
+    # sigmoid(-z) = 1 - sigmoid(z) (absolute: the right side cancels for large z)
+    np.testing.assert_allclose(oracle_lib.gate(1, -z), 1.0 - g, rtol=0, atol=3e-16)
+
+
+def test_gate_neg_softplus_against_library(oracle_lib):
+    z = np.concatenate([np.linspace(-40, 40, 2001), [-700.0, 700.0]])
+    la = oracle_lib.gate(2, z)
+    np.testing.assert_allclose(la, -np.logaddexp(0.0, z), rtol=1e-15, atol=0)
+    # log a = -softplus(z) is log sigmoid(-z): a = sigmoid(-z)
+    np.testing.assert_allclose(np.exp(la), scipy.special.expit(-z), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_gate_grad_finite_differences(oracle_lib, kind):
+    r = _rng(19)
+    z = np.concatenate([r.standard_normal(50) * 4, [0.0, -30.0, 30.0]])
+    dact = r.standard_normal(z.shape)
+    dz = oracle_lib.gate_grad(kind, z, dact)
+    eps = 1e-6
+    fd = (oracle_lib.gate(kind, z + eps) - oracle_lib.gate(kind, z - eps)) / (2 * eps) * dact
+    np.testing.assert_allclose(dz, fd, rtol=1e-7, atol=1e-10)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_gated_scans_adjoint_dot_product(oracle_lib, reverse):
+    """<dy, J v> = <J^T dy, v> through the gate: tangents of z enter as f'(z) zd."""
+    r = _rng(20)
+    T = 203
+    z, x = r.standard_normal((3, T)) * 2, r.standard_normal((3, T))
+    cu = gen.segments_random(r, T, 4)
+    h0 = r.standard_normal((4, 3))
+    zd, xd, h0d = r.standard_normal(z.shape), r.standard_normal(z.shape), r.standard_normal(h0.shape)
+    dy = r.standard_normal(z.shape)
+    g = scipy.special.expit(z)
+    _, hd = _tangent_scalar(g, x, h0, g * (1 - g) * zd, xd, h0d, cu, reverse)
+    h = oracle_lib.scan_fwd_gated(z, x, h0=h0, cu_seqlens=cu, reverse=reverse)
+    dx, dz, dh0 = oracle_lib.scan_bwd_gated(z, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    lhs = np.sum(dy * hd)
+    rhs = np.sum(dz * zd) + np.sum(dx * xd) + np.sum(dh0 * h0d)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    # log space: log_a = -softplus(z), tangent of log_a = -sigmoid(z) zd
+    lb = r.standard_normal(z.shape)
+    lh0 = r.standard_normal((4, 3))
+    lbd, lh0d = r.standard_normal(z.shape), r.standard_normal(lh0.shape)
+    la = -np.logaddexp(0.0, z)
+    _, hd = _tangent_log(la, lb, lh0, -scipy.special.expit(z) * zd, lbd, lh0d, cu, reverse)
+    h = oracle_lib.scan_log_fwd_gated(z, lb, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    dz, dlb, dlh0 = oracle_lib.scan_log_bwd_gated(z, lb, h, dy, log_h0=lh0, cu_seqlens=cu, reverse=reverse)
+    lhs = np.sum(dy * hd)
+    rhs = np.sum(dz * zd) + np.sum(dlb * lbd) + np.sum(dlh0 * lh0d)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
 
 
 # ---------------------------------------------------------------------------

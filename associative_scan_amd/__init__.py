@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dx, dg, dh0)
     scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False) -> h
     scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False) -> (dlog_a, dlog_b, dlog_h0)
+    scan_fwd_gated / scan_bwd_gated (gate logits z, g = sigmoid(z)) -> h / (dx, dz, dh0)
+    scan_log_fwd_gated / scan_log_bwd_gated (log a = -softplus(z)) -> h / (dz, dlog_b, dlog_h0)
     matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False) -> h
     matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False) -> (dA, dB, dh0)
 
@@ -31,7 +33,8 @@ import torch
 __all__ = [
     "lib", "library_path", "Problem", "MscanError",
     "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
-    "scan_causal", "scan_bidirectional_branched", "scan_log",
+    "scan_fwd_gated", "scan_bwd_gated", "scan_log_fwd_gated", "scan_log_bwd_gated",
+    "scan_causal", "scan_bidirectional_branched", "scan_log", "GATE_SIGMOID", "GATE_NEG_SOFTPLUS",
     "workspace_bytes", "OP_SCAN_FWD", "OP_SCAN_BWD", "OP_SCAN_LOG_FWD", "OP_MATRIX_FWD", "OP_MATRIX_BWD",
     "OP_SCAN_LOG_BWD",
 ]
@@ -41,6 +44,7 @@ library_path = os.path.join(_HERE, "libmscan.so")
 
 OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD, OP_SCAN_LOG_BWD = range(6)
 _F32, _BF16 = 0, 1
+GATE_NONE, GATE_SIGMOID, GATE_NEG_SOFTPLUS = 0, 1, 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error"}
 
 
@@ -73,6 +77,10 @@ def _load():
         "scan_bwd": (i32, [P, i32, p, p, p, p, p, p, p, p, sz, p]),
         "scan_log_fwd": (i32, [P, p, p, p, p, p, sz, p]),
         "scan_log_bwd": (i32, [P, p, p, p, p, p, p, p, p, p, sz, p]),
+        "scan_fwd_gated": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
+        "scan_bwd_gated": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "scan_log_fwd_gated": (i32, [P, i32, p, p, p, p, p, sz, p]),
+        "scan_log_bwd_gated": (i32, [P, i32, p, p, p, p, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_fwd": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_bwd": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
         "mscan_status_string": (ctypes.c_char_p, [i32]),
@@ -214,6 +222,15 @@ def _in_dtype(t, name):
 # ---------------------------------------------------------------------------
 def scan_fwd(g, x, h0=None, cu_seqlens=None, reverse=False, out=None):
     """h_t = g_t h_{t-1} + x_t per row and per packed sequence (fp32 result)."""
+    return _scan_fwd(g, x, h0, cu_seqlens, reverse, out, GATE_NONE)
+
+
+def scan_fwd_gated(z, x, h0=None, cu_seqlens=None, reverse=False, out=None):
+    """scan_fwd with gates g = sigmoid(z) computed inside the kernel from logits z."""
+    return _scan_fwd(z, x, h0, cu_seqlens, reverse, out, GATE_SIGMOID)
+
+
+def _scan_fwd(g, x, h0, cu_seqlens, reverse, out, gate):
     if g.shape != x.shape or g.dtype != x.dtype:
         raise ValueError("g and x must have the same shape and dtype")
     rows, T, stride = _rows_view(g, "g")
@@ -234,13 +251,26 @@ def scan_fwd(g, x, h0=None, cu_seqlens=None, reverse=False, out=None):
     sh = torch.cuda.current_stream(dev).cuda_stream
     need = workspace_bytes(prob, OP_SCAN_FWD)
     ws = _workspace(dev, sh, need)
-    _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
-                                    _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    if gate == GATE_NONE:
+        _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
+                                        _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    else:
+        _check("scan_fwd_gated", lib.scan_fwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
+                                                    _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
     return h
 
 
 def scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
     """Adjoint of scan_fwd: (dx, dg, dh0) given the forward's output h and dy."""
+    return _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, GATE_NONE)
+
+
+def scan_bwd_gated(z, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
+    """Adjoint of scan_fwd_gated: (dx, dz, dh0), dz = dg * g (1 - g)."""
+    return _scan_bwd(z, h, dy, h0, cu_seqlens, reverse, need_dh0, GATE_SIGMOID)
+
+
+def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
     if h.dtype != torch.float32 or dy.dtype != torch.float32:
         raise ValueError("h and dy must be float32")
     if g.shape != h.shape or dy.shape != h.shape:
@@ -265,13 +295,27 @@ def scan_bwd(g, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = torch.cuda.current_stream(dev).cuda_stream
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_BWD))
-    _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
-                                    _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    if gate == GATE_NONE:
+        _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
+                                        _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    else:
+        _check("scan_bwd_gated", lib.scan_bwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0),
+                                                    _ptr(dx), _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(),
+                                                    ctypes.c_void_p(sh)))
     return dx, dg, dh0
 
 
 def scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
     """h = exp of the log-space scan of h_t = a_t h_{t-1} + b_t (fp32 in, fp32 out)."""
+    return _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, GATE_NONE)
+
+
+def scan_log_fwd_gated(z, log_b, log_h0=None, cu_seqlens=None, reverse=False):
+    """scan_log_fwd with log a = -softplus(z) computed inside the kernel from logits z."""
+    return _scan_log_fwd(z, log_b, log_h0, cu_seqlens, reverse, GATE_NEG_SOFTPLUS)
+
+
+def _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, gate):
     if log_a.shape != log_b.shape or log_a.dtype != torch.float32 or log_b.dtype != torch.float32:
         raise ValueError("log_a and log_b must be float32 tensors of one shape")
     rows, T, stride = _rows_view(log_a, "log_a")
@@ -286,13 +330,27 @@ def scan_log_fwd(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = torch.cuda.current_stream(dev).cuda_stream
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_FWD))
-    _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
-                                            _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    if gate == GATE_NONE:
+        _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
+                                                _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+    else:
+        _check("scan_log_fwd_gated", lib.scan_log_fwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b),
+                                                            _ptr(log_h0), _ptr(h), _ptr(ws), ws.numel(),
+                                                            ctypes.c_void_p(sh)))
     return h
 
 
 def scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
     """Adjoint of scan_log_fwd for dL/dh = dy: (dlog_a, dlog_b, dlog_h0)."""
+    return _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, GATE_NONE)
+
+
+def scan_log_bwd_gated(z, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
+    """Adjoint of scan_log_fwd_gated: (dz, dlog_b, dlog_h0), dz = dlog_a * (-sigmoid(z))."""
+    return _scan_log_bwd(z, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, GATE_NEG_SOFTPLUS)
+
+
+def _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, gate):
     for t, n in ((log_a, "log_a"), (log_b, "log_b"), (h, "h"), (dy, "dy")):
         if t.dtype != torch.float32 or t.shape != log_a.shape:
             raise ValueError(f"{n} must be a float32 tensor of log_a's shape")
@@ -315,9 +373,14 @@ def scan_log_bwd(log_a, log_b, h, dy, log_h0=None, cu_seqlens=None, reverse=Fals
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = torch.cuda.current_stream(dev).cuda_stream
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_BWD))
-    _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
-                                            _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), _ptr(ws), ws.numel(),
-                                            ctypes.c_void_p(sh)))
+    if gate == GATE_NONE:
+        _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
+                                                _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), _ptr(ws), ws.numel(),
+                                                ctypes.c_void_p(sh)))
+    else:
+        _check("scan_log_bwd_gated", lib.scan_log_bwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b), _ptr(h),
+                                                            _ptr(dy), _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0),
+                                                            _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
     return dla, dlb, dlh0
 
 

@@ -103,8 +103,13 @@ mscan_status mscan_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hip_status(mscan::launch_zero(ws, ws_bytes, (hipStream_t)stream));
 }
 
-mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
-                      const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gate: MSCAN_GATE_NONE (g holds gates) or MSCAN_GATE_SIGMOID (g holds logits)
+mscan_status scalar_fwd_impl(const mscan_problem* prob, int in_dtype, int gate, const void* g, const void* x,
+                             const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
   if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
@@ -126,12 +131,13 @@ mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, co
   a.T = prob->T;
   a.stride = prob->row_stride;
   a.ws = ws;
-  return hip_status(mscan::launch_scalar(a, in_dtype, false, (hipStream_t)stream));
+  return hip_status(gate == MSCAN_GATE_SIGMOID ? mscan::launch_scalar_sigmoid(a, in_dtype, false, (hipStream_t)stream)
+                                               : mscan::launch_scalar(a, in_dtype, false, (hipStream_t)stream));
 }
 
-mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, const float* h,
-                      const float* dy, const float* h0, float* dx, float* dg, float* dh0, void* ws,
-                      size_t ws_bytes, void* stream) {
+mscan_status scalar_bwd_impl(const mscan_problem* prob, int in_dtype, int gate, const void* g, const float* h,
+                             const float* dy, const float* h0, float* dx, float* dg, float* dh0, void* ws,
+                             size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
   if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
@@ -164,10 +170,12 @@ mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, co
   a.T = prob->T;
   a.stride = prob->row_stride;
   a.ws = ws;
-  return hip_status(mscan::launch_scalar(a, in_dtype, true, st));
+  return hip_status(gate == MSCAN_GATE_SIGMOID ? mscan::launch_scalar_sigmoid(a, in_dtype, true, st)
+                                               : mscan::launch_scalar(a, in_dtype, true, st));
 }
 
-mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
+// gate: MSCAN_GATE_NONE (log_a holds log a) or MSCAN_GATE_NEG_SOFTPLUS (logits)
+mscan_status log_fwd_impl(const mscan_problem* prob, int gate, const float* log_a, const float* log_b,
                           const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
@@ -190,12 +198,13 @@ mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const f
   a.T = prob->T;
   a.stride = prob->row_stride;
   a.ws = ws;
-  return hip_status(mscan::launch_log(a, (hipStream_t)stream));
+  return hip_status(gate == MSCAN_GATE_NEG_SOFTPLUS ? mscan::launch_log_softplus(a, false, (hipStream_t)stream)
+                                                    : mscan::launch_log(a, (hipStream_t)stream));
 }
 
-mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const float* log_b, const float* h,
-                          const float* dy, const float* log_h0, float* dlog_a, float* dlog_b, float* dlog_h0,
-                          void* ws, size_t ws_bytes, void* stream) {
+mscan_status log_bwd_impl(const mscan_problem* prob, int gate, const float* log_a, const float* log_b,
+                          const float* h, const float* dy, const float* log_h0, float* dlog_a, float* dlog_b,
+                          float* dlog_h0, void* ws, size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
   if (!log_a || !log_b || !h || !dy || !dlog_a || !dlog_b) return MSCAN_ERR_INVALID;
@@ -229,7 +238,61 @@ mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const f
   a.T = prob->T;
   a.stride = prob->row_stride;
   a.ws = ws;
-  return hip_status(mscan::launch_log_bwd(a, st));
+  return hip_status(gate == MSCAN_GATE_NEG_SOFTPLUS ? mscan::launch_log_softplus(a, true, st)
+                                                    : mscan::launch_log_bwd(a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
+                      const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  return scalar_fwd_impl(prob, in_dtype, MSCAN_GATE_NONE, g, x, h0, h, ws, ws_bytes, stream);
+}
+
+mscan_status scan_bwd(const mscan_problem* prob, int in_dtype, const void* g, const float* h,
+                      const float* dy, const float* h0, float* dx, float* dg, float* dh0, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return scalar_bwd_impl(prob, in_dtype, MSCAN_GATE_NONE, g, h, dy, h0, dx, dg, dh0, ws, ws_bytes, stream);
+}
+
+mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_a, const float* log_b,
+                          const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  return log_fwd_impl(prob, MSCAN_GATE_NONE, log_a, log_b, log_h0, h, ws, ws_bytes, stream);
+}
+
+mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const float* log_b, const float* h,
+                          const float* dy, const float* log_h0, float* dlog_a, float* dlog_b, float* dlog_h0,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return log_bwd_impl(prob, MSCAN_GATE_NONE, log_a, log_b, h, dy, log_h0, dlog_a, dlog_b, dlog_h0, ws, ws_bytes,
+                      stream);
+}
+
+mscan_status scan_fwd_gated(const mscan_problem* prob, int in_dtype, int gate, const void* z, const void* x,
+                            const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  if (gate != MSCAN_GATE_SIGMOID) return MSCAN_ERR_UNSUPPORTED;
+  return scalar_fwd_impl(prob, in_dtype, gate, z, x, h0, h, ws, ws_bytes, stream);
+}
+
+mscan_status scan_bwd_gated(const mscan_problem* prob, int in_dtype, int gate, const void* z, const float* h,
+                            const float* dy, const float* h0, float* dx, float* dz, float* dh0, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (gate != MSCAN_GATE_SIGMOID) return MSCAN_ERR_UNSUPPORTED;
+  return scalar_bwd_impl(prob, in_dtype, gate, z, h, dy, h0, dx, dz, dh0, ws, ws_bytes, stream);
+}
+
+mscan_status scan_log_fwd_gated(const mscan_problem* prob, int gate, const float* z, const float* log_b,
+                                const float* log_h0, float* h, void* ws, size_t ws_bytes, void* stream) {
+  if (gate != MSCAN_GATE_NEG_SOFTPLUS) return MSCAN_ERR_UNSUPPORTED;
+  return log_fwd_impl(prob, gate, z, log_b, log_h0, h, ws, ws_bytes, stream);
+}
+
+mscan_status scan_log_bwd_gated(const mscan_problem* prob, int gate, const float* z, const float* log_b,
+                                const float* h, const float* dy, const float* log_h0, float* dz, float* dlog_b,
+                                float* dlog_h0, void* ws, size_t ws_bytes, void* stream) {
+  if (gate != MSCAN_GATE_NEG_SOFTPLUS) return MSCAN_ERR_UNSUPPORTED;
+  return log_bwd_impl(prob, gate, z, log_b, h, dy, log_h0, dz, dlog_b, dlog_h0, ws, ws_bytes, stream);
 }
 
 mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

@@ -36,6 +36,10 @@ hipError_t launch_log(const ScalarArgs& a, hipStream_t st);
 // Log-space backward (g = log a, lb = log b, b = dy, hs = h, h0 = log h0;
 // out0 = dlog_b, out1 = dlog_a, dh0 = dlog_h0; fp32).
 hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st);
+// Gate-logit variants: linear scan with g = sigmoid(z); log-space scan with
+// log a = -softplus(z) (g holds z; the backward's out1 is dz).
+hipError_t launch_scalar_sigmoid(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
+hipError_t launch_log_softplus(const ScalarArgs& a, bool bwd, hipStream_t st);
 
 // Arguments of the matrix-affine kernels (see scan_matrix.hip). Strides and
 // offsets count time steps; a step holds a k x k block of A and k x v blocks

@@ -14,6 +14,13 @@
 // the chain rule: dlog_b = lam * b, dlog_a = lam * a * h_prev,
 // dlog_h0 = lam * a * h0 (template flag LOGB).
 //
+// Gate logits (template GATE): the gate is computed from a logit z as it is
+// loaded, so no separate pointwise pass writes and rereads it. The activations
+// are the ones the pages' workloads draw gates with: g = sigmoid(z) for the
+// linear scan (README benchmark inputs), log a = -softplus(z) for the log-space
+// scan (minGRU "One associative-scan family": a positive coefficient in (0,1)).
+// The backward recomputes the activation and returns dz = dg * f'(z).
+//
 // Both directions are the same affine scan run along a "processing order":
 //   forward : element (a, b) = (g_t, x_t), order = time (reversed if reverse),
 //             a sequence's first element becomes (0, g h0 + x);
@@ -137,14 +144,41 @@ __device__ __forceinline__ int slice_find(const SegSlice& s, int64_t q) {
 }
 
 enum : int { kRowLoop = 0, kLookback = 1 };
+enum : int { kGateNone = 0, kGateSigmoid = 1, kGateNegSoftplus = 2 };
+
+__device__ __forceinline__ float sigmoid_f(float z) { return __frcp_rn(1.f + __expf(-z)); }
+// log(1 + e^z) = max(z, 0) + log1p(u), u = e^{-|z|} in (0, 1], without overflow
+// and without losing its tail for z << 0. log1p(u): for u < 1/16 the series
+// u - u^2/2 + u^3/3 - u^4/4 + u^5/5 (truncation below u^6/6 < 1e-8 relative);
+// otherwise log(1 + u), whose rounding of 1 + u costs at most ~1e-6 relative
+// there. Both branches are a few VALU ops, where log1pf's range reduction
+// doubled the time of the (VALU-bound) log-space forward.
+__device__ __forceinline__ float softplus_f(float z) {
+  const float u = __expf(-fabsf(z));
+  const float series = u * __builtin_fmaf(-u, __builtin_fmaf(-u, __builtin_fmaf(-u, __builtin_fmaf(-u, 0.2f, 0.25f),
+                                                                               1.f / 3.f), 0.5f), 1.f);
+  const float lg = __logf(1.f + u);
+  return fmaxf(z, 0.f) + (u < 0.0625f ? series : lg);
+}
+
+// The gate value the scan uses, from a loaded gate operand: the operand itself,
+// the activation of a logit, and, for the log-space backward, a = e^{log a}.
+template <int GATE, bool LOGB>
+__device__ __forceinline__ float gate_value(float v) {
+  if constexpr (GATE == kGateSigmoid) return sigmoid_f(v);                 // g = sigmoid(z)
+  if constexpr (GATE == kGateNegSoftplus) return LOGB ? sigmoid_f(-v)      // a = e^{-softplus(z)}
+                                                      : -softplus_f(v);    // log a = -softplus(z)
+  return LOGB ? __expf(v) : v;
+}
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <class Ops, typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL,
-          bool LOGB = false>
+          bool LOGB = false, int GATE = kGateNone>
 __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   static_assert(!LOGB || (BWD && sizeof(Tin) == 4), "the log-space adjoint is an fp32 backward");
+  static_assert(GATE != kGateNegSoftplus || (sizeof(Tin) == 4 && (LOGB || !BWD)), "-softplus gates feed the log-space scan");
   using S = typename Ops::S;
   using C = typename Ops::C;
   constexpr int NS = Ops::NS, NC = Ops::NC, ND = NS + NC;
@@ -245,6 +279,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       for (int s = 0; s < SUBS; ++s) {
         const int64_t u0 = span_lo(s);
         load_span<Tin, EL>(gp + base + u0, Lg[s]);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) Lg[s][e] = gate_value<GATE, LOGB>(Lg[s][e]);
         if constexpr (!BWD) {
           load_span<Tin, EL>((const Tin*)a.b + base + u0, Lb[s]);
         } else {
@@ -261,7 +297,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         for (int e = 0; e < EL; ++e) {
           const int64_t t = u0 + e - lead;
           const bool ok = (t >= 0) && (t < T);
-          Lg[s][e] = ok ? InTraits<Tin>::load1(gp + rowoff + t) : Ops::kMaskA;
+          Lg[s][e] = ok ? gate_value<GATE, LOGB>(InTraits<Tin>::load1(gp + rowoff + t)) : Ops::kMaskA;
           if constexpr (!BWD) {
             Lb[s][e] = ok ? InTraits<Tin>::load1((const Tin*)a.b + rowoff + t) : Ops::kMaskB;
           } else {
@@ -273,14 +309,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       }
     }
     if constexpr (LOGB) {
-      // a = e^{log a} (0 for log a = -inf), b = e^{log b}
+      // b = e^{log b} (a = e^{log a} was taken on load, 0 for log a = -inf)
 #pragma unroll
       for (int s = 0; s < SUBS; ++s)
 #pragma unroll
-        for (int e = 0; e < EL; ++e) {
-          Lg[s][e] = __expf(Lg[s][e]);
-          Lx[s][e] = __expf(Lx[s][e]);
-        }
+        for (int e = 0; e < EL; ++e) Lx[s][e] = __expf(Lx[s][e]);
     }
     // processing order: element e of a lane is physical component P_(e)
     auto P_ = [](int e) { return REV ? EL - 1 - e : e; };
@@ -314,8 +347,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         } else if (l == 0) {
           const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
           const int64_t t = u_of(j) - lead;
-          gprev = (j >= 0 && t >= 0 && t < T) ? InTraits<Tin>::load1(gp + rowoff + t) : 0.f;
-          if constexpr (LOGB) gprev = (j >= 0 && t >= 0 && t < T) ? __expf(gprev) : 0.f;
+          gprev = (j >= 0 && t >= 0 && t < T) ? gate_value<GATE, LOGB>(InTraits<Tin>::load1(gp + rowoff + t)) : 0.f;
         }
         if (s + 1 < SUBS) {
           const float hn = readlane_f(N[s + 1][0], 0);
@@ -527,10 +559,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       for (int e = 0; e < EL; ++e) {
         if constexpr (!LOGB) {
           o0[P_(e)] = O[s][e];
-          if constexpr (BWD) o1[P_(e)] = O[s][e] * N[s][e];
+          if constexpr (BWD) {
+            if constexpr (GATE == kGateSigmoid)
+              o1[P_(e)] = (O[s][e] * N[s][e]) * (G[s][e] * (1.f - G[s][e]));  // dz = dg * g (1 - g)
+            else
+              o1[P_(e)] = O[s][e] * N[s][e];                                    // dg = lam * h_prev
+          }
         } else {
           o0[P_(e)] = O[s][e] * Lx[s][P_(e)];             // dlog_b = lam * b
-          o1[P_(e)] = (O[s][e] * N[s][e]) * G[s][e];      // dlog_a = lam * h_prev * a
+          if constexpr (GATE == kGateNegSoftplus)         // dz = dlog_a * (-sigmoid(z)), sigmoid(z) = 1 - a
+            o1[P_(e)] = -((O[s][e] * N[s][e]) * (G[s][e] * (1.f - G[s][e])));
+          else
+            o1[P_(e)] = (O[s][e] * N[s][e]) * G[s][e];    // dlog_a = lam * h_prev * a
         }
       }
       if (interior) {
@@ -568,7 +608,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 // host launch
 // ---------------------------------------------------------------------------
 
-template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL, bool LOGB = false>
+template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL, bool LOGB = false,
+          int GATE = kGateNone>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
   ScalarArgs a = a0;
@@ -578,16 +619,16 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   const dim3 block(WAVES * 64);
   if (!lookback) {
     const dim3 grid((unsigned)a.rows);
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
   } else {
     // fresh descriptors for this call (zero tag = not published)
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(Ops::NS + Ops::NC);
     const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
     if (z != hipSuccess) return z;
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -611,14 +652,28 @@ bool scalar_uses_lookback(int64_t rows, int64_t ntiles) {
   return ntiles > 1;
 }
 
-hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
+template <int GATE>
+static hipError_t launch_scalar_gate(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
   const bool rev = a.rev != 0;
   if (in_dtype == 0) {
-    if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, true, false, 4, 4, 1>(a, st);
-    return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, float, false, false, 4, 4, 1>(a, st);
+    if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, false, GATE>(a, st)
+                        : launch_cfg<LinOps, float, true, false, 4, 4, 1, false, GATE>(a, st);
+    return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1, false, GATE>(a, st)
+               : launch_cfg<LinOps, float, false, false, 4, 4, 1, false, GATE>(a, st);
   }
-  if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, uint16_t, true, false, 4, 4, 1>(a, st);
-  return rev ? launch_cfg<LinOps, uint16_t, false, true, 4, 4, 1>(a, st) : launch_cfg<LinOps, uint16_t, false, false, 4, 4, 1>(a, st);
+  if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 4, 1, false, GATE>(a, st)
+                      : launch_cfg<LinOps, uint16_t, true, false, 4, 4, 1, false, GATE>(a, st);
+  return rev ? launch_cfg<LinOps, uint16_t, false, true, 4, 4, 1, false, GATE>(a, st)
+             : launch_cfg<LinOps, uint16_t, false, false, 4, 4, 1, false, GATE>(a, st);
+}
+
+hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
+  return launch_scalar_gate<kGateNone>(a, in_dtype, bwd, st);
+}
+
+// Linear scan with gates g = sigmoid(z) (z fp32 or bf16).
+hipError_t launch_scalar_sigmoid(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
+  return launch_scalar_gate<kGateSigmoid>(a, in_dtype, bwd, st);
 }
 
 // Log-space forward: fp32 (log a, log b), same tiles as the fp32 scalar scan.
@@ -630,6 +685,14 @@ hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
 hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
   return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true>(a, st)
                : launch_cfg<LinOps, float, true, false, 4, 4, 1, true>(a, st);
+}
+
+// Log-space scan with log a = -softplus(z): forward and backward.
+hipError_t launch_log_softplus(const ScalarArgs& a, bool bwd, hipStream_t st) {
+  if (bwd) return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true, kGateNegSoftplus>(a, st)
+                        : launch_cfg<LinOps, float, true, false, 4, 4, 1, true, kGateNegSoftplus>(a, st);
+  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 4, 1, false, kGateNegSoftplus>(a, st)
+               : launch_cfg<LogOps, float, false, false, 4, 4, 1, false, kGateNegSoftplus>(a, st);
 }
 
 }  // namespace mscan

@@ -309,7 +309,29 @@ def other_workloads(m, gen, torch, dev, stream, np):
         "workload": "C=1536, 65536 packed tokens in 16 sequences, bf16 g and x, fp32 h, two branches (causal + reverse)",
         "fwd": _entry(2 * 8 * n, _time(torch, stream, vf, 10), 2 * n, "elements"),
         "fwd_bwd": _entry(2 * (8 + 18) * n, _time(torch, stream, vfb, 10), 2 * n, "elements")}
-    del br, dy
+    del br
+
+    # the same packed workload given gate logits z ~ N(2, 1) (bf16; resets z = -inf):
+    # g = sigmoid(z) is computed inside the scan kernels
+    bz = []
+    for _ in range(2):
+        z = torch.randn((C, Tt), device=dev, generator=gt) + 2.0
+        z[:, torch.rand(Tt, device=dev, generator=gt) < 1.0 / 1024] = float("-inf")
+        bz.append((z.to(torch.bfloat16), torch.randn((C, Tt), device=dev, generator=gt).to(torch.bfloat16)))
+
+    def zf():
+        return [m.scan_fwd_gated(b[0], b[1], cu_seqlens=cu, reverse=(i == 1)) for i, b in enumerate(bz)]
+
+    def zfb():
+        hs = zf()
+        for i, b in enumerate(bz):
+            m.scan_bwd_gated(b[0], hs[i], dy, cu_seqlens=cu, reverse=(i == 1), need_dh0=False)
+
+    out["varlen_bidir_bf16_logits"] = {
+        "workload": "the packed bidirectional workload with bf16 gate logits, g = sigmoid(z) fused into the scan",
+        "fwd": _entry(2 * 8 * n, _time(torch, stream, zf, 10), 2 * n, "elements"),
+        "fwd_bwd": _entry(2 * (8 + 18) * n, _time(torch, stream, zfb, 10), 2 * n, "elements")}
+    del bz, dy
     torch.cuda.empty_cache()
 
     # log space
@@ -329,7 +351,23 @@ def other_workloads(m, gen, torch, dev, stream, np):
                        "bwd": _entry(24 * n, _time(torch, stream, lambda: m.scan_log_bwd(la, lb, hl, dyl, need_dh0=False), 10),
                                      n, "elements"),
                        "fwd_bwd": _entry(36 * n, _time(torch, stream, lfb, 10), n, "elements")}
-    del la, lb, dyl, hl
+    del la, hl
+    # the same workload given the gate logits: log_a = -softplus(z) fused into the scan
+    zl = torch.randn((B, D, T), device=dev, generator=gt)
+    hz = m.scan_log_fwd_gated(zl, lb)
+
+    def zlfb():
+        h_ = m.scan_log_fwd_gated(zl, lb)
+        m.scan_log_bwd_gated(zl, lb, h_, dyl, need_dh0=False)
+
+    out["logspace_logits"] = {"workload": "B=8 D=1024 T=8192 fp32, logits z ~ N(0,1) with log_a = -softplus(z) fused",
+                              "fwd": _entry(12 * n, _time(torch, stream, lambda: m.scan_log_fwd_gated(zl, lb), 10), n,
+                                            "elements"),
+                              "bwd": _entry(24 * n, _time(torch, stream,
+                                                          lambda: m.scan_log_bwd_gated(zl, lb, hz, dyl, need_dh0=False),
+                                                          10), n, "elements"),
+                              "fwd_bwd": _entry(36 * n, _time(torch, stream, zlfb, 10), n, "elements")}
+    del zl, hz, lb, dyl
     torch.cuda.empty_cache()
 
     # matrix-affine: rotations (k=2, v=1) and scaled orthogonal blocks (k=4, v=4)

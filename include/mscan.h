@@ -86,6 +86,14 @@ typedef enum {
 
 typedef enum { MSCAN_F32 = 0, MSCAN_BF16 = 1 } mscan_dtype;
 
+/* Gate activation of the *_gated entry points, which take gate logits z and
+ * compute the gate as they load it (no separate pointwise pass). */
+typedef enum {
+  MSCAN_GATE_NONE = 0,         /* (plain entry points) the operand is the gate itself */
+  MSCAN_GATE_SIGMOID = 1,      /* linear scan: g = sigmoid(z)                          */
+  MSCAN_GATE_NEG_SOFTPLUS = 2  /* log-space scan: log a = -softplus(z), a in (0, 1)    */
+} mscan_gate;
+
 /* Which computation a workspace is sized for. */
 typedef enum {
   MSCAN_OP_SCAN_FWD = 0,
@@ -165,6 +173,33 @@ MSCAN_API mscan_status scan_log_fwd(const mscan_problem* prob, const float* log_
 MSCAN_API mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_a, const float* log_b,
                           const float* h, const float* dy, const float* log_h0, float* dlog_a,
                           float* dlog_b, float* dlog_h0, void* ws, size_t ws_bytes, void* stream);
+
+/* Scans that take gate logits z instead of gates. The activations are the ones
+ * the pages' workloads draw their gates with: g = sigmoid(z) for the linear
+ * scan (the associative-scan-triton README's benchmark gates), and
+ * log a = -softplus(z) for the log-space scan (minGRU "One associative-scan
+ * family": the base log-space member's coefficient is a positive scalar in
+ * (0, 1)). Each computes exactly what the plain entry point computes on f(z);
+ * the backward returns dz = dg * f'(z) in place of dg (resp. dlog_a):
+ *   sigmoid      : dz = dg * g (1 - g)
+ *   -softplus    : dz = dlog_a * (-sigmoid(z))
+ * Arguments, layouts, workspace and errors are those of scan_fwd / scan_bwd /
+ * scan_log_fwd / scan_log_bwd; z has the gate's type (fp32 or bf16 for the
+ * linear scan, fp32 for the log-space scan). A gate kind other than the one
+ * listed for the entry point returns MSCAN_ERR_UNSUPPORTED.                 */
+MSCAN_API mscan_status scan_fwd_gated(const mscan_problem* prob, int in_dtype, int gate /* MSCAN_GATE_SIGMOID */,
+                            const void* z, const void* x, const float* h0, float* h, void* ws,
+                            size_t ws_bytes, void* stream);
+MSCAN_API mscan_status scan_bwd_gated(const mscan_problem* prob, int in_dtype, int gate /* MSCAN_GATE_SIGMOID */,
+                            const void* z, const float* h, const float* dy, const float* h0, float* dx,
+                            float* dz, float* dh0, void* ws, size_t ws_bytes, void* stream);
+MSCAN_API mscan_status scan_log_fwd_gated(const mscan_problem* prob, int gate /* MSCAN_GATE_NEG_SOFTPLUS */,
+                                const float* z, const float* log_b, const float* log_h0, float* h, void* ws,
+                                size_t ws_bytes, void* stream);
+MSCAN_API mscan_status scan_log_bwd_gated(const mscan_problem* prob, int gate /* MSCAN_GATE_NEG_SOFTPLUS */,
+                                const float* z, const float* log_b, const float* h, const float* dy,
+                                const float* log_h0, float* dz, float* dlog_b, float* dlog_h0, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Matrix-affine forward ("Triton scan kernels", "One associative-scan family":
  * h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t k x v; matrix_scan is

@@ -118,3 +118,17 @@ def test_scan_log_bwd_validation(m):
     assert need == 128 + 4 * 5 * 24  # 3 words per 4096-element tile, 5 tiles per row
     assert m.lib.scan_log_bwd(ctypes.byref(long), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need - 8,
                               None) == 3
+
+
+def test_gated_entry_points_reject_other_gates(m):
+    p = _prob(m)
+    # args (scan_fwd_gated): prob, in_dtype, gate, z, x, h0, h, ws, ws_bytes, stream
+    assert m.lib.scan_fwd_gated(ctypes.byref(p), 0, 0, FAKE, FAKE, None, FAKE, None, 0, None) == 2
+    assert m.lib.scan_fwd_gated(ctypes.byref(p), 0, 2, FAKE, FAKE, None, FAKE, None, 0, None) == 2
+    assert m.lib.scan_bwd_gated(ctypes.byref(p), 0, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == 2
+    assert m.lib.scan_log_fwd_gated(ctypes.byref(p), 1, FAKE, FAKE, None, FAKE, None, 0, None) == 2
+    assert m.lib.scan_log_bwd_gated(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 0,
+                                    None) == 2
+    # the supported gate still validates its arguments on the host
+    assert m.lib.scan_fwd_gated(ctypes.byref(p), 0, 1, None, FAKE, None, FAKE, None, 0, None) == 1
+    assert m.lib.scan_log_fwd_gated(ctypes.byref(p), 2, FAKE, FAKE, None, FAKE + 4, None, 0, None) == 1

@@ -19,8 +19,8 @@ Scalar tensors are [..., T] (every leading axis is an independent row, time
 contiguous); matrix tensors are [..., T, k, k] and [..., T, k, v]. ``h0`` is
 [nseg, rows] ([nseg, rows, k, v] for matrices) or, with one sequence, the shape
 of the leading axes. ``cu_seqlens`` is an int32 device tensor in the flash-attn
-convention. Inputs are fp32, or bf16 for the scalar scan's g and x; outputs
-are fp32.
+convention. Inputs are fp32, or bf16 / fp16 for the scalar scan's g and x;
+outputs are fp32.
 """
 from __future__ import annotations
 
@@ -34,7 +34,7 @@ __all__ = [
     "lib", "library_path", "Problem", "MscanError",
     "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
     "scan_fwd_gated", "scan_bwd_gated", "scan_log_fwd_gated", "scan_log_bwd_gated",
-    "scan_causal", "scan_bidirectional_branched", "scan_log", "GATE_SIGMOID", "GATE_NEG_SOFTPLUS",
+    "scan_causal", "scan_bidirectional_branched", "scan_log", "matrix_scan", "GATE_SIGMOID", "GATE_NEG_SOFTPLUS",
     "workspace_bytes", "OP_SCAN_FWD", "OP_SCAN_BWD", "OP_SCAN_LOG_FWD", "OP_MATRIX_FWD", "OP_MATRIX_BWD",
     "OP_SCAN_LOG_BWD",
 ]
@@ -43,7 +43,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libmscan.so")
 
 OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD, OP_SCAN_LOG_BWD = range(6)
-_F32, _BF16 = 0, 1
+_F32, _BF16, _F16 = 0, 1, 2
 GATE_NONE, GATE_SIGMOID, GATE_NEG_SOFTPLUS = 0, 1, 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error"}
 
@@ -214,7 +214,9 @@ def _in_dtype(t, name):
         return _F32
     if t.dtype == torch.bfloat16:
         return _BF16
-    raise ValueError(f"{name}: only float32 and bfloat16 inputs are supported")
+    if t.dtype == torch.float16:
+        return _F16
+    raise ValueError(f"{name}: only float32, bfloat16 and float16 inputs are supported")
 
 
 # ---------------------------------------------------------------------------
@@ -440,57 +442,29 @@ def matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False, ne
 
 
 # ---------------------------------------------------------------------------
-# autograd wrappers in the README's calling convention
+# differentiable entry points: torch.library custom ops (see _torch_ops.py),
+# in the README's calling convention for the scalar scan
 # ---------------------------------------------------------------------------
-class _ScanFn(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, g, x, h0, cu_seqlens, reverse):
-        h = scan_fwd(g, x, h0=h0, cu_seqlens=cu_seqlens, reverse=reverse)
-        ctx.save_for_backward(g, h, h0, cu_seqlens)
-        ctx.reverse = reverse
-        ctx.x_dtype = x.dtype
-        return h
-
-    @staticmethod
-    def backward(ctx, dy):
-        g, h, h0, cu = ctx.saved_tensors
-        dx, dg, dh0 = scan_bwd(g, h, dy.contiguous().float(), h0=h0, cu_seqlens=cu, reverse=ctx.reverse,
-                               need_dh0=h0 is not None and ctx.needs_input_grad[2])
-        if dh0 is not None and h0 is not None:
-            dh0 = dh0.view(h0.shape)
-        return dg.to(g.dtype), dx.to(ctx.x_dtype), dh0, None, None
+from . import _torch_ops  # noqa: E402  (registers the mscan:: custom ops)
 
 
-class _LogScanFn(torch.autograd.Function):
-    @staticmethod
-    def forward(ctx, log_a, log_b, log_h0, cu_seqlens, reverse):
-        h = scan_log_fwd(log_a, log_b, log_h0=log_h0, cu_seqlens=cu_seqlens, reverse=reverse)
-        ctx.save_for_backward(log_a, log_b, h, log_h0, cu_seqlens)
-        ctx.reverse = reverse
-        return h
+def scan_causal(gates, tokens, cu_seqlens=None, h0=None):
+    """Differentiable causal scan h[t] = gates[t] h[t-1] + tokens[t] (fp32 output)."""
+    return torch.ops.mscan.scan(gates, tokens, h0, cu_seqlens, False)
 
-    @staticmethod
-    def backward(ctx, dy):
-        log_a, log_b, h, log_h0, cu = ctx.saved_tensors
-        dla, dlb, dlh0 = scan_log_bwd(log_a, log_b, h, dy.contiguous().float(), log_h0=log_h0, cu_seqlens=cu,
-                                      reverse=ctx.reverse, need_dh0=log_h0 is not None and ctx.needs_input_grad[2])
-        if dlh0 is not None and log_h0 is not None:
-            dlh0 = dlh0.view(log_h0.shape)
-        return dla, dlb, dlh0, None, None
+
+def scan_bidirectional_branched(gates_fwd, tokens_fwd, gates_bwd, tokens_bwd, cu_seqlens=None):
+    """Two independent branches: a causal scan and a reverse-in-time scan."""
+    return (torch.ops.mscan.scan(gates_fwd, tokens_fwd, None, cu_seqlens, False),
+            torch.ops.mscan.scan(gates_bwd, tokens_bwd, None, cu_seqlens, True))
 
 
 def scan_log(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
     """Differentiable log-space scan: h = exp of h_t = a_t h_{t-1} + b_t carried
     in log space, with the native adjoint kernel for the backward."""
-    return _LogScanFn.apply(log_a, log_b, log_h0, cu_seqlens, reverse)
+    return torch.ops.mscan.scan_log(log_a, log_b, log_h0, cu_seqlens, reverse)
 
 
-def scan_causal(gates, tokens, cu_seqlens=None, h0=None):
-    """Differentiable causal scan h[t] = gates[t] h[t-1] + tokens[t] (fp32 output)."""
-    return _ScanFn.apply(gates, tokens, h0, cu_seqlens, False)
-
-
-def scan_bidirectional_branched(gates_fwd, tokens_fwd, gates_bwd, tokens_bwd, cu_seqlens=None):
-    """Two independent branches: a causal scan and a reverse-in-time scan."""
-    return (_ScanFn.apply(gates_fwd, tokens_fwd, None, cu_seqlens, False),
-            _ScanFn.apply(gates_bwd, tokens_bwd, None, cu_seqlens, True))
+def matrix_scan(A, B, h0=None, cu_seqlens=None, reverse=False):
+    """Differentiable matrix-affine scan h_t = A_t h_{t-1} + B_t."""
+    return torch.ops.mscan.matrix_scan(A, B, h0, cu_seqlens, reverse)

@@ -44,7 +44,7 @@ int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
 // the log-space scan).
 size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
   int64_t nt = 0;
-  for (int dt = MSCAN_F32; dt <= (f32_only ? MSCAN_F32 : MSCAN_BF16); ++dt) {
+  for (int dt = MSCAN_F32; dt <= (f32_only ? MSCAN_F32 : MSCAN_F16); ++dt) {
     const int64_t n = scalar_tiles_for(p, dt);
     if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
   }
@@ -112,7 +112,7 @@ mscan_status scalar_fwd_impl(const mscan_problem* prob, int in_dtype, int gate, 
                              const float* h0, float* h, void* ws, size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
-  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
+  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16 && in_dtype != MSCAN_F16) return MSCAN_ERR_UNSUPPORTED;
   if (!g || !x || !h) return MSCAN_ERR_INVALID;
   if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
@@ -140,7 +140,7 @@ mscan_status scalar_bwd_impl(const mscan_problem* prob, int in_dtype, int gate, 
                              size_t ws_bytes, void* stream) {
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
-  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16) return MSCAN_ERR_UNSUPPORTED;
+  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16 && in_dtype != MSCAN_F16) return MSCAN_ERR_UNSUPPORTED;
   if (!g || !h || !dy || !dx || !dg) return MSCAN_ERR_INVALID;
   if (!aligned16(g) || !aligned16(h) || !aligned16(dy) || !aligned16(dx) || !aligned16(dg))
     return MSCAN_ERR_INVALID;

@@ -84,6 +84,19 @@ struct InTraits<uint16_t> {
   }
 };
 
+// fp16, widened exactly (every fp16 value is an fp32 value); the same 8-byte
+// layout as bf16.
+template <>
+struct InTraits<_Float16> {
+  static constexpr int VEC = 4;
+  __device__ static __forceinline__ void loadv(const _Float16* p, float* o) {
+    typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+    const v4h v = __builtin_nontemporal_load((const v4h*)p);  // streamed once
+    o[0] = (float)v.x; o[1] = (float)v.y; o[2] = (float)v.z; o[3] = (float)v.w;
+  }
+  __device__ static __forceinline__ float load1(const _Float16* p) { return (float)(*p); }
+};
+
 // N consecutive elements starting at a vector-aligned address
 template <typename T, int N>
 __device__ __forceinline__ void load_span(const T* p, float (&o)[N]) {
@@ -660,6 +673,12 @@ static hipError_t launch_scalar_gate(const ScalarArgs& a, int in_dtype, bool bwd
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, false, GATE>(a, st);
     return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1, false, GATE>(a, st)
                : launch_cfg<LinOps, float, false, false, 4, 4, 1, false, GATE>(a, st);
+  }
+  if (in_dtype == 2) {
+    if (bwd) return rev ? launch_cfg<LinOps, _Float16, true, true, 4, 4, 1, false, GATE>(a, st)
+                        : launch_cfg<LinOps, _Float16, true, false, 4, 4, 1, false, GATE>(a, st);
+    return rev ? launch_cfg<LinOps, _Float16, false, true, 4, 4, 1, false, GATE>(a, st)
+               : launch_cfg<LinOps, _Float16, false, false, 4, 4, 1, false, GATE>(a, st);
   }
   if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 4, 4, 1, false, GATE>(a, st)
                       : launch_cfg<LinOps, uint16_t, true, false, 4, 4, 1, false, GATE>(a, st);

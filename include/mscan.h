@@ -38,7 +38,8 @@
  *              its last element to its first, h_t = a_t h_{t+1} + b_t, with h0
  *              entering at the last element (the second, opposite-direction
  *              branch of the README's bidirectional scan).
- *  Precision.  Inputs are fp32 or bf16; bf16 is widened exactly. All
+ *  Precision.  Inputs are fp32, bf16 or fp16 (the scalar scan's g and x);
+ *              bf16 and fp16 are widened exactly. All
  *              accumulation and every output is fp32 ("Triton scan kernels",
  *              "Kernel design": accumulation is fp32 regardless of input
  *              dtype).
@@ -84,7 +85,7 @@ typedef enum {
   MSCAN_ERR_HIP = 4
 } mscan_status;
 
-typedef enum { MSCAN_F32 = 0, MSCAN_BF16 = 1 } mscan_dtype;
+typedef enum { MSCAN_F32 = 0, MSCAN_BF16 = 1, MSCAN_F16 = 2 } mscan_dtype;
 
 /* Gate activation of the *_gated entry points, which take gate logits z and
  * compute the gate as they load it (no separate pointwise pass). */
@@ -124,7 +125,7 @@ MSCAN_API mscan_status mscan_workspace_init(void* ws, size_t ws_bytes, void* str
 /* Scalar forward scan (associative-scan-triton README, intro and quick start:
  * h[t] = g[t] * h[t-1] + x[t]; "how it works": chunked scan with a running
  * prefix carried across chunks).
- *   g, x : [rows][T] of in_dtype (MSCAN_F32 or MSCAN_BF16), read only.
+ *   g, x : [rows][T] of in_dtype (MSCAN_F32, MSCAN_BF16 or MSCAN_F16), read only.
  *   h0   : fp32 [nseg][rows] or NULL.
  *   h    : fp32 [rows][T], written.                                          */
 MSCAN_API mscan_status scan_fwd(const mscan_problem* prob, int in_dtype, const void* g, const void* x,

@@ -201,6 +201,35 @@ def test_bf16_inputs(m, oracle_lib):
         run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev, bits=(gb, xb))
 
 
+@pytest.mark.parametrize("T,stride", [(15000, 15000), (4097, 4099)])
+def test_fp16_inputs(m, oracle_lib, T, stride):
+    """fp16 g and x (widened exactly), packed sequences with h0, both directions;
+    odd row strides start rows at every 2-byte offset of an 8-byte vector."""
+    r = np.random.default_rng(9 + T)
+    rows = 5
+    g16 = r.uniform(0, 1, (rows, stride)).astype(np.float16)
+    x16 = r.standard_normal((rows, stride)).astype(np.float16)
+    g, x = g16[:, :T].astype(np.float32), x16[:, :T].astype(np.float32)
+    dy = r.standard_normal((rows, T)).astype(np.float32)
+    cu = gen.segments_random(r, T, 4)
+    h0 = r.standard_normal((4, rows)).astype(np.float32)
+    gt = torch.from_numpy(g16).to(DEV)[:, :T]
+    xt = torch.from_numpy(x16).to(DEV)[:, :T]
+    cu_t = _t(cu, torch.int32)
+    for rev in (False, True):
+        out = torch.full((rows, stride), 7.0, device=DEV)
+        h = m.scan_fwd(gt, xt, h0=_t(h0), cu_seqlens=cu_t, reverse=rev, out=out[:, :T])
+        href = oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=rev)
+        close(h, href, TAU_FWD, "h")
+        assert torch.all(out[:, T:] == 7.0), "wrote outside the rows"
+        if stride == T:
+            dx, dg, dh0 = m.scan_bwd(gt, h, _t(dy), h0=_t(h0), cu_seqlens=cu_t, reverse=rev)
+            rx, rg, rh0 = oracle_lib.scan_bwd(g, href, dy, h0=h0, cu_seqlens=cu, reverse=rev)
+            close(dx, rx, TAU_BWD, "dx")
+            close(dg, rg, TAU_BWD, "dg")
+            close(dh0, rh0, TAU_BWD, "dh0")
+
+
 def test_workspace_reuse_across_calls(m, oracle_lib):
     """Consecutive multi-tile calls of different sizes share one workspace."""
     r = np.random.default_rng(9)

@@ -132,3 +132,25 @@ def test_gated_entry_points_reject_other_gates(m):
     # the supported gate still validates its arguments on the host
     assert m.lib.scan_fwd_gated(ctypes.byref(p), 0, 1, None, FAKE, None, FAKE, None, 0, None) == 1
     assert m.lib.scan_log_fwd_gated(ctypes.byref(p), 2, FAKE, FAKE, None, FAKE + 4, None, 0, None) == 1
+
+
+def test_torch_custom_ops_registered_with_fake_kernels(m):
+    """The mscan:: custom ops exist with their schemas, and their fake kernels give
+    output shapes on meta tensors (what torch.compile traces with), no GPU needed."""
+    import torch
+    assert str(torch.ops.mscan.scan.default._schema) == \
+        "mscan::scan(Tensor g, Tensor x, Tensor? h0, Tensor? cu_seqlens, bool reverse) -> Tensor"
+    for name in ("scan", "scan_backward", "scan_log", "scan_log_backward", "matrix_scan", "matrix_scan_backward"):
+        assert hasattr(torch.ops.mscan, name)
+    g = torch.empty(3, 5, 100, device="meta", dtype=torch.bfloat16)
+    h = torch.ops.mscan.scan(g, g, None, None, False)
+    assert h.shape == (3, 5, 100) and h.dtype == torch.float32 and h.device.type == "meta"
+    hf = torch.empty(3, 5, 100, device="meta")
+    cu = torch.empty(4, device="meta", dtype=torch.int32)
+    dx, dg, dh0 = torch.ops.mscan.scan_backward(g, hf, hf, None, cu, True, True)
+    assert dx.shape == dg.shape == (3, 5, 100) and dh0.shape == (3, 15)
+    A = torch.empty(2, 7, 4, 4, device="meta")
+    B = torch.empty(2, 7, 4, 1, device="meta")
+    assert torch.ops.mscan.matrix_scan(A, B, None, None, False).shape == (2, 7, 4, 1)
+    dA, dB, dh0 = torch.ops.mscan.matrix_scan_backward(A, B, B, None, None, False, True)
+    assert dA.shape == A.shape and dB.shape == B.shape and dh0.shape == (1, 2, 4, 1)

@@ -53,6 +53,128 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // ---------------------------------------------------------------------------
+// LDS staging of one array over a wave window
+// ---------------------------------------------------------------------------
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+
+// N floats per step, EL steps per lane, 64 lanes. The window's floats are cut
+// into 16-byte units; lane l owns units [l*LU, (l+1)*LU). Unit u is kept at
+// LDS unit swz(u) = u ^ ((u >> SH) & MSK): that flips only the low 4 bits (so
+// u stays in its aligned group of 16 units, and each group of 16 / 64 units
+// is still one contiguous block of memory) and spreads the lanes that read
+// unit c of their blocks over 16 different 16-byte bank groups. swz is its
+// own inverse.
+template <int N, int EL>
+struct Stage {
+  static constexpr int FLOATS = N * 64 * EL;  // floats per window
+  static constexpr int UNITS = FLOATS / 4;
+  static constexpr int LU = N * EL / 4;       // units per lane
+  static_assert((N * EL) % 4 == 0 && (LU & (LU - 1)) == 0, "lane blocks must be whole powers-of-two of units");
+  static constexpr int SH = LU >= 16 ? ilog2c(LU) : 4;
+  static constexpr int MSK = (LU >= 16 ? 16 : LU) - 1;
+  __device__ static __forceinline__ int swz(int u) { return u ^ ((u >> SH) & MSK); }
+  // LDS float index of window float f
+  __device__ static __forceinline__ int at(int f) { return swz(f >> 2) * 4 + (f & 3); }
+
+  // window floats [0, nvalid) come from g[0, nvalid); the rest are left as
+  // they are (callers mask those steps). vec: g is 16-byte aligned.
+  __device__ static __forceinline__ void load(const float* g, float* lds, int nvalid, bool vec) {
+    const int l = lane_id();
+    if (vec && nvalid == FLOATS) {
+#pragma unroll
+      for (int i = 0; i < UNITS / 64; ++i) {
+        const int u = swz(i * 64 + l);
+        __builtin_amdgcn_global_load_lds((const void*)(g + u * 4),
+                                         (__attribute__((address_space(3))) void*)(lds + i * 256), 16, 0, 0);
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < FLOATS / 64; ++i) {
+        const int p = i * 64 + l;
+        const int f = swz(p >> 2) * 4 + (p & 3);
+        if (f < nvalid)
+          __builtin_amdgcn_global_load_lds((const void*)(g + f),
+                                           (__attribute__((address_space(3))) void*)(lds + i * 64), 4, 0, 0);
+      }
+    }
+  }
+  // window floats [0, nvalid) go to g[0, nvalid)
+  __device__ static __forceinline__ void store(float* g, const float* lds, int nvalid, bool vec) {
+    const int l = lane_id();
+    if (vec && nvalid == FLOATS) {
+#pragma unroll
+      for (int i = 0; i < UNITS / 64; ++i) {
+        const int p = i * 64 + l;
+        const v4f t = *(const v4f*)(lds + p * 4);
+        __builtin_nontemporal_store(t, (v4f*)(g + swz(p) * 4));
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < FLOATS / 64; ++i) {
+        const int p = i * 64 + l;
+        const int f = swz(p >> 2) * 4 + (p & 3);
+        if (f < nvalid) g[f] = lds[p];
+      }
+    }
+  }
+  // the N floats of window step s
+  __device__ static __forceinline__ void get(const float* lds, int s, float* o) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j) {
+        const v4f t = *(const v4f*)(lds + swz(s * (N / 4) + j) * 4);
+        o[4 * j] = t.x; o[4 * j + 1] = t.y; o[4 * j + 2] = t.z; o[4 * j + 3] = t.w;
+      }
+    } else {
+      static_assert(N == 2, "steps of 2 floats or whole units");
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f t = *(const v2f*)(lds + swz(s >> 1) * 4 + (s & 1) * 2);
+      o[0] = t.x; o[1] = t.y;
+    }
+  }
+  // the LU units (4 LU floats) of lane block `blk`, in order
+  __device__ static __forceinline__ void read_block(const float* lds, int blk, float* o) {
+#pragma unroll
+    for (int j = 0; j < LU; ++j) {
+      const v4f t = *(const v4f*)(lds + swz(blk * LU + j) * 4);
+      o[4 * j] = t.x; o[4 * j + 1] = t.y; o[4 * j + 2] = t.z; o[4 * j + 3] = t.w;
+    }
+  }
+  __device__ static __forceinline__ void write_block(float* lds, int blk, const float* v) {
+#pragma unroll
+    for (int j = 0; j < LU; ++j) {
+      const v4f t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+      *(v4f*)(lds + swz(blk * LU + j) * 4) = t;
+    }
+  }
+  __device__ static __forceinline__ void put(float* lds, int s, const float* v) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < N / 4; ++j) {
+        const v4f t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        *(v4f*)(lds + swz(s * (N / 4) + j) * 4) = t;
+      }
+    } else {
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f t = {v[0], v[1]};
+      *(v2f*)(lds + swz(s >> 1) * 4 + (s & 1) * 2) = t;
+    }
+  }
+};
+
+// Completion of this wave's direct-to-LDS loads, then of its LDS writes, made
+// visible to all of its lanes (the staging areas are private to one wave).
+__device__ __forceinline__ void wait_stage_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
 // Linear affine monoid
 // ---------------------------------------------------------------------------
 // compose(e, l): e earlier, l later. A zero l.P keeps l (see the file comment).

@@ -188,7 +188,7 @@ __device__ __forceinline__ float gate_value(float v) {
 // the kernel
 // ---------------------------------------------------------------------------
 template <class Ops, typename Tin, bool BWD, bool REV, bool VARLEN, int MODE, int WAVES, int SUBS, int GPL,
-          bool LOGB = false, int GATE = kGateNone>
+          bool LOGB = false, int GATE = kGateNone, bool XP = false>
 __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   static_assert(!LOGB || (BWD && sizeof(Tin) == 4), "the log-space adjoint is an fp32 backward");
   static_assert(GATE != kGateNegSoftplus || (sizeof(Tin) == 4 && (LOGB || !BWD)), "-softplus gates feed the log-space scan");
@@ -200,6 +200,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   constexpr int WREG = SUBS * 64 * EL;   // elements per wave
   constexpr int TILE = WAVES * WREG;     // elements per tile
   static_assert(EL <= 16, "per-lane span too long");
+  // XP: lanes own 16 consecutive elements (one DPP scan per wave instead of
+  // one per 256-element sub-chunk); every array of the wave's 1024-element
+  // window moves between HBM and registers through an XOR-swizzled LDS stage
+  // (coalesced direct loads, coalesced stores), so HBM still sees fully
+  // coalesced 16-byte accesses.
+  static_assert(!XP || (SUBS == 1 && EL == 16 && sizeof(Tin) == 4), "staged windows are fp32, 16 per lane");
+  using SX = Stage<1, EL>;
+  constexpr int NXR = BWD ? (LOGB ? 4 : 3) : 2;  // staged arrays per wave
+  __shared__ __attribute__((aligned(16))) float s_x[XP ? WAVES : 1][XP ? NXR * SX::FLOATS : 4];
 
   __shared__ float s_agg[2][WAVES][NS];
   __shared__ float s_carry[NC];
@@ -287,7 +296,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 
     // ---- load: every vector of the tile is in flight before the first use
     float Lg[SUBS][EL], Lb[SUBS][EL], Lh[BWD ? SUBS : 1][EL], Lx[LOGB ? SUBS : 1][EL];
-    if (interior) {
+    // XP: padded coordinate of this wave's window and this lane's block in it
+    const int64_t wlo = REV ? urow - jt0 - (int64_t)(w + 1) * WREG : jt0 + (int64_t)w * WREG;
+    const int xblk = REV ? 63 - l : l;
+    float* xr = s_x[XP ? w : 0];
+    if (XP && interior) {
+      if constexpr (XP) {
+        SX::load((const float*)gp + base + wlo, xr, SX::FLOATS, true);
+        SX::load((const float*)a.b + base + wlo, xr + SX::FLOATS, SX::FLOATS, true);
+        if constexpr (BWD) SX::load(a.hs + base + wlo, xr + 2 * SX::FLOATS, SX::FLOATS, true);
+        if constexpr (LOGB) SX::load(a.lb + base + wlo, xr + 3 * SX::FLOATS, SX::FLOATS, true);
+        wait_stage_loads();
+        SX::read_block(xr, xblk, Lg[0]);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) Lg[0][e] = gate_value<GATE, LOGB>(Lg[0][e]);
+        SX::read_block(xr + SX::FLOATS, xblk, Lb[0]);
+        if constexpr (BWD) SX::read_block(xr + 2 * SX::FLOATS, xblk, Lh[0]);
+        if constexpr (LOGB) SX::read_block(xr + 3 * SX::FLOATS, xblk, Lx[0]);
+      }
+    } else if (interior) {
 #pragma unroll
       for (int s = 0; s < SUBS; ++s) {
         const int64_t u0 = span_lo(s);
@@ -586,7 +613,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             o1[P_(e)] = (O[s][e] * N[s][e]) * G[s][e];    // dlog_a = lam * h_prev * a
         }
       }
-      if (interior) {
+      if (XP && interior) {
+        if constexpr (XP) {
+          wave_lds_sync();
+          SX::write_block(xr, xblk, o0);
+          if constexpr (BWD) SX::write_block(xr + SX::FLOATS, xblk, o1);
+          wave_lds_sync();
+          SX::store(a.out0 + base + wlo, xr, SX::FLOATS, true);
+          if constexpr (BWD) SX::store(a.out1 + base + wlo, xr + SX::FLOATS, SX::FLOATS, true);
+        }
+      } else if (interior) {
         store_span<EL>(a.out0 + base + u0, o0);
         if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
       } else {
@@ -622,7 +658,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 // ---------------------------------------------------------------------------
 
 template <class Ops, typename Tin, bool BWD, bool REV, int WAVES, int SUBS, int GPL, bool LOGB = false,
-          int GATE = kGateNone>
+          int GATE = kGateNone, bool XP = false>
 static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   constexpr int TILE = WAVES * SUBS * 64 * InTraits<Tin>::VEC * GPL;
   ScalarArgs a = a0;
@@ -632,16 +668,16 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
   const dim3 block(WAVES * 64);
   if (!lookback) {
     const dim3 grid((unsigned)a.rows);
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kRowLoop, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
   } else {
     // fresh descriptors for this call (zero tag = not published)
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(Ops::NS + Ops::NC);
     const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
     if (z != hipSuccess) return z;
     const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
-    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB, GATE>), grid, block, 0, st, a);
+    if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -695,9 +731,15 @@ hipError_t launch_scalar_sigmoid(const ScalarArgs& a, int in_dtype, bool bwd, hi
   return launch_scalar_gate<kGateSigmoid>(a, in_dtype, bwd, st);
 }
 
-// Log-space forward: fp32 (log a, log b), same tiles as the fp32 scalar scan.
+// Log-space forward: fp32 (log a, log b), 4096-element tiles like the fp32
+// scalar scan, with lanes owning 16 consecutive elements through LDS-staged
+// windows: it carries the most VALU work per element (one exp per
+// composition), and one DPP scan per wave instead of four measured 3% faster
+// on dense rows and 13% on packed ones. (The memory-bound linear scans are
+// 6-11% slower that way and keep 4-element lanes.)
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
-  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 4, 1>(a, st) : launch_cfg<LogOps, float, false, false, 4, 4, 1>(a, st);
+  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNone, true>(a, st)
+               : launch_cfg<LogOps, float, false, false, 4, 1, 4, false, kGateNone, true>(a, st);
 }
 
 // Log-space backward: the fp32 adjoint scan with exponentiated gates.
@@ -710,8 +752,8 @@ hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
 hipError_t launch_log_softplus(const ScalarArgs& a, bool bwd, hipStream_t st) {
   if (bwd) return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true, kGateNegSoftplus>(a, st)
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, true, kGateNegSoftplus>(a, st);
-  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 4, 1, false, kGateNegSoftplus>(a, st)
-               : launch_cfg<LogOps, float, false, false, 4, 4, 1, false, kGateNegSoftplus>(a, st);
+  return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNegSoftplus, true>(a, st)
+               : launch_cfg<LogOps, float, false, false, 4, 1, 4, false, kGateNegSoftplus, true>(a, st);
 }
 
 }  // namespace mscan

@@ -354,17 +354,34 @@ __device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
   if (valid) Ops::compose(e, x);
 }
 
-// Row and tile of this workgroup in look-back mode. Blocks are numbered
-// tile-major (block = c * rows + r): every row's tile c is dispatched before
-// any row's tile c + 1, so by the time a tile looks back its predecessor has
-// usually published its inclusive value and one descriptor read settles the
-// carry. Tiles still wait only on lower-numbered blocks of their own row,
-// which were dispatched earlier, so the look-back always makes progress.
-__device__ __forceinline__ void tile_of_block(int64_t rows, int64_t& r, int& c) {
-  const uint32_t b = blockIdx.x, nr = (uint32_t)rows;
-  const uint32_t q = b / nr;
-  c = (int)q;
-  r = (int64_t)(b - q * nr);
+// Row and tile of this workgroup in look-back mode.
+//   row-major  (block = r * ntiles + c): the tiles of a row run side by side,
+//              so concurrent workgroups stream one contiguous stretch of
+//              memory. The dense linear scans use it: their descriptors are
+//              3 words and a look-back window costs little.
+//   tile-major (block = c * rows + r): every row's tile c is dispatched before
+//              any row's tile c + 1, so by the time a tile looks back its
+//              predecessor has usually published its inclusive value and one
+//              descriptor read settles the carry. The matrix kernels (up to
+//              48-word descriptors, where reading back through a window cost
+//              more than the data), the packed and the log-space scans use it.
+//              (On dense linear rows it made concurrent workgroups read the
+//              same offset of rows a power of two apart and cost ~10% at
+//              T >= 16384.)
+// Either way a tile waits only on lower-numbered blocks of its own row, which
+// were dispatched earlier, so the look-back always makes progress.
+template <bool TILE_MAJOR>
+__device__ __forceinline__ void tile_of_block(int64_t rows, int ntiles, int64_t& r, int& c) {
+  const uint32_t b = blockIdx.x;
+  if constexpr (TILE_MAJOR) {
+    const uint32_t q = b / (uint32_t)rows;
+    c = (int)q;
+    r = (int64_t)(b - q * (uint32_t)rows);
+  } else {
+    const uint32_t q = b / (uint32_t)ntiles;
+    r = (int64_t)q;
+    c = (int)(b - q * (uint32_t)ntiles);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -373,14 +390,15 @@ __device__ __forceinline__ void tile_of_block(int64_t rows, int64_t& r, int& c) 
 // returns the state entering tile `c` of the row whose first descriptor set
 // is `row_desc`.
 // ---------------------------------------------------------------------------
-template <class Ops>
+template <class Ops, bool FAST = false>
 __device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c) {
   using S = typename Ops::S;
   constexpr int ND = Ops::NS + Ops::NC;
   const int l = lane_id();
   const uint32_t tagA = kTagAgg, tagI = kTagIncl;
-  // fast path: the immediate predecessor has published its inclusive value
-  {
+  // fast path (FAST: tile-major dispatch, where it usually succeeds): the
+  // immediate predecessor has published its inclusive value
+  if constexpr (FAST) {
     bool ok = true;
     typename Ops::C cc;
 #pragma unroll

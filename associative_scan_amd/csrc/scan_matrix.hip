@@ -196,8 +196,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     r = blockIdx.x;
     c = 0;
   } else {
-    // tile-major numbering (see tile_of_block)
-    tile_of_block(a.rows, r, c);
+    tile_of_block<true>(a.rows, a.ntiles, r, c);
   }
   const int64_t T = a.T;
   const int64_t row0 = r * a.stride;  // first step of the row
@@ -435,7 +434,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
             }
           }
         }
-        if (c > 0) carry = lookback<Ops>(ws, rd, c);
+        if (c > 0) carry = lookback<Ops, true>(ws, rd, c);
         if (l == 0) {
           if (!hard) {
             const S tagg = (WAVES > 1) ? tile_agg() : wagg;

@@ -46,6 +46,8 @@
 //              row loop and measured faster at every benchmark row count.
 // Rows whose start is not 16-byte aligned are handled by aligning vector
 // groups to absolute addresses and masking the elements outside the row.
+#include <type_traits>
+
 #include "mscan_device.hpp"
 #include "mscan_launch.hpp"
 
@@ -207,6 +209,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   // coalesced 16-byte accesses.
   static_assert(!XP || (SUBS == 1 && EL == 16 && sizeof(Tin) == 4), "staged windows are fp32, 16 per lane");
   using SX = Stage<1, EL>;
+  // Look-back dispatch order (see tile_of_block), from timing each workload:
+  // dense linear rows stream memory best row-major (tile-major cost ~10% at
+  // T = 16384); packed sequences and the log-space kernels resolve their
+  // look-back faster tile-major (4-10%).
+  constexpr bool kTileMajor = VARLEN || LOGB || !std::is_same<Ops, LinOps>::value;
   constexpr int NXR = BWD ? (LOGB ? 4 : 3) : 2;  // staged arrays per wave
   __shared__ __attribute__((aligned(16))) float s_x[XP ? WAVES : 1][XP ? NXR * SX::FLOATS : 4];
 
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     c_last = a.ntiles - 1;
   } else {
     int c;
-    tile_of_block(a.rows, r, c);
+    tile_of_block<kTileMajor>(a.rows, a.ntiles, r, c);
     c_first = c_last = c;
   }
   const int64_t T = a.T;
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
         }
-        if (c > 0) carry = lookback<Ops>(ws, rd, c);
+        if (c > 0) carry = lookback<Ops, kTileMajor>(ws, rd, c);
         if (l == 0) {
           if (!hard) {
             const C inc = Ops::apply(tagg, carry);

@@ -61,6 +61,7 @@ mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
 // Workspace of a matrix op: header, then (look-back only) k*k + 2*k*v
 // descriptor words per tile.
 size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
+  if (k == 16) return mscan::matrix16_ws_bytes(p->rows, p->T);
   int64_t nt = 0;
   for (int b = 0; b < 2; ++b) {
     const int64_t n = mscan::matrix_tiles(p->T, k, v, b == 1);
@@ -71,7 +72,13 @@ size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
 }
 
 bool matrix_shape_ok(int k, int v) {
-  return (k == 1 && v == 1) || (k == 2 && (v == 1 || v == 2)) || (k == 4 && (v == 1 || v == 4));
+  return (k == 1 && v == 1) || (k == 2 && (v == 1 || v == 2)) || (k == 4 && (v == 1 || v == 4)) ||
+         (k == 16 && v == 16);
+}
+
+// Whether a matrix call chains its row through the workspace (k = 16 always does).
+bool matrix_needs_ws(const mscan_problem* p, int k, int64_t nt) {
+  return k == 16 || mscan::scalar_uses_lookback(p->rows, nt);
 }
 
 }  // namespace
@@ -306,7 +313,7 @@ mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, con
   if (!aligned16(A) || !aligned16(B) || !aligned16(h) || (h0 && !aligned16(h0))) return MSCAN_ERR_INVALID;
   const int64_t nt = mscan::matrix_tiles(prob->T, k, v, false);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+  if (matrix_needs_ws(prob, k, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
     return MSCAN_ERR_WORKSPACE;
   mscan::MatArgs a{};
   a.A = A;
@@ -335,7 +342,7 @@ mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, con
   if ((h0 && !aligned16(h0)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = mscan::matrix_tiles(prob->T, k, v, true);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+  if (matrix_needs_ws(prob, k, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
     return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dh0 && prob->cu_seqlens) {

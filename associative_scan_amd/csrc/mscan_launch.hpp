@@ -63,6 +63,11 @@ struct MatArgs {
 // Tiles per row of the matrix kernels for (k, v) (0 if unsupported).
 int64_t matrix_tiles(int64_t T, int k, int v, bool bwd);
 hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t st);
+// k = v = 16 on the matrix cores (scan_matrix16.hip): chunks per row, the
+// workspace a call needs (always), and the three-kernel launch.
+int64_t matrix16_chunks(int64_t T);
+size_t matrix16_ws_bytes(int64_t rows, int64_t T);
+hipError_t launch_matrix16(const MatArgs& a, bool bwd, hipStream_t st);
 
 // Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so
 // callers may capture it in a graph).

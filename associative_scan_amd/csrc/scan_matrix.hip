@@ -605,6 +605,7 @@ int64_t matrix_tiles(int64_t T, int k, int v, bool bwd) {
   else if (k == 2 && v == 2) tile = matrix_tile_steps<2, 2>(bwd);
   else if (k == 4 && v == 1) tile = matrix_tile_steps<4, 1>(bwd);
   else if (k == 4 && v == 4) tile = matrix_tile_steps<4, 4>(bwd);
+  else if (k == 16 && v == 16) return matrix16_chunks(T);
   else return 0;
   return (T + tile - 1) / tile;
 }
@@ -614,6 +615,7 @@ hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t s
   if (k == 2 && v == 2) return launch_kv<2, 2>(a, bwd, st);
   if (k == 4 && v == 1) return launch_kv<4, 1>(a, bwd, st);
   if (k == 4 && v == 4) return launch_kv<4, 4>(a, bwd, st);
+  if (k == 16 && v == 16) return launch_matrix16(a, bwd, st);
   return hipErrorInvalidValue;
 }
 

@@ -71,7 +71,7 @@ def test_matrix_lengths_lookback(m, oracle_lib, kv, T, reverse):
     run(m, oracle_lib, A, B, dy, h0=h0, reverse=reverse)
 
 
-@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("kv", KV + [(16, 16)])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_matrix_varlen(m, oracle_lib, kv, reverse):
     k, v = kv
@@ -93,6 +93,40 @@ def test_matrix_row_loop(m, oracle_lib, kv, reverse):
     cu = np.array([0, 700, 700, 2100], dtype=np.int32)
     h0 = r.standard_normal((3, 1024, k, v)).astype(np.float32)
     run(m, oracle_lib, A, B, dy, h0=h0, cu=cu, reverse=reverse)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 511, 1025, 5000])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix16_lengths(m, oracle_lib, T, reverse):
+    """k = v = 16 (matrix cores): chunk boundaries of 64 steps, ragged tails, h0."""
+    r = np.random.default_rng(700 + T + reverse)
+    A, B, dy = _random_case(r, 16, 16, 3, T)
+    h0 = r.standard_normal((1, 3, 16, 16)).astype(np.float32)
+    run(m, oracle_lib, A, B, dy, h0=h0, reverse=reverse)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix16_many_rows(m, oracle_lib, reverse):
+    """k = v = 16 with more rows than chunks per row, segments and empty segments."""
+    r = np.random.default_rng(800 + reverse)
+    A, B, dy = _random_case(r, 16, 16, 96, 700)
+    cu = np.array([0, 100, 100, 640, 641, 700], dtype=np.int32)
+    h0 = r.standard_normal((5, 96, 16, 16)).astype(np.float32)
+    run(m, oracle_lib, A, B, dy, h0=h0, cu=cu, reverse=reverse)
+
+
+def test_matrix16_no_h0_no_dh0(m, oracle_lib):
+    r = np.random.default_rng(900)
+    A, B, dy = _random_case(r, 16, 16, 2, 300)
+    Ad = _t(A)
+    h = m.matrix_affine_scan_fwd(Ad, _t(B))
+    href = oracle_lib.matrix_affine_scan_fwd(A, B)
+    close(h, href, TAU_FWD, "h")
+    dA, dB, dh0 = m.matrix_affine_scan_bwd(Ad, h, _t(dy), need_dh0=False)
+    assert dh0 is None
+    rA, rB, _ = oracle_lib.matrix_affine_scan_bwd(A, href, dy)
+    close(dB, rB, TAU_BWD, "dB")
+    close(dA, rA, TAU_BWD, "dA")
 
 
 def test_matrix_k1_is_scalar_scan(m):
@@ -176,15 +210,17 @@ def _signed_perm_case(r, k, v, rows, T, max_run=2048, p_zero=0.02):
     return A, B, dy
 
 
-@pytest.mark.parametrize("kv", KV)
+@pytest.mark.parametrize("kv", KV + [(16, 16)])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
     """Integer data: the GPU must equal the oracle bit for bit (segments, resets,
-    h0 injection, tile and look-back boundaries, reverse, adjoint)."""
+    h0 injection, tile and look-back boundaries, reverse, adjoint). At k = 16 an
+    entry of dA sums v = 16 products, so runs stop at 512 steps: every partial
+    sum stays below 16 * 512^2 = 2^22."""
     k, v = kv
     r = np.random.default_rng(300 + 10 * k + v + reverse)
     rows, T = 3, 9001
-    A, B, dy = _signed_perm_case(r, k, v, rows, T)
+    A, B, dy = _signed_perm_case(r, k, v, rows, T, max_run=512 if k == 16 else 2048)
     cu = gen.segments_random(r, T, 9)
     h0 = r.integers(-1, 2, size=(len(cu) - 1, rows, k, v)).astype(np.float32)
     cu_t, h0_t, Ad = _t(cu, torch.int32), _t(h0), _t(A)
@@ -198,7 +234,7 @@ def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
     assert np.array_equal(dh0.cpu().double().numpy(), rh0)
 
 
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16)])
 @pytest.mark.parametrize("T", [700, 5001])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_matrix_odd_row_stride(m, oracle_lib, kv, T, reverse):
@@ -234,7 +270,7 @@ def test_matrix_odd_row_stride(m, oracle_lib, kv, T, reverse):
     assert torch.all(dA[:, T:] == 7.0) and torch.all(dB[:, T:] == 7.0), "wrote past the row"
 
 
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16)])
 def test_matrix_nan_poison_stays_in_its_sequence(m, oracle_lib, kv):
     """A sequence full of NaN/Inf changes nothing in any other sequence (bitwise)."""
     k, v = kv

@@ -154,3 +154,19 @@ def test_torch_custom_ops_registered_with_fake_kernels(m):
     assert torch.ops.mscan.matrix_scan(A, B, None, None, False).shape == (2, 7, 4, 1)
     dA, dB, dh0 = torch.ops.mscan.matrix_scan_backward(A, B, B, None, None, False, True)
     assert dA.shape == A.shape and dB.shape == B.shape and dh0.shape == (1, 2, 4, 1)
+
+
+def test_matrix16_workspace_always_required(m):
+    # k = v = 16 chains 64-step chunks through the workspace on every call:
+    # header (128) + per chunk P, Q and carry-in (3 x 1 KiB) + a 4-byte flag
+    p = _prob(m, rows=5, T=100)
+    need = m.workspace_bytes(p, m.OP_MATRIX_FWD, 16, 16)
+    assert need == 128 + 5 * 2 * (3 * 1024 + 4)
+    assert m.workspace_bytes(p, m.OP_MATRIX_BWD, 16, 16) == need
+    # args (fwd): prob, k, v, A, B, h0, h, ws, ws_bytes, stream
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 16, FAKE, FAKE, None, FAKE, None, 0, None) == 3
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 16, FAKE, FAKE, None, FAKE, FAKE, need - 4, None) == 3
+    # (8, 8) and (16, 4) lie outside the supported shapes
+    assert m.workspace_bytes(p, m.OP_MATRIX_FWD, 8, 8) == 0
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 8, 8, FAKE, FAKE, None, FAKE, FAKE, need, None) == 2
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 4, FAKE, FAKE, None, FAKE, FAKE, need, None) == 2

@@ -61,7 +61,7 @@ mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
 // Workspace of a matrix op: header, then (look-back only) k*k + 2*k*v
 // descriptor words per tile.
 size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
-  if (k == 16) return mscan::matrix16_ws_bytes(p->rows, p->T);
+  if (mscan::matrix_core_shape(k, v)) return mscan::matrix16_ws_bytes(p->rows, p->T);
   int64_t nt = 0;
   for (int b = 0; b < 2; ++b) {
     const int64_t n = mscan::matrix_tiles(p->T, k, v, b == 1);
@@ -71,14 +71,16 @@ size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
   return mscan::ws_desc_offset() + (size_t)p->rows * (size_t)nt * (size_t)(k * k + 2 * k * v) * sizeof(uint64_t);
 }
 
+// The envelope k, v in {1, 2, 4, 8, 16}: (1, 1) is the scalar scan, four small
+// shapes have VALU kernels, the rest run on the matrix cores.
 bool matrix_shape_ok(int k, int v) {
-  return (k == 1 && v == 1) || (k == 2 && (v == 1 || v == 2)) || (k == 4 && (v == 1 || v == 4)) ||
-         (k == 16 && v == 16);
+  return (k == 1 && v == 1) || mscan::matrix_valu_shape(k, v) || mscan::matrix_core_shape(k, v);
 }
 
-// Whether a matrix call chains its row through the workspace (k = 16 always does).
-bool matrix_needs_ws(const mscan_problem* p, int k, int64_t nt) {
-  return k == 16 || mscan::scalar_uses_lookback(p->rows, nt);
+// Whether a matrix call chains its row through the workspace (the matrix-core
+// path always does).
+bool matrix_needs_ws(const mscan_problem* p, int k, int v, int64_t nt) {
+  return mscan::matrix_core_shape(k, v) || mscan::scalar_uses_lookback(p->rows, nt);
 }
 
 }  // namespace
@@ -98,7 +100,7 @@ size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
     case MSCAN_OP_MATRIX_FWD:
     case MSCAN_OP_MATRIX_BWD:
       if (!matrix_shape_ok(k, v)) return 0;
-      if (k == 1) return scalar_ws_bytes(prob, 3, true);
+      if (k == 1 && v == 1) return scalar_ws_bytes(prob, 3, true);
       return matrix_ws_bytes(prob, k, v);
     default:
       return 0;
@@ -308,12 +310,12 @@ mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, con
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
   if (!matrix_shape_ok(k, v)) return MSCAN_ERR_UNSUPPORTED;
-  if (k == 1) return scan_fwd(prob, MSCAN_F32, A, B, h0, h, ws, ws_bytes, stream);  // the scalar scan
+  if (k == 1 && v == 1) return scan_fwd(prob, MSCAN_F32, A, B, h0, h, ws, ws_bytes, stream);  // the scalar scan
   if (!A || !B || !h) return MSCAN_ERR_INVALID;
   if (!aligned16(A) || !aligned16(B) || !aligned16(h) || (h0 && !aligned16(h0))) return MSCAN_ERR_INVALID;
   const int64_t nt = mscan::matrix_tiles(prob->T, k, v, false);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (matrix_needs_ws(prob, k, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+  if (matrix_needs_ws(prob, k, v, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
     return MSCAN_ERR_WORKSPACE;
   mscan::MatArgs a{};
   a.A = A;
@@ -336,13 +338,13 @@ mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, con
   mscan_status s = check_problem(prob);
   if (s != MSCAN_OK) return s;
   if (!matrix_shape_ok(k, v)) return MSCAN_ERR_UNSUPPORTED;
-  if (k == 1) return scan_bwd(prob, MSCAN_F32, A, h, dy, h0, dB, dA, dh0, ws, ws_bytes, stream);
+  if (k == 1 && v == 1) return scan_bwd(prob, MSCAN_F32, A, h, dy, h0, dB, dA, dh0, ws, ws_bytes, stream);
   if (!A || !h || !dy || !dA || !dB) return MSCAN_ERR_INVALID;
   if (!aligned16(A) || !aligned16(h) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB)) return MSCAN_ERR_INVALID;
   if ((h0 && !aligned16(h0)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = mscan::matrix_tiles(prob->T, k, v, true);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (matrix_needs_ws(prob, k, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
+  if (matrix_needs_ws(prob, k, v, nt) && (!ws || !aligned16(ws) || ws_bytes < matrix_ws_bytes(prob, k, v)))
     return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dh0 && prob->cu_seqlens) {

@@ -599,13 +599,21 @@ static hipError_t launch_kv(const MatArgs& a, bool bwd, hipStream_t st) {
   return a.rev ? launch_mat<K, V, false, true>(a, st) : launch_mat<K, V, false, false>(a, st);
 }
 
+static bool envelope_size(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+bool matrix_valu_shape(int k, int v) { return (k == 2 && (v == 1 || v == 2)) || (k == 4 && (v == 1 || v == 4)); }
+
+bool matrix_core_shape(int k, int v) {
+  return envelope_size(k) && envelope_size(v) && !(k == 1 && v == 1) && !matrix_valu_shape(k, v);
+}
+
 int64_t matrix_tiles(int64_t T, int k, int v, bool bwd) {
   int64_t tile = 0;
   if (k == 2 && v == 1) tile = matrix_tile_steps<2, 1>(bwd);
   else if (k == 2 && v == 2) tile = matrix_tile_steps<2, 2>(bwd);
   else if (k == 4 && v == 1) tile = matrix_tile_steps<4, 1>(bwd);
   else if (k == 4 && v == 4) tile = matrix_tile_steps<4, 4>(bwd);
-  else if (k == 16 && v == 16) return matrix16_chunks(T);
+  else if (matrix_core_shape(k, v)) return matrix16_chunks(T);
   else return 0;
   return (T + tile - 1) / tile;
 }
@@ -615,7 +623,12 @@ hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t s
   if (k == 2 && v == 2) return launch_kv<2, 2>(a, bwd, st);
   if (k == 4 && v == 1) return launch_kv<4, 1>(a, bwd, st);
   if (k == 4 && v == 4) return launch_kv<4, 4>(a, bwd, st);
-  if (k == 16 && v == 16) return launch_matrix16(a, bwd, st);
+  if (matrix_core_shape(k, v)) {
+    MatArgs b = a;
+    b.k = k;
+    b.v = v;
+    return launch_matrix16(b, bwd, st);
+  }
   return hipErrorInvalidValue;
 }
 

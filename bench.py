@@ -370,9 +370,10 @@ def other_workloads(m, gen, torch, dev, stream, np):
     del zl, hz, lb, dyl
     torch.cuda.empty_cache()
 
-    # matrix-affine: rotations (k=2, v=1) and scaled orthogonal blocks (k=4, v=4)
-    R, T = 8 * 512, 8192
-    for name, k, v in (("matrix_rot2", 2, 1), ("matrix_orth4", 4, 4)):
+    # matrix-affine: rotations (k=2, v=1) and scaled orthogonal blocks (k=4, v=4
+    # over 8 x 512 blocks, T=8192; k=16, v=16 over 8 x 64 blocks, T=4096)
+    for name, k, v in (("matrix_rot2", 2, 1), ("matrix_orth4", 4, 4), ("matrix_orth16", 16, 16)):
+        R, T = (8 * 64, 4096) if k == 16 else (8 * 512, 8192)
         if k == 2:
             rr = 0.5 + 0.5 * torch.rand((R, T), device=dev, generator=gt)
             th = (torch.rand((R, T), device=dev, generator=gt) * 2 - 1) * np.pi
@@ -380,8 +381,8 @@ def other_workloads(m, gen, torch, dev, stream, np):
                              torch.stack([rr * th.sin(), rr * th.cos()], -1)], -2)
             del rr, th
         else:
-            A = torch.randn((R, T, 4, 4), device=dev, generator=gt)
-            for j in range(4):  # Gram-Schmidt on the columns
+            A = torch.randn((R, T, k, k), device=dev, generator=gt)
+            for j in range(k):  # Gram-Schmidt on the columns
                 for i in range(j):
                     A[..., :, j] -= (A[..., :, i] * A[..., :, j]).sum(-1, keepdim=True) * A[..., :, i]
                 A[..., :, j] /= A[..., :, j].norm(dim=-1, keepdim=True)
@@ -394,7 +395,7 @@ def other_workloads(m, gen, torch, dev, stream, np):
         steps = R * T
         tf = _time(torch, stream, lambda: m.matrix_affine_scan_fwd(A, Bm), 5)
         tb = _time(torch, stream, lambda: m.matrix_affine_scan_bwd(A, h, dyk, need_dh0=False), 5)
-        out[name] = {"workload": f"B=8 x 512 state blocks, T=8192, k={k} v={v}, fp32, resets 1/2048",
+        out[name] = {"workload": f"B=8 x {R // 8} state blocks, T={T}, k={k} v={v}, fp32, resets 1/2048",
                      "fwd": _entry(fb * steps, tf, steps, "steps"), "bwd": _entry(bb * steps, tb, steps, "steps")}
         del A, Bm, dyk, h
         torch.cuda.empty_cache()

@@ -281,6 +281,31 @@ def matrix_orth4(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 /
             "reset": reset, "k": 4, "v": 4}
 
 
+def matrix_orth16(B: int = 8, N: int = 64, T: int = 4096, p_reset: float = 1.0 / 2048, cfg_id: int = 53,
+                  rows=None):
+    """k=16, v=16, fp32: A_t = 0.9 * Q_t with Q_t the Q factor (positive diag R)
+    of an N(0,1) 16x16 matrix; B ~ N(0,1) [16,16]; resets A = 0 with
+    probability p_reset i.i.d. per (lane, t); dy ~ N(0,1) [16,16]. With ``rows``
+    only those rows of the B*N are drawn.
+
+    Tensors (spawn order): A (from G), B, reset mask, dy.
+    """
+    R = B * N
+    sa, sb, sm, sdy = _tensors(cfg_id, T, 4, B, N)
+
+    def orth(rng, shp):
+        G = _n01(rng, shp).astype(np.float64)
+        Q, Rf = np.linalg.qr(G)  # Householder; flip columns so that diag(R) > 0
+        Q *= np.sign(np.diagonal(Rf, axis1=-2, axis2=-1))[..., None, :]
+        return (0.9 * Q).astype(np.float32)
+
+    A = _draw(sa, (R, T, 16, 16), orth, rows=rows)
+    reset = _draw(sm, (R, T), lambda r, s: r.random(s) < p_reset, dtype=bool, rows=rows)
+    A[reset] = 0.0
+    return {"A": A, "B": _draw(sb, (R, T, 16, 16), _n01, rows=rows),
+            "dy": _draw(sdy, (R, T, 16, 16), _n01, rows=rows), "reset": reset, "k": 16, "v": 16}
+
+
 # ----------------------------------------------------------------------------
 # small structured inputs for edge cases
 # ----------------------------------------------------------------------------

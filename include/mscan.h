@@ -204,11 +204,13 @@ MSCAN_API mscan_status scan_log_bwd_gated(const mscan_problem* prob, int gate /*
 
 /* Matrix-affine forward ("Triton scan kernels", "One associative-scan family":
  * h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t k x v; matrix_scan is
- * k=2, v=1 and matrix_affine_scan is generic (k, v)). Supported: (k, v) in
- * {(1,1), (2,1), (2,2), (4,1), (4,4), (16,16)}; others return
- * MSCAN_ERR_UNSUPPORTED. (16,16) runs its 16 x 16 x 16 products on the matrix
- * cores in IEEE fp32 (the page's precision guard at k = 16) and always needs
- * the workspace (mscan_workspace_bytes).
+ * k=2, v=1 and matrix_affine_scan is generic (k, v)). Supported: the page's
+ * kernel envelope, k and v each in {1, 2, 4, 8, 16}, any T >= 1; any other
+ * (k, v) returns MSCAN_ERR_UNSUPPORTED. (1, 1) is the scalar scan; (2,1),
+ * (2,2), (4,1) and (4,4) run on the vector ALUs; every other pair runs its
+ * products on the matrix cores, zero-padded to 16 x 16, in IEEE fp32 (the
+ * page's precision guard at k = 16), and always needs the workspace
+ * (mscan_workspace_bytes).
  *   A : fp32 [rows][T][k][k]; B : fp32 [rows][T][k][v];
  *   h0 : fp32 [nseg][rows][k][v] or NULL; h : fp32 [rows][T][k][v], written. */
 MSCAN_API mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

@@ -129,6 +129,22 @@ def test_matrix16_no_h0_no_dh0(m, oracle_lib):
     close(dA, rA, TAU_BWD, "dA")
 
 
+ENVELOPE = [(k, v) for k in (1, 2, 4, 8, 16) for v in (1, 2, 4, 8, 16)]
+
+
+@pytest.mark.parametrize("kv", ENVELOPE)
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_envelope(m, oracle_lib, kv, reverse):
+    """Every (k, v) of the envelope {1, 2, 4, 8, 16}^2: several 64-step chunks,
+    a ragged tail, segments (one empty) with h0."""
+    k, v = kv
+    r = np.random.default_rng(1000 + 40 * k + v + reverse)
+    A, B, dy = _random_case(r, k, v, 2, 333)
+    cu = np.array([0, 64, 64, 200, 333], dtype=np.int32)
+    h0 = r.standard_normal((4, 2, k, v)).astype(np.float32)
+    run(m, oracle_lib, A, B, dy, h0=h0, cu=cu, reverse=reverse)
+
+
 def test_matrix_k1_is_scalar_scan(m):
     r = np.random.default_rng(7)
     g = r.uniform(0, 1, (4, 3000)).astype(np.float32)
@@ -189,6 +205,26 @@ def test_orthogonal_4x4_full_sampled(m, oracle_lib):
     assert torch.isfinite(h).all() and torch.isfinite(dA).all()
 
 
+@pytest.mark.timeout(400)
+def test_orthogonal_16x16_full_sampled(m, oracle_lib):
+    """k = v = 16 at the benchmarked size (B=8 x 64 blocks, T=4096): A = 0.9 Q,
+    resets 1/2048; the oracle checks whole rows drawn from every 64-row block
+    boundary region."""
+    d = gen.matrix_orth16()
+    A, B, dy = d["A"], d["B"], d["dy"]
+    Ad = _t(A)
+    h = m.matrix_affine_scan_fwd(Ad, _t(B))
+    dA, dB, _ = m.matrix_affine_scan_bwd(Ad, h, _t(dy), need_dh0=False)
+    rows = np.array([0, 1, 63, 64, 300, 511])
+    idx = torch.as_tensor(rows, device=DEV)
+    href = oracle_lib.matrix_affine_scan_fwd(A[rows], B[rows])
+    close(h[idx], href, TAU_FWD, "h")
+    rA, rB, _ = oracle_lib.matrix_affine_scan_bwd(A[rows], href, dy[rows])
+    close(dB[idx], rB, TAU_BWD, "dB")
+    close(dA[idx], rA, TAU_BWD, "dA")
+    assert torch.isfinite(h).all() and torch.isfinite(dA).all()
+
+
 # ---------------------------------------------------------------------------
 # exact mode, strided rows, non-finite containment
 # ---------------------------------------------------------------------------
@@ -210,17 +246,17 @@ def _signed_perm_case(r, k, v, rows, T, max_run=2048, p_zero=0.02):
     return A, B, dy
 
 
-@pytest.mark.parametrize("kv", KV + [(16, 16)])
+@pytest.mark.parametrize("kv", KV + [(16, 16), (8, 8), (16, 1), (1, 16), (2, 16), (8, 2)])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
     """Integer data: the GPU must equal the oracle bit for bit (segments, resets,
-    h0 injection, tile and look-back boundaries, reverse, adjoint). At k = 16 an
-    entry of dA sums v = 16 products, so runs stop at 512 steps: every partial
-    sum stays below 16 * 512^2 = 2^22."""
+    h0 injection, tile and look-back boundaries, reverse, adjoint). An entry of
+    dA sums v products, so with v > 4 runs stop at 512 steps: every partial sum
+    stays below 16 * 512^2 = 2^22."""
     k, v = kv
     r = np.random.default_rng(300 + 10 * k + v + reverse)
     rows, T = 3, 9001
-    A, B, dy = _signed_perm_case(r, k, v, rows, T, max_run=512 if k == 16 else 2048)
+    A, B, dy = _signed_perm_case(r, k, v, rows, T, max_run=512 if max(k, v) > 4 else 2048)
     cu = gen.segments_random(r, T, 9)
     h0 = r.integers(-1, 2, size=(len(cu) - 1, rows, k, v)).astype(np.float32)
     cu_t, h0_t, Ad = _t(cu, torch.int32), _t(h0), _t(A)
@@ -234,7 +270,7 @@ def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
     assert np.array_equal(dh0.cpu().double().numpy(), rh0)
 
 
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16), (8, 2), (1, 4)])
 @pytest.mark.parametrize("T", [700, 5001])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_matrix_odd_row_stride(m, oracle_lib, kv, T, reverse):
@@ -270,7 +306,7 @@ def test_matrix_odd_row_stride(m, oracle_lib, kv, T, reverse):
     assert torch.all(dA[:, T:] == 7.0) and torch.all(dB[:, T:] == 7.0), "wrote past the row"
 
 
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16), (8, 4)])
 def test_matrix_nan_poison_stays_in_its_sequence(m, oracle_lib, kv):
     """A sequence full of NaN/Inf changes nothing in any other sequence (bitwise)."""
     k, v = kv

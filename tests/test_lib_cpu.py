@@ -156,17 +156,26 @@ def test_torch_custom_ops_registered_with_fake_kernels(m):
     assert dA.shape == A.shape and dB.shape == B.shape and dh0.shape == (1, 2, 4, 1)
 
 
-def test_matrix16_workspace_always_required(m):
-    # k = v = 16 chains 64-step chunks through the workspace on every call:
-    # header (128) + per chunk P, Q and carry-in (3 x 1 KiB) + a 4-byte flag
+def test_matrix_core_workspace_always_required(m):
+    # the matrix-core shapes chain 64-step chunks through the workspace on every
+    # call: header (128) + per chunk P, Q and carry-in as padded 16 x 16 blocks
+    # (3 x 1 KiB) + a 4-byte flag
     p = _prob(m, rows=5, T=100)
-    need = m.workspace_bytes(p, m.OP_MATRIX_FWD, 16, 16)
-    assert need == 128 + 5 * 2 * (3 * 1024 + 4)
-    assert m.workspace_bytes(p, m.OP_MATRIX_BWD, 16, 16) == need
+    need = 128 + 5 * 2 * (3 * 1024 + 4)
+    for k, v in ((16, 16), (8, 8), (1, 16), (16, 1), (2, 4), (4, 8)):
+        assert m.workspace_bytes(p, m.OP_MATRIX_FWD, k, v) == need
+        assert m.workspace_bytes(p, m.OP_MATRIX_BWD, k, v) == need
     # args (fwd): prob, k, v, A, B, h0, h, ws, ws_bytes, stream
     assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 16, FAKE, FAKE, None, FAKE, None, 0, None) == 3
-    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 16, FAKE, FAKE, None, FAKE, FAKE, need - 4, None) == 3
-    # (8, 8) and (16, 4) lie outside the supported shapes
-    assert m.workspace_bytes(p, m.OP_MATRIX_FWD, 8, 8) == 0
-    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 8, 8, FAKE, FAKE, None, FAKE, FAKE, need, None) == 2
-    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 4, FAKE, FAKE, None, FAKE, FAKE, need, None) == 2
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 8, 2, FAKE, FAKE, None, FAKE, FAKE, need - 4, None) == 3
+
+
+@pytest.mark.parametrize("kv", [(3, 3), (16, 32), (32, 32), (8, 6), (1, 32), (0, 1), (4, 0), (-2, 2)])
+def test_matrix_outside_envelope_unsupported(m, kv):
+    """k, v outside {1, 2, 4, 8, 16} is refused on the host, never masked."""
+    k, v = kv
+    p = _prob(m, rows=5, T=100)
+    assert m.workspace_bytes(p, m.OP_MATRIX_FWD, k, v) == 0
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), k, v, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, None) == 2
+    assert m.lib.matrix_affine_scan_bwd(ctypes.byref(p), k, v, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                                        1 << 20, None) == 2

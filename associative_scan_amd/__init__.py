@@ -468,3 +468,18 @@ def scan_log(log_a, log_b, log_h0=None, cu_seqlens=None, reverse=False):
 def matrix_scan(A, B, h0=None, cu_seqlens=None, reverse=False):
     """Differentiable matrix-affine scan h_t = A_t h_{t-1} + B_t."""
     return torch.ops.mscan.matrix_scan(A, B, h0, cu_seqlens, reverse)
+
+
+def matrix_cumprod(A, cu_seqlens=None, reverse=False):
+    """Running products Abar_t = A_t Abar_{t-1} with Abar = I before each
+    sequence's first step (reverse: Abar_t = A_t Abar_{t+1}), the cumulative-
+    product output of the generic affine scan. It is the matrix-affine scan
+    with v = k, B = 0 and h0 = I, and runs as that scan (differentiable in A)."""
+    k = int(A.shape[-1])
+    if A.dim() < 3 or A.shape[-2] != k:
+        raise ValueError("A must be [..., T, k, k]")
+    rows = A.numel() // (A.shape[-3] * k * k) if A.shape[-3] > 0 else 0
+    nseg = 1 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    eye = torch.eye(k, dtype=torch.float32, device=A.device)
+    h0 = eye.expand(nseg, rows, k, k).contiguous()
+    return torch.ops.mscan.matrix_scan(A, torch.zeros_like(A), h0, cu_seqlens, reverse)

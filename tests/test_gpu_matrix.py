@@ -329,3 +329,49 @@ def test_matrix_nan_poison_stays_in_its_sequence(m, oracle_lib, kv):
             assert torch.equal(a[:, keep], b[:, keep])
         assert torch.equal(d1[2][[0, 2, 3]], d2[2][[0, 2, 3]])
         close(h[:, keep], oracle_lib.matrix_affine_scan_fwd(A, B, cu_seqlens=cu, reverse=rev)[:, keep], TAU_FWD, "h")
+
+
+@pytest.mark.parametrize("k", [2, 4, 16])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_cumprod(m, k, reverse):
+    """Running products against explicit fp64 matrix products per sequence,
+    and the gradient through the autograd op against finite differences of a
+    scalar loss."""
+    r = np.random.default_rng(1100 + k + reverse)
+    T = 150
+    A = (r.standard_normal((2, T, k, k)) * (1.0 / np.sqrt(k))).astype(np.float32)
+    cu = np.array([0, 70, 70, 150], dtype=np.int32)
+    Ab = m.matrix_cumprod(_t(A), cu_seqlens=_t(cu, torch.int32), reverse=reverse).cpu().double().numpy()
+    ref = np.empty(A.shape)
+    for row in range(2):
+        for s0, s1 in zip(cu[:-1], cu[1:]):
+            acc = np.eye(k)
+            steps = range(s1 - 1, s0 - 1, -1) if reverse else range(s0, s1)
+            for t in steps:
+                acc = A[row, t].astype(np.float64) @ acc
+                ref[row, t] = acc
+    err = np.abs(Ab - ref) / (1.0 + np.abs(ref))
+    assert err.max() <= TAU_FWD, err.max()
+    # gradient of sum(W * Abar) w.r.t. A, checked on a few entries by central differences in fp64
+    W = r.standard_normal(A.shape)
+    Ad = _t(A).requires_grad_(True)
+    (m.matrix_cumprod(Ad, cu_seqlens=_t(cu, torch.int32), reverse=reverse) * _t(W)).sum().backward()
+    g = Ad.grad.cpu().double().numpy()
+
+    def loss(Ax):
+        tot = 0.0
+        for row in range(2):
+            for s0, s1 in zip(cu[:-1], cu[1:]):
+                acc = np.eye(k)
+                steps = range(s1 - 1, s0 - 1, -1) if reverse else range(s0, s1)
+                for t in steps:
+                    acc = Ax[row, t] @ acc
+                    tot += float((W[row, t] * acc).sum())
+        return tot
+    A64 = A.astype(np.float64)
+    for (row, t, i, j) in [(0, 0, 0, 0), (0, 69, k - 1, 0), (1, 100, 0, k - 1), (1, 149, k - 1, k - 1), (1, 70, 1, 0)]:
+        e = np.zeros_like(A64)
+        e[row, t, i, j] = 1e-6
+        fd = (loss(A64 + e) - loss(A64 - e)) / 2e-6
+        assert abs(g[row, t, i, j] - fd) <= 1e-3 * (1 + abs(fd)), (row, t, i, j, g[row, t, i, j], fd)
+

@@ -201,6 +201,37 @@ def test_bf16_inputs(m, oracle_lib):
         run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev, bits=(gb, xb))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("T,stride", [(40000, 40000), (40001, 40003), (8192, 8192), (8193, 8195)])
+def test_16bit_forward_tiles(m, oracle_lib, dt, T, stride):
+    """16-bit forward: rows of several 4096-element tiles (look-back), exactly
+    two tiles, two tiles plus one element, rows starting at odd 2-byte offsets;
+    packed sequences with h0, both directions."""
+    r = np.random.default_rng(50 + T + stride + (dt == "fp16"))
+    rows = 3
+    g32 = r.uniform(0, 1, (rows, stride)).astype(np.float32)
+    x32 = r.standard_normal((rows, stride)).astype(np.float32)
+    if dt == "bf16":
+        gb = gen.bf16_round(g32).reshape(rows, stride)
+        xb = gen.bf16_round(x32).reshape(rows, stride)
+        g = gen.bf16_bits_to_f32(gb).reshape(rows, stride)[:, :T]
+        x = gen.bf16_bits_to_f32(xb).reshape(rows, stride)[:, :T]
+        gt, xt = _bf16(gb)[:, :T], _bf16(xb)[:, :T]
+    else:
+        g16, x16 = g32.astype(np.float16), x32.astype(np.float16)
+        g, x = g16[:, :T].astype(np.float32), x16[:, :T].astype(np.float32)
+        gt, xt = torch.from_numpy(g16).to(DEV)[:, :T], torch.from_numpy(x16).to(DEV)[:, :T]
+    cu = gen.segments_random(r, T, 6)
+    h0 = r.standard_normal((6, rows)).astype(np.float32)
+    for rev in (False, True):
+        out = torch.full((rows, stride), 7.0, device=DEV)
+        h = m.scan_fwd(gt, xt, h0=_t(h0), cu_seqlens=_t(cu, torch.int32), reverse=rev, out=out[:, :T])
+        close(h, oracle_lib.scan_fwd(g, x, h0=h0, cu_seqlens=cu, reverse=rev), TAU_FWD, "h")
+        assert torch.all(out[:, T:] == 7.0), "wrote outside the rows"
+        h = m.scan_fwd(gt, xt, reverse=rev, out=out[:, :T])
+        close(h, oracle_lib.scan_fwd(g, x, reverse=rev), TAU_FWD, "h dense")
+
+
 @pytest.mark.parametrize("T,stride", [(15000, 15000), (4097, 4099)])
 def test_fp16_inputs(m, oracle_lib, T, stride):
     """fp16 g and x (widened exactly), packed sequences with h0, both directions;

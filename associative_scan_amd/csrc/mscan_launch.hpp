@@ -73,7 +73,7 @@ hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t s
 // Blocks up to 16 x 16 on the matrix cores (scan_matrix16.hip), zero-padded
 // to 16 x 16: chunks per row, the workspace a call needs (always), and the
 // three-kernel launch (a.k, a.v in 1..16).
-int64_t matrix16_chunks(int64_t T);
+int64_t matrix16_chunks(int64_t T, bool bwd);
 size_t matrix16_ws_bytes(int64_t rows, int64_t T);
 hipError_t launch_matrix16(const MatArgs& a, bool bwd, hipStream_t st);
 

@@ -613,7 +613,7 @@ int64_t matrix_tiles(int64_t T, int k, int v, bool bwd) {
   else if (k == 2 && v == 2) tile = matrix_tile_steps<2, 2>(bwd);
   else if (k == 4 && v == 1) tile = matrix_tile_steps<4, 1>(bwd);
   else if (k == 4 && v == 4) tile = matrix_tile_steps<4, 4>(bwd);
-  else if (matrix_core_shape(k, v)) return matrix16_chunks(T);
+  else if (matrix_core_shape(k, v)) return matrix16_chunks(T, bwd);
   else return 0;
   return (T + tile - 1) / tile;
 }

@@ -22,25 +22,19 @@
 // result of one step (D layout) is the next step's B operand without moving
 // any data between lanes, and each A_t is one coalesced load.
 //
-// Three kernels per call (workspace per chunk of kChunk steps: P, Q and the
-// chunk's carry-in state as padded 16 x 16 blocks, and a flag for chunks that
-// contain a sequence start; nothing is read before it is written, so no
-// clearing is needed):
-//   summary : one wave per (row, chunk) walks the chunk: P <- X P, Q <- X Q + Y
-//   carry   : one wave per row composes the chunk summaries in order
-//   apply   : one wave per (row, chunk) recomputes every state from its
-//             carry-in and stores it (backward: dB, dA and dh0 as well).
+// One kernel per call (below: one wave per chunk of S steps, the chunk held in
+// registers, carries chained from chunk to chunk through the workspace).
 // Forward element (X, Y) = (A_t, B_t); backward element = (A of the previous
 // step in processing order, transposed; dy_t). A sequence's first step in
 // processing order is hard: forward h = A h0 + B, backward lam = dy.
+#include <algorithm>
+
 #include "mscan_device.hpp"
 #include "mscan_launch.hpp"
 
 namespace mscan {
 
-constexpr int kChunk16 = 64;                     // steps per chunk
-constexpr int kM16Floats = 256;                  // floats per padded 16 x 16 block
-constexpr size_t kM16ChunkBytes = 3 * 256 * 4;   // P, Q, carry-in per chunk
+constexpr int kM16Floats = 256;  // floats per padded 16 x 16 block
 
 __device__ __forceinline__ int m16_q() { return (int)(threadIdx.x >> 4) & 3; }
 __device__ __forceinline__ int m16_c() { return (int)(threadIdx.x & 15); }
@@ -158,19 +152,8 @@ struct M16Seq {
   __device__ __forceinline__ int seg() const { return min(max(k, 0), nseg - 1); }
 };
 
-struct M16Ws {
-  float* blocks;    // [rows][nchunks][3][256]: P, Q, carry-in
-  int32_t* hard;    // [rows][nchunks]
-};
-__device__ __forceinline__ M16Ws m16_ws(void* ws, int64_t rows, int nchunks) {
-  M16Ws w;
-  w.blocks = (float*)((char*)ws + ws_desc_offset());
-  w.hard = (int32_t*)((char*)ws + ws_desc_offset() + (size_t)rows * nchunks * kM16ChunkBytes);
-  return w;
-}
-
 // ---------------------------------------------------------------------------
-// step walking shared by the summary and apply kernels
+// step walking along one row
 // ---------------------------------------------------------------------------
 template <bool FULL, bool BWD, bool REV, bool VARLEN>
 struct M16Walk {
@@ -206,6 +189,39 @@ struct M16Walk {
     }
   }
   // step t of a row of A (k x k blocks) or of B / h / dy / dA-shaped outputs
+  // Bit s of first / last: processing step j0 + s (s < n <= 32) opens / closes
+  // a sequence in processing order (the row's ends always do).
+  __device__ __forceinline__ void masks(int64_t j0, int n, uint32_t& firstm, uint32_t& lastm) {
+    firstm = 0u;
+    lastm = 0u;
+    if constexpr (VARLEN) {
+      begin(j0);
+      for (int s = 0; s < n; ++s) {
+        bool f, l;
+        int sk;
+        at(j0 + s, f, l, sk);
+        firstm |= (uint32_t)f << s;
+        lastm |= (uint32_t)l << s;
+      }
+    } else {
+      if (j0 == 0) firstm = 1u;
+      if (j0 + n == T) lastm = 1u << (n - 1);
+    }
+  }
+  // sequence index of processing step j (0 without cu_seqlens), clamped to [0, nseg)
+  __device__ __forceinline__ int seg_of(int64_t j) const {
+    if constexpr (!VARLEN) {
+      return 0;
+    } else {
+      const int64_t t = phys(j);
+      int lo = 0, hi = a.nseg + 1;  // largest i with cu[i] <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)a.cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      return min(lo, a.nseg - 1);
+    }
+  }
   __device__ __forceinline__ const float* blkA(const float* base, int64_t t) const { return base + (row0 + t) * sh.na(); }
   __device__ __forceinline__ float* blkA(float* base, int64_t t) const { return base + (row0 + t) * sh.na(); }
   __device__ __forceinline__ const float* blkB(const float* base, int64_t t) const { return base + (row0 + t) * sh.nb(); }
@@ -221,119 +237,167 @@ struct M16Walk {
 };
 
 // ---------------------------------------------------------------------------
-// kernel 1: chunk summaries
+// single pass: chunk held in registers, carries chained through the workspace
 // ---------------------------------------------------------------------------
-template <bool FULL, bool BWD, bool REV, bool VARLEN>
-__global__ __launch_bounds__(64) void k_m16_summary(const MatArgs a) {
-  int64_t r;
-  int c;
-  tile_of_block<true>(a.rows, a.ntiles, r, c);
-  M16Walk<FULL, BWD, REV, VARLEN> wk(a, r);
-  const int64_t j0 = (int64_t)c * kChunk16, j1 = min(j0 + kChunk16, a.T);
-  wk.begin(j0);
-  v4f P = m16_ident(), Q = m16_zero();
-  bool hard = false;
-#pragma unroll 2
-  for (int64_t j = j0; j < j1; ++j) {
-    bool first, last;
-    int sk;
-    wk.at(j, first, last, sk);
-    const v4f Y = wk.sh.ldB_D(wk.blkB(a.B, wk.phys(j)));
-    if (first) {
-      hard = true;
-      P = m16_zero();
-      if constexpr (!BWD) Q = a.h0 ? m16_mm(wk.sh.ldA_R(wk.blkA(a.A, wk.phys(j))), wk.h0D(sk), Y) : Y;
-      else Q = Y;
-    } else {
-      const v4f X = wk.xop(j);
-      P = m16_mm(X, P, m16_zero());
-      Q = m16_mm(X, Q, Y);
-    }
-  }
-  const M16Ws w = m16_ws(a.ws, a.rows, a.ntiles);
-  float* out = w.blocks + ((int64_t)r * a.ntiles + c) * 3 * kM16Floats;
-  m16_stD(out, P);
-  m16_stD(out + kM16Floats, Q);
-  if (threadIdx.x == 0) w.hard[(int64_t)r * a.ntiles + c] = hard ? 1 : 0;
-}
+// A wave owns S steps of one row. It loads the chunk's transition and
+// injection blocks once into registers, walks them for the chunk summary
+// (P, Q), takes its carry-in from the chunk before it, publishes the state
+// after the chunk (h_out = P h_in + Q) and applies the carry from the same
+// registers, so every input block crosses HBM once.
+//
+// Publication: h_out as 256 self-validating 64-bit words {tag, value} per
+// chunk (lane order, four per lane), written and read with relaxed
+// agent-scope atomics, so no fence is needed; the words are zero-filled
+// before each call. A chunk that contains a sequence start publishes h_out
+// right after its summary (it does not depend on the carry-in); the row's
+// first chunk always does, so every chain starts. Each chunk reads only its
+// predecessor's h_out, never an aggregate further back, so the rounding of
+// every result is fixed: repeated calls give identical bits.
+constexpr uint32_t kM16Tag = 2u;
+constexpr size_t kM16PubBytes = 256 * 8;  // one published h_out
 
-// ---------------------------------------------------------------------------
-// kernel 2: carry-in state of every chunk of a row
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_m16_carry(const MatArgs a) {
-  const int64_t r = blockIdx.x;
-  const M16Ws w = m16_ws(a.ws, a.rows, a.ntiles);
-  float* rowb = w.blocks + (int64_t)r * a.ntiles * 3 * kM16Floats;
-  const int32_t* hard = w.hard + (int64_t)r * a.ntiles;
-  v4f h = m16_zero();
-  // the next chunk's summary is loaded while the current one is applied
-  v4f Pn = m16_ldR(rowb), Qn = m16_ldD(rowb + kM16Floats);
-  int hn = hard[0];
-  for (int c = 0; c < a.ntiles; ++c) {
-    const v4f P = Pn, Q = Qn;
-    const int hc = hn;
-    if (c + 1 < a.ntiles) {
-      const float* nb = rowb + (int64_t)(c + 1) * 3 * kM16Floats;
-      Pn = m16_ldR(nb);
-      Qn = m16_ldD(nb + kM16Floats);
-      hn = hard[c + 1];
+__device__ __forceinline__ void m16_publish(uint64_t* w, v4f v) {
+  uint64_t* p = w + threadIdx.x * 4;
+  st_u64(p + 0, pack_word(kM16Tag, v.x));
+  st_u64(p + 1, pack_word(kM16Tag, v.y));
+  st_u64(p + 2, pack_word(kM16Tag, v.z));
+  st_u64(p + 3, pack_word(kM16Tag, v.w));
+}
+// h_out of a chunk once every lane sees all four of its words published;
+// false after the spin limit (then the header's error word is set)
+__device__ __forceinline__ bool m16_wait(const uint64_t* w, uint32_t* hdr, v4f& v) {
+  const uint64_t* p = w + threadIdx.x * 4;
+  for (uint32_t spins = 0;; ++spins) {
+    const uint64_t a = ld_u64(p + 0), b = ld_u64(p + 1), c = ld_u64(p + 2), d = ld_u64(p + 3);
+    const bool ok = word_tag(a) == kM16Tag && word_tag(b) == kM16Tag && word_tag(c) == kM16Tag &&
+                    word_tag(d) == kM16Tag;
+    if (__ballot(!ok) == 0ull) {
+      v = v4f{word_val(a), word_val(b), word_val(c), word_val(d)};
+      return true;
     }
-    m16_stD(rowb + (int64_t)c * 3 * kM16Floats + 2 * kM16Floats, h);  // carry-in of chunk c
-    h = hc ? Q : m16_mm(P, h, Q);
+    if (spins > kSpinLimit) {
+      if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
-// ---------------------------------------------------------------------------
-// kernel 3: states (forward) or adjoints and gradients (backward)
-// ---------------------------------------------------------------------------
-template <bool FULL, bool BWD, bool REV, bool VARLEN>
-__global__ __launch_bounds__(64) void k_m16_apply(const MatArgs a) {
+// D layout in, R layout out (a transpose of the register tile) through LDS
+__device__ __forceinline__ v4f m16_d_to_r(float* s_t, v4f x) {
+  const int q = m16_q(), c = m16_c();
+  s_t[(4 * q + 0) * 20 + c] = x.x;
+  s_t[(4 * q + 1) * 20 + c] = x.y;
+  s_t[(4 * q + 2) * 20 + c] = x.z;
+  s_t[(4 * q + 3) * 20 + c] = x.w;
+  wave_lds_sync();
+  const v4f r = *(const v4f*)(s_t + c * 20 + 4 * q);
+  wave_lds_sync();
+  return r;
+}
+
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+__global__ __launch_bounds__(64) void k_m16_fused(const MatArgs a) {
+  static_assert(S <= 32, "step masks are 32-bit");
   // 16 x 16 transpose tile, rows padded to 20 floats (conflict-free both ways)
-  __shared__ __attribute__((aligned(16))) float s_t[BWD ? 16 * 20 : 4];
+  __shared__ __attribute__((aligned(16))) float s_t[16 * 20];
   int64_t r;
   int c;
   tile_of_block<true>(a.rows, a.ntiles, r, c);
   M16Walk<FULL, BWD, REV, VARLEN> wk(a, r);
-  const int64_t j0 = (int64_t)c * kChunk16, j1 = min(j0 + kChunk16, a.T);
-  wk.begin(j0);
-  const M16Ws w = m16_ws(a.ws, a.rows, a.ntiles);
-  v4f h = m16_ldD(w.blocks + ((int64_t)r * a.ntiles + c) * 3 * kM16Floats + 2 * kM16Floats);
-  const int q = m16_q(), cl = m16_c();
-#pragma unroll 2
-  for (int64_t j = j0; j < j1; ++j) {
-    bool first, last;
-    int sk;
-    wk.at(j, first, last, sk);
-    const int64_t t = wk.phys(j);
-    const v4f Y = wk.sh.ldB_D(wk.blkB(a.B, t));
-    if constexpr (!BWD) {
-      if (first) h = a.h0 ? m16_mm(wk.sh.ldA_R(wk.blkA(a.A, t)), wk.h0D(sk), Y) : Y;
-      else h = m16_mm(wk.xop(j), h, Y);
-      wk.sh.stB_D(wk.blkB(a.out0, t), h);
-    } else {
-      h = first ? Y : m16_mm(wk.xop(j), h, Y);  // h holds lam
-      wk.sh.stB_D(wk.blkB(a.out0, t), h);     // dB = lam
-      // dA_t = lam h_prev^T: lam to R layout through LDS, h_prev^T in D
-      // layout is h_prev in R layout (h_prev = h0 at the sequence's
-      // forward-first step, else the forward state one processing step on)
-      s_t[(4 * q + 0) * 20 + cl] = h.x;
-      s_t[(4 * q + 1) * 20 + cl] = h.y;
-      s_t[(4 * q + 2) * 20 + cl] = h.z;
-      s_t[(4 * q + 3) * 20 + cl] = h.w;
-      wave_lds_sync();
-      const v4f lamR = *(const v4f*)(s_t + cl * 20 + 4 * q);
-      wave_lds_sync();
-      v4f hpR;
-      if (last) {
-        hpR = a.h0 ? wk.sh.ldB_R(wk.h0p(sk)) : m16_zero();
+  const int64_t j0 = (int64_t)c * S;
+  const int n = (int)min((int64_t)S, a.T - j0);
+
+  // sequence starts and ends in the chunk (before the loads: nothing is live yet)
+  uint32_t firstm, lastm;
+  wk.masks(j0, n, firstm, lastm);
+
+  // ---- load the chunk: transition operand X (R layout) and injection Y (D
+  // layout); backward also the forward state one processing step on, in R
+  // layout (h_prev^T in D layout, for dA = lam h_prev^T). Steps past the row's
+  // end (s >= n) hold zeros and are computed but never stored or published.
+  v4f X[S], Y[S], H[BWD ? S : 1];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    X[s] = m16_zero();
+    Y[s] = m16_zero();
+    if constexpr (BWD) H[s] = m16_zero();
+    if (s < n) {
+      const int64_t j = j0 + s;
+      const int64_t t = wk.phys(j);
+      Y[s] = wk.sh.ldB_D(wk.blkB(a.B, t));
+      if constexpr (!BWD) {
+        X[s] = wk.sh.ldA_R(wk.blkA(a.A, t));
       } else {
-        hpR = wk.sh.ldB_R(wk.blkB(a.hs, wk.phys(j + 1)));
+        if (j > 0) X[s] = wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j - 1)));  // (A one processing step back)^T
+        if (j + 1 < a.T) H[s] = wk.sh.ldB_R(wk.blkB(a.hs, wk.phys(j + 1)));
       }
-      wk.sh.stA_D(wk.blkA(a.out1, t), m16_mm(lamR, hpR, m16_zero()));  // dA = lam h_prev^T
-      if (last && a.dh0) {
-        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
-        const v4f d = m16_mm(wk.sh.ldA_D(wk.blkA(a.A, t)), h, m16_zero());
-        wk.sh.stB_D(a.dh0 + ((int64_t)sk * a.rows + r) * wk.sh.nb(), d);
+    }
+  }
+  wait_stage_loads();
+  // Sequence boundaries, folded into the registers so that the step loops
+  // below hold no loads (a load in them would make every step wait for the
+  // stores before it): forward, a first step's value A h0 + B; backward, the
+  // h_prev of a sequence's forward-first step is h0.
+  if (a.h0 && (BWD ? lastm : firstm)) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (((BWD ? lastm : firstm) >> s) & 1u) {
+        const int sk = wk.seg_of(j0 + s);
+        if constexpr (!BWD) Y[s] = m16_mm(X[s], wk.h0D(sk), Y[s]);
+        else H[s] = wk.sh.ldB_R(wk.h0p(sk));
+      }
+    }
+    wait_stage_loads();
+  } else if (BWD && lastm) {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if ((lastm >> s) & 1u) H[s] = m16_zero();
+  }
+
+  // ---- chunk summary (a sequence's first step is hard: P = 0, Q = its value)
+  const bool hard = firstm != 0u, first0 = (firstm & 1u) != 0u;
+  v4f P = m16_ident(), Q = m16_zero();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool f = (firstm >> s) & 1u;
+    const v4f Pn = m16_mm(X[s], P, m16_zero()), Qn = m16_mm(X[s], Q, Y[s]);
+    P = f ? m16_zero() : Pn;
+    Q = f ? Y[s] : Qn;
+  }
+
+  // ---- carry-in from the chunk before, h_out for the chunk after
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
+  const int64_t me = r * a.ntiles + c;
+  const bool publish = c + 1 < a.ntiles;
+  if (publish && hard) m16_publish(pub + me * 256, Q);  // h_out = Q whatever the carry-in
+  const v4f PR = (publish && !hard) ? m16_d_to_r(s_t, P) : m16_zero();  // off the chain
+  v4f hin = m16_zero();
+  if (!first0) {
+    if (!m16_wait(pub + (me - 1) * 256, hdr, hin)) hin = m16_zero();
+  }
+  if (publish && !hard) m16_publish(pub + me * 256, m16_mm(PR, hin, Q));
+
+  // ---- apply from the registers
+  v4f h = hin;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool first = (firstm >> s) & 1u;
+    const v4f hn = m16_mm(X[s], h, Y[s]);
+    h = first ? Y[s] : hn;  // h holds lam in the backward
+    if (s < n) {
+      const int64_t j = j0 + s;
+      const int64_t t = wk.phys(j);
+      wk.sh.stB_D(wk.blkB(a.out0, t), h);  // forward h; backward dB = lam
+      if constexpr (BWD) {
+        // dA_t = lam h_prev^T
+        wk.sh.stA_D(wk.blkA(a.out1, t), m16_mm(m16_d_to_r(s_t, h), H[s], m16_zero()));
+        if (((lastm >> s) & 1u) && a.dh0) {
+          // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
+          const v4f d = m16_mm(wk.sh.ldA_D(wk.blkA(a.A, t)), h, m16_zero());
+          wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), d);
+        }
       }
     }
   }
@@ -342,37 +406,48 @@ __global__ __launch_bounds__(64) void k_m16_apply(const MatArgs a) {
 // ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
-int64_t matrix16_chunks(int64_t T) { return (T + kChunk16 - 1) / kChunk16; }
+// Steps per chunk of the single-pass kernel, from timing 8 / 16 / 32 at
+// (16, 16), 512 rows, T = 4096: the forward is fastest with 32 (half the
+// chained hops and published words of 16, despite one wave per SIMD), the
+// backward ties at 16 and 32 and takes 16 (32 spills).
+constexpr int kChunkFwd = 32, kChunkBwd = 16;
 
-size_t matrix16_ws_bytes(int64_t rows, int64_t T) {
-  const int64_t n = rows * matrix16_chunks(T);
-  return ws_desc_offset() + (size_t)n * kM16ChunkBytes + (size_t)n * sizeof(int32_t);
+int64_t matrix16_chunks(int64_t T, bool bwd) {
+  const int64_t S = bwd ? kChunkBwd : kChunkFwd;
+  return (T + S - 1) / S;
 }
 
-template <bool FULL, bool BWD, bool REV, bool VARLEN>
-static hipError_t launch_m16_dir(const MatArgs& a, hipStream_t st) {
-  const dim3 tiles((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles)), one(64);
-  hipLaunchKernelGGL((k_m16_summary<FULL, BWD, REV, VARLEN>), tiles, one, 0, st, a);
-  hipLaunchKernelGGL(k_m16_carry, dim3((unsigned)a.rows), one, 0, st, a);
-  hipLaunchKernelGGL((k_m16_apply<FULL, BWD, REV, VARLEN>), tiles, one, 0, st, a);
+size_t matrix16_ws_bytes(int64_t rows, int64_t T) {
+  const int64_t n = std::max(matrix16_chunks(T, false), matrix16_chunks(T, true));
+  return ws_desc_offset() + (size_t)(rows * n) * kM16PubBytes;
+}
+
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+static hipError_t launch_m16f_dir(const MatArgs& a0, hipStream_t st) {
+  MatArgs a = a0;
+  a.ntiles = (int32_t)((a.T + S - 1) / S);
+  const int64_t n = a.rows * a.ntiles;
+  // fresh words (and header) for this call: a zero tag = not published
+  const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kM16PubBytes, st);
+  if (z != hipSuccess) return z;
+  hipLaunchKernelGGL((k_m16_fused<FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool FULL>
 static hipError_t launch_m16_shape(const MatArgs& a, bool bwd, hipStream_t st) {
+  constexpr int SF = kChunkFwd, SB = kChunkBwd;
   const bool rev = a.rev != 0, vl = a.cu != nullptr;
   if (bwd) {
-    if (rev) return vl ? launch_m16_dir<FULL, true, true, true>(a, st) : launch_m16_dir<FULL, true, true, false>(a, st);
-    return vl ? launch_m16_dir<FULL, true, false, true>(a, st) : launch_m16_dir<FULL, true, false, false>(a, st);
+    if (rev) return vl ? launch_m16f_dir<FULL, true, true, true, SB>(a, st) : launch_m16f_dir<FULL, true, true, false, SB>(a, st);
+    return vl ? launch_m16f_dir<FULL, true, false, true, SB>(a, st) : launch_m16f_dir<FULL, true, false, false, SB>(a, st);
   }
-  if (rev) return vl ? launch_m16_dir<FULL, false, true, true>(a, st) : launch_m16_dir<FULL, false, true, false>(a, st);
-  return vl ? launch_m16_dir<FULL, false, false, true>(a, st) : launch_m16_dir<FULL, false, false, false>(a, st);
+  if (rev) return vl ? launch_m16f_dir<FULL, false, true, true, SF>(a, st) : launch_m16f_dir<FULL, false, true, false, SF>(a, st);
+  return vl ? launch_m16f_dir<FULL, false, false, true, SF>(a, st) : launch_m16f_dir<FULL, false, false, false, SF>(a, st);
 }
 
-hipError_t launch_matrix16(const MatArgs& a0, bool bwd, hipStream_t st) {
-  if (a0.k < 1 || a0.k > 16 || a0.v < 1 || a0.v > 16) return hipErrorInvalidValue;
-  MatArgs a = a0;
-  a.ntiles = (int32_t)matrix16_chunks(a.T);
+hipError_t launch_matrix16(const MatArgs& a, bool bwd, hipStream_t st) {
+  if (a.k < 1 || a.k > 16 || a.v < 1 || a.v > 16) return hipErrorInvalidValue;
   if (a.k == 16 && a.v == 16) return launch_m16_shape<true>(a, bwd, st);
   return launch_m16_shape<false>(a, bwd, st);
 }

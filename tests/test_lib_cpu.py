@@ -157,11 +157,13 @@ def test_torch_custom_ops_registered_with_fake_kernels(m):
 
 
 def test_matrix_core_workspace_always_required(m):
-    # the matrix-core shapes chain 64-step chunks through the workspace on every
-    # call: header (128) + per chunk P, Q and carry-in as padded 16 x 16 blocks
-    # (3 x 1 KiB) + a 4-byte flag
+    # the matrix-core shapes chain chunks of 32 (forward) or 16 (backward) steps
+    # through the workspace on every call: header (128), then per chunk its
+    # published h_out as 256 tagged 8-byte words (a padded 16 x 16 block),
+    # sized for the larger chunk count
     p = _prob(m, rows=5, T=100)
-    need = 128 + 5 * 2 * (3 * 1024 + 4)
+    n = 5 * 7
+    need = 128 + n * 256 * 8
     for k, v in ((16, 16), (8, 8), (1, 16), (16, 1), (2, 4), (4, 8)):
         assert m.workspace_bytes(p, m.OP_MATRIX_FWD, k, v) == need
         assert m.workspace_bytes(p, m.OP_MATRIX_BWD, k, v) == need

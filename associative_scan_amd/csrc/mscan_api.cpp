@@ -61,7 +61,7 @@ mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
 // Workspace of a matrix op: header, then (look-back only) k*k + 2*k*v
 // descriptor words per tile.
 size_t matrix_ws_bytes(const mscan_problem* p, int k, int v) {
-  if (mscan::matrix_core_shape(k, v)) return mscan::matrix16_ws_bytes(p->rows, p->T);
+  if (mscan::matrix_core_shape(k, v)) return mscan::matrix_core_ws_bytes(p->rows, p->T, k, v);
   int64_t nt = 0;
   for (int b = 0; b < 2; ++b) {
     const int64_t n = mscan::matrix_tiles(p->T, k, v, b == 1);

@@ -64,18 +64,19 @@ struct MatArgs {
 
 // (k, v) served by the VALU kernels (scan_matrix.hip): (2,1), (2,2), (4,1), (4,4).
 bool matrix_valu_shape(int k, int v);
-// (k, v) served by the matrix-core kernels (scan_matrix16.hip): every other
-// pair of the envelope k, v in {1, 2, 4, 8, 16} except (1, 1), the scalar scan.
+// (k, v) served by the matrix-core kernels (scan_matrix_cores.hip): every
+// other pair of the envelope k, v in {1, 2, 4, 8, 16} except (1, 1), the
+// scalar scan.
 bool matrix_core_shape(int k, int v);
 // Tiles per row of the matrix kernels for (k, v) (0 if unsupported).
 int64_t matrix_tiles(int64_t T, int k, int v, bool bwd);
 hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t st);
-// Blocks up to 16 x 16 on the matrix cores (scan_matrix16.hip), zero-padded
-// to 16 x 16: chunks per row, the workspace a call needs (always), and the
-// three-kernel launch (a.k, a.v in 1..16).
-int64_t matrix16_chunks(int64_t T, bool bwd);
-size_t matrix16_ws_bytes(int64_t rows, int64_t T);
-hipError_t launch_matrix16(const MatArgs& a, bool bwd, hipStream_t st);
+// Matrix-core kernels, blocks zero-padded to 4 x 4 (k, v <= 4) or 16 x 16:
+// chunks per row, the workspace a call needs (always), and the launch
+// (a.k, a.v in 1..16).
+int64_t matrix_core_chunks(int64_t T, bool bwd);
+size_t matrix_core_ws_bytes(int64_t rows, int64_t T, int k, int v);
+hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st);
 
 // Fill n floats (or bytes / 4 words) with zero on `st` (no hipMemsetAsync, so
 // callers may capture it in a graph).

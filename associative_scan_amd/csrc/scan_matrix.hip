@@ -613,7 +613,7 @@ int64_t matrix_tiles(int64_t T, int k, int v, bool bwd) {
   else if (k == 2 && v == 2) tile = matrix_tile_steps<2, 2>(bwd);
   else if (k == 4 && v == 1) tile = matrix_tile_steps<4, 1>(bwd);
   else if (k == 4 && v == 4) tile = matrix_tile_steps<4, 4>(bwd);
-  else if (matrix_core_shape(k, v)) return matrix16_chunks(T, bwd);
+  else if (matrix_core_shape(k, v)) return matrix_core_chunks(T, bwd);
   else return 0;
   return (T + tile - 1) / tile;
 }
@@ -627,7 +627,7 @@ hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t s
     MatArgs b = a;
     b.k = k;
     b.v = v;
-    return launch_matrix16(b, bwd, st);
+    return launch_matrix_core(b, bwd, st);
   }
   return hipErrorInvalidValue;
 }

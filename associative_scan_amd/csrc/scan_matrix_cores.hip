@@ -1,0 +1,464 @@
+// Matrix-affine scan on the matrix cores, h_t = A_t h_{t-1} + B_t with k x k
+// transitions and k x v states ("Triton scan kernels", "One associative-scan
+// family": matrix_affine_scan with block size k and injection width v; the
+// page's kernel envelope is k, v in {1, 2, 4, 8, 16}), and its reverse adjoint
+// (same page, "Autograd integration and the reversed-scan backward").
+//
+// Each step is one or two small dense products, run on the matrix cores in
+// IEEE fp32 (fp32 inputs, fp32 accumulation: the precision the page's TF32 /
+// IEEE guard asks for at k = 16). Two register tiles:
+//   Tile16: one 16 x 16 block per wave (k or v above 4), products on
+//           v_mfma_f32_16x16x4_f32;
+//   Tile4 : sixteen 4 x 4 blocks per wave, one per row of a group of 16 rows
+//           (k, v <= 4), products on v_mfma_f32_4x4x1_16b_f32. Its per-row
+//           accesses are short (64 bytes of A per step), and on (4, 4) and
+//           (2, 1) it measured 1.2-6x slower than the VALU kernels, which keep
+//           (2, 1), (2, 2), (4, 1) and (4, 4); Tile4 serves the other shapes
+//           with k, v <= 4 (4x less padding than Tile16).
+// Blocks smaller than the tile are zero-padded in registers: rows and columns
+// past k (or v) load as 0 and are never stored, and a zero-padded A and B keep
+// the padding of h, the adjoint and the chunk summaries at 0, so the padded
+// arithmetic gives the k x v result exactly.
+//
+// Layouts, with E the tile edge, dr0 = the lane's first D-layout row and
+// dc = its column (Tile16: lane 16 q + c has dr0 = 4 q, dc = c; Tile4: lane
+// 4 b + c, block b, has dr0 = 0, dc = c):
+//   D layout: register i holds X[dr0 + i][dc]   (an MFMA result)
+//   R layout: register i holds X[dc][dr0 + i]   (one 16-byte load of a row)
+// A product splits its K index into four MFMAs taking register s of M in R
+// layout and register s of P in D layout, so a step's result (D layout) is the
+// next step's operand without moving data between lanes; the R layout of X is
+// the D layout of X^T.
+//
+// One kernel per call: a wave owns S steps of one row (Tile16) or of 16 rows
+// (Tile4), carries chained from chunk to chunk through the workspace (below).
+// Forward element (X, Y) = (A_t, B_t); backward element = (A of the previous
+// step in processing order, transposed; dy_t). A sequence's first step in
+// processing order is hard: forward h = A h0 + B, backward lam = dy.
+#include <algorithm>
+
+#include "mscan_device.hpp"
+#include "mscan_launch.hpp"
+
+namespace mscan {
+
+__device__ __forceinline__ v4f mc_zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// register tiles
+// ---------------------------------------------------------------------------
+struct Tile16 {
+  static constexpr int E = 16, RPW = 1;  // tile edge, rows per wave
+  __device__ static __forceinline__ int lrow() { return 0; }
+  __device__ static __forceinline__ int dr0() { return 4 * (int)((threadIdx.x >> 4) & 3); }
+  __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 15); }
+  // acc + M P with M in R layout and P in D layout; result in D layout
+  __device__ static __forceinline__ v4f mm(v4f mR, v4f pD, v4f acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mR.x, pD.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mR.y, pD.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mR.z, pD.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(mR.w, pD.w, acc, 0, 0, 0);
+    return acc;
+  }
+  // D layout in, R layout out, through LDS (rows padded to 20 floats)
+  __device__ static __forceinline__ v4f d_to_r(float* s, v4f x) {
+    const int r0 = dr0(), c = dc();
+    s[(r0 + 0) * 20 + c] = x.x;
+    s[(r0 + 1) * 20 + c] = x.y;
+    s[(r0 + 2) * 20 + c] = x.z;
+    s[(r0 + 3) * 20 + c] = x.w;
+    wave_lds_sync();
+    const v4f r = *(const v4f*)(s + c * 20 + r0);
+    wave_lds_sync();
+    return r;
+  }
+};
+
+struct Tile4 {
+  static constexpr int E = 4, RPW = 16;
+  __device__ static __forceinline__ int lrow() { return (int)(threadIdx.x >> 2); }
+  __device__ static __forceinline__ int dr0() { return 0; }
+  __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 3); }
+  __device__ static __forceinline__ v4f mm(v4f mR, v4f pD, v4f acc) {
+    acc = __builtin_amdgcn_mfma_f32_4x4x1f32(mR.x, pD.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_4x4x1f32(mR.y, pD.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_4x4x1f32(mR.z, pD.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_4x4x1f32(mR.w, pD.w, acc, 0, 0, 0);
+    return acc;
+  }
+  __device__ static __forceinline__ v4f d_to_r(float* s, v4f x) {
+    float* b = s + lrow() * 16;
+    const int c = dc();
+    b[0 * 4 + c] = x.x;
+    b[1 * 4 + c] = x.y;
+    b[2 * 4 + c] = x.z;
+    b[3 * 4 + c] = x.w;
+    wave_lds_sync();
+    const v4f r = *(const v4f*)(b + c * 4);
+    wave_lds_sync();
+    return r;
+  }
+};
+
+template <class TL>
+__device__ __forceinline__ v4f tile_ident() {
+  const int r0 = TL::dr0(), c = TL::dc();
+  return v4f{(r0 + 0 == c) ? 1.f : 0.f, (r0 + 1 == c) ? 1.f : 0.f, (r0 + 2 == c) ? 1.f : 0.f,
+             (r0 + 3 == c) ? 1.f : 0.f};
+}
+
+// Block shapes on a tile. FULL: k = v = E, 16-byte loads where the layout
+// allows. Otherwise k, v <= E at run time, element-wise loads masked to the
+// block (zero outside) and stores masked to it.
+template <class TL, bool FULL>
+struct TileShape {
+  static constexpr int E = TL::E;
+  int k, v;
+  __device__ __forceinline__ int64_t na() const { return FULL ? E * E : k * k; }  // floats of A per step
+  __device__ __forceinline__ int64_t nb() const { return FULL ? E * E : k * v; }  // floats of B / h per step
+  __device__ static __forceinline__ float el(const float* X, int row, int col, int rows, int cols) {
+    return (row < rows && col < cols) ? X[row * cols + col] : 0.f;
+  }
+  __device__ static __forceinline__ v4f ld_D(const float* X, int rows, int cols) {
+    const int r0 = TL::dr0(), c = TL::dc();
+    if (FULL) return v4f{X[(r0 + 0) * E + c], X[(r0 + 1) * E + c], X[(r0 + 2) * E + c], X[(r0 + 3) * E + c]};
+    return v4f{el(X, r0 + 0, c, rows, cols), el(X, r0 + 1, c, rows, cols), el(X, r0 + 2, c, rows, cols),
+               el(X, r0 + 3, c, rows, cols)};
+  }
+  __device__ static __forceinline__ v4f ld_R(const float* X, int rows, int cols) {
+    const int r0 = TL::dr0(), c = TL::dc();
+    if (FULL) return *(const v4f*)(X + c * E + r0);
+    return v4f{el(X, c, r0 + 0, rows, cols), el(X, c, r0 + 1, rows, cols), el(X, c, r0 + 2, rows, cols),
+               el(X, c, r0 + 3, rows, cols)};
+  }
+  __device__ static __forceinline__ void st_D(float* X, v4f x, int rows, int cols) {
+    const int r0 = TL::dr0(), c = TL::dc();
+    if (c < cols) {
+      if (r0 + 0 < rows) X[(r0 + 0) * cols + c] = x.x;
+      if (r0 + 1 < rows) X[(r0 + 1) * cols + c] = x.y;
+      if (r0 + 2 < rows) X[(r0 + 2) * cols + c] = x.z;
+      if (r0 + 3 < rows) X[(r0 + 3) * cols + c] = x.w;
+    }
+  }
+  // A (k x k) in R layout, and in D layout (= A^T in R layout)
+  __device__ __forceinline__ v4f ldA_R(const float* X) const { return ld_R(X, FULL ? E : k, FULL ? E : k); }
+  __device__ __forceinline__ v4f ldA_D(const float* X) const { return ld_D(X, FULL ? E : k, FULL ? E : k); }
+  // B / h / dy / h0 (k x v) in D layout, and in R layout (= the D layout of the transpose)
+  __device__ __forceinline__ v4f ldB_D(const float* X) const { return ld_D(X, FULL ? E : k, FULL ? E : v); }
+  __device__ __forceinline__ v4f ldB_R(const float* X) const { return ld_R(X, FULL ? E : k, FULL ? E : v); }
+  __device__ __forceinline__ void stB_D(float* X, v4f x) const { st_D(X, x, FULL ? E : k, FULL ? E : v); }
+  __device__ __forceinline__ void stA_D(float* X, v4f x) const { st_D(X, x, FULL ? E : k, FULL ? E : k); }
+};
+
+// Sequence bookkeeping along one row, walked one physical step at a time in
+// processing order (uniform across the wave). k = largest index with cu[k] <= t.
+struct McSeq {
+  const int32_t* cu;
+  int ncu, nseg;
+  int k;
+  __device__ __forceinline__ void init(const int32_t* cu_, int nseg_, int64_t t) {
+    cu = cu_;
+    nseg = nseg_;
+    ncu = nseg_ + 1;
+    int lo = 0, hi = ncu;  // largest i in [0, ncu) with cu[i] <= t (0 if none)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    k = lo;
+  }
+  __device__ __forceinline__ void move_to(int64_t t, bool up) {
+    if (up) {
+      while (k + 1 < ncu && (int64_t)cu[k + 1] <= t) ++k;
+    } else {
+      while (k > 0 && (int64_t)cu[k] > t) --k;
+    }
+  }
+  __device__ __forceinline__ bool is_start(int64_t t) const { return (int64_t)cu[k] == t; }
+  __device__ __forceinline__ bool is_end(int64_t t) const { return k + 1 < ncu && (int64_t)cu[k + 1] - 1 == t; }
+  __device__ __forceinline__ int seg() const { return min(max(k, 0), nseg - 1); }
+};
+
+// ---------------------------------------------------------------------------
+// step walking along one row (the lane's row)
+// ---------------------------------------------------------------------------
+template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN>
+struct McWalk {
+  const MatArgs& a;
+  TileShape<TL, FULL> sh;
+  int64_t row0, T, r;
+  McSeq seq;
+  __device__ __forceinline__ McWalk(const MatArgs& a_, int64_t r_) : a(a_), r(r_) {
+    sh.k = a_.k;
+    sh.v = a_.v;
+    row0 = r_ * a_.stride;
+    T = a_.T;
+  }
+  __device__ __forceinline__ int64_t phys(int64_t j) const { return REV ? T - 1 - j : j; }
+  // Bit s of first / last: processing step j0 + s (s < n <= 32) opens / closes
+  // a sequence in processing order; the row's ends always do, whatever
+  // cu_seqlens holds, so no step reaches a neighbour outside the row.
+  __device__ __forceinline__ void masks(int64_t j0, int n, uint32_t& firstm, uint32_t& lastm) {
+    firstm = 0u;
+    lastm = 0u;
+    if constexpr (VARLEN) {
+      seq.init(a.cu, a.nseg, phys(j0));
+      for (int s = 0; s < n; ++s) {
+        const int64_t j = j0 + s, t = phys(j);
+        seq.move_to(t, !REV);
+        const bool st = seq.is_start(t), en = seq.is_end(t);
+        firstm |= (uint32_t)((REV ? en : st) || j == 0) << s;
+        lastm |= (uint32_t)((REV ? st : en) || j == T - 1) << s;
+      }
+    } else {
+      if (j0 == 0) firstm = 1u;
+      if (j0 + n == T) lastm = 1u << (n - 1);
+    }
+  }
+  // sequence index of processing step j (0 without cu_seqlens), clamped to [0, nseg)
+  __device__ __forceinline__ int seg_of(int64_t j) const {
+    if constexpr (!VARLEN) {
+      return 0;
+    } else {
+      const int64_t t = phys(j);
+      int lo = 0, hi = a.nseg + 1;  // largest i with cu[i] <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)a.cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      return min(lo, a.nseg - 1);
+    }
+  }
+  // step t of this row of A (k x k blocks) or of B / h / dy (k x v blocks)
+  __device__ __forceinline__ const float* blkA(const float* base, int64_t t) const { return base + (row0 + t) * sh.na(); }
+  __device__ __forceinline__ float* blkA(float* base, int64_t t) const { return base + (row0 + t) * sh.na(); }
+  __device__ __forceinline__ const float* blkB(const float* base, int64_t t) const { return base + (row0 + t) * sh.nb(); }
+  __device__ __forceinline__ float* blkB(float* base, int64_t t) const { return base + (row0 + t) * sh.nb(); }
+  // initial state (k x v) of sequence sk of this row
+  __device__ __forceinline__ const float* h0p(int sk) const { return a.h0 + ((int64_t)sk * a.rows + r) * sh.nb(); }
+};
+
+// ---------------------------------------------------------------------------
+// single pass: chunk held in registers, carries chained through the workspace
+// ---------------------------------------------------------------------------
+// A wave owns S steps of its rows. It loads the chunk's transition and
+// injection blocks once into registers, walks them for the chunk summary
+// (P, Q), takes its carry-in from the chunk before it, publishes the state
+// after the chunk (h_out = P h_in + Q) and applies the carry from the same
+// registers, so every input block crosses HBM once.
+//
+// Publication: h_out as 256 self-validating 64-bit words {tag, value} per
+// chunk (lane order, four per lane), written and read with relaxed
+// agent-scope atomics, so no fence is needed; the words are zero-filled
+// before each call. A chunk that contains a sequence start publishes h_out
+// right after its summary (it does not depend on the carry-in); the row's
+// first chunk always does, so every chain starts. Each chunk reads only its
+// predecessor's h_out, never an aggregate further back, so the rounding of
+// every result is fixed: repeated calls give identical bits.
+constexpr uint32_t kMcTag = 2u;
+constexpr size_t kMcPubBytes = 256 * 8;  // one published h_out
+
+__device__ __forceinline__ void mc_publish(uint64_t* w, v4f v) {
+  uint64_t* p = w + threadIdx.x * 4;
+  st_u64(p + 0, pack_word(kMcTag, v.x));
+  st_u64(p + 1, pack_word(kMcTag, v.y));
+  st_u64(p + 2, pack_word(kMcTag, v.z));
+  st_u64(p + 3, pack_word(kMcTag, v.w));
+}
+// h_out of a chunk once every lane sees all four of its words published;
+// false after the spin limit (then the header's error word is set)
+__device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, v4f& v) {
+  const uint64_t* p = w + threadIdx.x * 4;
+  for (uint32_t spins = 0;; ++spins) {
+    const uint64_t a = ld_u64(p + 0), b = ld_u64(p + 1), c = ld_u64(p + 2), d = ld_u64(p + 3);
+    const bool ok = word_tag(a) == kMcTag && word_tag(b) == kMcTag && word_tag(c) == kMcTag &&
+                    word_tag(d) == kMcTag;
+    if (__ballot(!ok) == 0ull) {
+      v = v4f{word_val(a), word_val(b), word_val(c), word_val(d)};
+      return true;
+    }
+    if (spins > kSpinLimit) {
+      if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+__global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
+  static_assert(S <= 32, "step masks are 32-bit");
+  __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
+  const int64_t ngroups = (a.rows + TL::RPW - 1) / TL::RPW;
+  int64_t g;
+  int c;
+  tile_of_block<true>(ngroups, a.ntiles, g, c);
+  const int64_t r = g * TL::RPW + TL::lrow();
+  const bool valid = r < a.rows;  // Tile4: rows past the end compute on zeros, store nothing
+  McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, valid ? r : 0);
+  const int64_t j0 = (int64_t)c * S;
+  const int n = (int)min((int64_t)S, a.T - j0);
+
+  // sequence starts and ends in the chunk (before the loads: nothing is live yet)
+  uint32_t firstm, lastm;
+  wk.masks(j0, n, firstm, lastm);
+
+  // ---- load the chunk: transition operand X (R layout) and injection Y (D
+  // layout); backward also the forward state one processing step on, in R
+  // layout (h_prev^T in D layout, for dA = lam h_prev^T). Steps past the row's
+  // end (s >= n) hold zeros and are computed but never stored or published.
+  v4f X[S], Y[S], H[BWD ? S : 1];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    X[s] = mc_zero();
+    Y[s] = mc_zero();
+    if constexpr (BWD) H[s] = mc_zero();
+    if (s < n && valid) {
+      const int64_t j = j0 + s;
+      const int64_t t = wk.phys(j);
+      Y[s] = wk.sh.ldB_D(wk.blkB(a.B, t));
+      if constexpr (!BWD) {
+        X[s] = wk.sh.ldA_R(wk.blkA(a.A, t));
+      } else {
+        if (j > 0) X[s] = wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j - 1)));  // (A one processing step back)^T
+        if (j + 1 < a.T) H[s] = wk.sh.ldB_R(wk.blkB(a.hs, wk.phys(j + 1)));
+      }
+    }
+  }
+  wait_stage_loads();
+  // Sequence boundaries, folded into the registers so that the step loops
+  // below hold no loads (a load in them would make every step wait for the
+  // stores before it): forward, a first step's value A h0 + B; backward, the
+  // h_prev of a sequence's forward-first step is h0.
+  if (a.h0 && (BWD ? lastm : firstm)) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (((BWD ? lastm : firstm) >> s) & 1u) {
+        const int sk = wk.seg_of(j0 + s);
+        if constexpr (!BWD) {
+          const v4f h0D = valid ? wk.sh.ldB_D(wk.h0p(sk)) : mc_zero();
+          Y[s] = TL::mm(X[s], h0D, Y[s]);
+        } else {
+          H[s] = valid ? wk.sh.ldB_R(wk.h0p(sk)) : mc_zero();
+        }
+      }
+    }
+    wait_stage_loads();
+  } else if (BWD && lastm) {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if ((lastm >> s) & 1u) H[s] = mc_zero();
+  }
+
+  // ---- chunk summary (a sequence's first step is hard: P = 0, Q = its value)
+  const bool hard = firstm != 0u, first0 = (firstm & 1u) != 0u;
+  v4f P = tile_ident<TL>(), Q = mc_zero();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool f = (firstm >> s) & 1u;
+    const v4f Pn = TL::mm(X[s], P, mc_zero()), Qn = TL::mm(X[s], Q, Y[s]);
+    P = f ? mc_zero() : Pn;
+    Q = f ? Y[s] : Qn;
+  }
+
+  // ---- carry-in from the chunk before, h_out for the chunk after
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
+  const int64_t me = g * a.ntiles + c;
+  const bool publish = c + 1 < a.ntiles;
+  if (publish && hard) mc_publish(pub + me * 256, Q);  // h_out = Q whatever the carry-in
+  const v4f PR = (publish && !hard) ? TL::d_to_r(s_t, P) : mc_zero();  // off the chain
+  v4f hin = mc_zero();
+  if (!first0) {
+    if (!mc_wait(pub + (me - 1) * 256, hdr, hin)) hin = mc_zero();
+  }
+  if (publish && !hard) mc_publish(pub + me * 256, TL::mm(PR, hin, Q));
+
+  // ---- apply from the registers
+  v4f h = hin;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool first = (firstm >> s) & 1u;
+    const v4f hn = TL::mm(X[s], h, Y[s]);
+    h = first ? Y[s] : hn;  // h holds lam in the backward
+    if constexpr (BWD) {
+      // dA_t = lam h_prev^T (the transpose is a whole-wave operation)
+      const v4f dA = TL::mm(TL::d_to_r(s_t, h), H[s], mc_zero());
+      if (s < n && valid) {
+        const int64_t j = j0 + s;
+        const int64_t t = wk.phys(j);
+        wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
+        wk.sh.stA_D(wk.blkA(a.out1, t), dA);
+      }
+      if (((lastm >> s) & 1u) && a.dh0 && s < n) {
+        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
+        const int64_t j = j0 + s;
+        const v4f Ad = valid ? wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j))) : mc_zero();
+        const v4f d = TL::mm(Ad, h, mc_zero());
+        if (valid) wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), d);
+      }
+    } else {
+      if (s < n && valid) wk.sh.stB_D(wk.blkB(a.out0, wk.phys(j0 + s)), h);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------
+// Steps per chunk, from timing 8 / 16 / 32 at (16, 16), 512 rows, T = 4096:
+// the forward is fastest with 32 (half the chained hops and published words
+// of 16, despite one wave per SIMD), the backward ties at 16 and 32 and takes
+// 16 (32 spills).
+constexpr int kChunkFwd = 32, kChunkBwd = 16;
+
+static bool tile4_shape(int k, int v) { return k <= 4 && v <= 4; }
+
+int64_t matrix_core_chunks(int64_t T, bool bwd) {
+  const int64_t S = bwd ? kChunkBwd : kChunkFwd;
+  return (T + S - 1) / S;
+}
+
+// row groups of a call: 16 rows per wave on Tile4, one on Tile16
+static int64_t mc_groups(int64_t rows, int k, int v) { return tile4_shape(k, v) ? (rows + 15) / 16 : rows; }
+
+size_t matrix_core_ws_bytes(int64_t rows, int64_t T, int k, int v) {
+  const int64_t n = std::max(matrix_core_chunks(T, false), matrix_core_chunks(T, true));
+  return ws_desc_offset() + (size_t)(mc_groups(rows, k, v) * n) * kMcPubBytes;
+}
+
+template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+static hipError_t launch_mc_dir(const MatArgs& a0, hipStream_t st) {
+  MatArgs a = a0;
+  a.ntiles = (int32_t)((a.T + S - 1) / S);
+  const int64_t n = mc_groups(a.rows, a.k, a.v) * a.ntiles;
+  // fresh words (and header) for this call: a zero tag = not published
+  const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kMcPubBytes, st);
+  if (z != hipSuccess) return z;
+  hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class TL, bool FULL>
+static hipError_t launch_mc_shape(const MatArgs& a, bool bwd, hipStream_t st) {
+  constexpr int SF = kChunkFwd, SB = kChunkBwd;
+  const bool rev = a.rev != 0, vl = a.cu != nullptr;
+  if (bwd) {
+    if (rev) return vl ? launch_mc_dir<TL, FULL, true, true, true, SB>(a, st) : launch_mc_dir<TL, FULL, true, true, false, SB>(a, st);
+    return vl ? launch_mc_dir<TL, FULL, true, false, true, SB>(a, st) : launch_mc_dir<TL, FULL, true, false, false, SB>(a, st);
+  }
+  if (rev) return vl ? launch_mc_dir<TL, FULL, false, true, true, SF>(a, st) : launch_mc_dir<TL, FULL, false, true, false, SF>(a, st);
+  return vl ? launch_mc_dir<TL, FULL, false, false, true, SF>(a, st) : launch_mc_dir<TL, FULL, false, false, false, SF>(a, st);
+}
+
+hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st) {
+  if (a.k < 1 || a.k > 16 || a.v < 1 || a.v > 16) return hipErrorInvalidValue;
+  if (tile4_shape(a.k, a.v)) {
+    if (a.k == 4 && a.v == 4) return launch_mc_shape<Tile4, true>(a, bwd, st);
+    return launch_mc_shape<Tile4, false>(a, bwd, st);
+  }
+  if (a.k == 16 && a.v == 16) return launch_mc_shape<Tile16, true>(a, bwd, st);
+  return launch_mc_shape<Tile16, false>(a, bwd, st);
+}
+
+}  // namespace mscan

@@ -47,6 +47,32 @@ def test_opcheck_matrix_scan(m):
     torch.library.opcheck(torch.ops.mscan.matrix_scan.default, (A, B, None, None, False))
 
 
+def test_opcheck_matrix_scan_matrix_cores(m):
+    """The custom op over the matrix-core kernels: (8, 4) with h0 and segments."""
+    A = (_r(3, 300, 8, 8, seed=21) * 0.3).requires_grad_()
+    B = _r(3, 300, 8, 4, seed=22).requires_grad_()
+    cu = torch.tensor([0, 100, 100, 300], dtype=torch.int32, device=DEV)
+    h0 = _r(3, 3, 8, 4, seed=23).requires_grad_()
+    torch.library.opcheck(torch.ops.mscan.matrix_scan.default, (A, B, h0, cu, True))
+
+
+def test_matrix_scan_16x16_gradients_match_oracle(m, oracle_lib):
+    """Autograd through mscan::matrix_scan at (16, 16) against the oracle's adjoint."""
+    r = np.random.default_rng(24)
+    A = (r.standard_normal((2, 400, 16, 16)) * 0.2).astype(np.float32)
+    B = r.standard_normal((2, 400, 16, 16)).astype(np.float32)
+    h0 = r.standard_normal((1, 2, 16, 16)).astype(np.float32)
+    dy = r.standard_normal((2, 400, 16, 16)).astype(np.float32)
+    At, Bt, h0t = (torch.from_numpy(a).to(DEV).requires_grad_() for a in (A, B, h0))
+    h = m.matrix_scan(At, Bt, h0=h0t, reverse=True)
+    (h * torch.from_numpy(dy).to(DEV)).sum().backward()
+    href = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, reverse=True)
+    rA, rB, rh0 = oracle_lib.matrix_affine_scan_bwd(A, href, dy, h0=h0, reverse=True)
+    for got, ref in ((At.grad, rA), (Bt.grad, rB), (h0t.grad, rh0)):
+        err = np.max(np.abs(got.cpu().double().numpy() - ref) / (1 + np.abs(ref)))
+        assert err <= 1e-4, err
+
+
 def test_compile_fullgraph_training_step(m):
     """A small 'mixer' step using all three ops compiles into one graph (no break)
     and gives the eager values and gradients."""

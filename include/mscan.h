@@ -45,7 +45,7 @@
  *              dtype).
  *  Workspace.  Calls that split a row into several tiles chain them through a
  *              small device workspace of mscan_workspace_bytes() bytes (about
- *              0.2% of the inputs). The call itself clears the part it uses,
+ *              0.2% of the inputs; 2-4% for the matrix-core shapes). The call itself clears the part it uses,
  *              with a small fill kernel on `stream` before the scan kernel, so
  *              the contents between calls do not matter. Calls that overlap in
  *              time (different streams) must not share a workspace.
@@ -208,9 +208,11 @@ MSCAN_API mscan_status scan_log_bwd_gated(const mscan_problem* prob, int gate /*
  * kernel envelope, k and v each in {1, 2, 4, 8, 16}, any T >= 1; any other
  * (k, v) returns MSCAN_ERR_UNSUPPORTED. (1, 1) is the scalar scan; (2,1),
  * (2,2), (4,1) and (4,4) run on the vector ALUs; every other pair runs its
- * products on the matrix cores, zero-padded to 16 x 16, in IEEE fp32 (the
- * page's precision guard at k = 16), and always needs the workspace
- * (mscan_workspace_bytes).
+ * products on the matrix cores, zero-padded to 4 x 4 (k, v <= 4) or 16 x 16,
+ * with fp32 operands and fp32 accumulation (the page's precision guard at
+ * k = 16), and always needs the workspace (mscan_workspace_bytes: 2 KiB per
+ * chunk of 16 or 32 steps and row, or per 16 rows when k, v <= 4). Its
+ * results are bit-reproducible from call to call.
  *   A : fp32 [rows][T][k][k]; B : fp32 [rows][T][k][v];
  *   h0 : fp32 [nseg][rows][k][v] or NULL; h : fp32 [rows][T][k][v], written. */
 MSCAN_API mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

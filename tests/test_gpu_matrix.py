@@ -115,6 +115,19 @@ def test_matrix16_many_rows(m, oracle_lib, reverse):
     run(m, oracle_lib, A, B, dy, h0=h0, cu=cu, reverse=reverse)
 
 
+@pytest.mark.parametrize("kv", [(2, 4), (4, 2), (1, 4)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_core_4x4_tiles_row_groups(m, oracle_lib, kv, reverse):
+    """4x4 matrix-core tiles hold 16 rows per wave: 37 rows (three groups, the
+    last with 5 rows), chunks across segments, h0 and dh0 per row."""
+    k, v = kv
+    r = np.random.default_rng(1200 + 10 * k + v + reverse)
+    A, B, dy = _random_case(r, k, v, 37, 777)
+    cu = np.array([0, 5, 300, 300, 777], dtype=np.int32)
+    h0 = r.standard_normal((4, 37, k, v)).astype(np.float32)
+    run(m, oracle_lib, A, B, dy, h0=h0, cu=cu, reverse=reverse)
+
+
 def test_matrix16_no_h0_no_dh0(m, oracle_lib):
     r = np.random.default_rng(900)
     A, B, dy = _random_case(r, 16, 16, 2, 300)

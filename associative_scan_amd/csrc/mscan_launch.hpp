@@ -74,7 +74,7 @@ hipError_t launch_matrix(const MatArgs& a, int k, int v, bool bwd, hipStream_t s
 // Matrix-core kernels, blocks zero-padded to 4 x 4 (k, v <= 4) or 16 x 16:
 // chunks per row, the workspace a call needs (always), and the launch
 // (a.k, a.v in 1..16).
-int64_t matrix_core_chunks(int64_t T, bool bwd);
+int64_t matrix_core_chunks(int64_t T, bool bwd, int k, int v);
 size_t matrix_core_ws_bytes(int64_t rows, int64_t T, int k, int v);
 hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st);
 

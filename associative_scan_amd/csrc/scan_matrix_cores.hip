@@ -201,6 +201,7 @@ struct McWalk {
   __device__ __forceinline__ void masks(int64_t j0, int n, uint32_t& firstm, uint32_t& lastm) {
     firstm = 0u;
     lastm = 0u;
+    if (n <= 0) return;
     if constexpr (VARLEN) {
       seq.init(a.cu, a.nseg, phys(j0));
       for (int s = 0; s < n; ++s) {
@@ -404,6 +405,207 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 4 x 4 blocks, one row per wave: blocks in time
+// ---------------------------------------------------------------------------
+// For k, v <= 4 a wave owns 16 S consecutive steps of ONE row: lane group b
+// (lanes 4b .. 4b+3) owns steps b S .. b S + S - 1 of the wave's span, so the
+// wave's loads stay inside one contiguous window of the row. Each group walks
+// its S steps for its block summary (sixteen 4x4x4 products per MFMA), the
+// groups combine their summaries by an inclusive scan over groups (4 levels,
+// operands moved 4, 8, 16, 32 lanes up), every group applies the result to
+// the carry-in of the wave to get the state after it, and group b starts from
+// group b-1's. Waves chain as above, through 16 published words (a 4x4 h_out).
+// Control flow stays uniform across the wave around every MFMA: a step where
+// only some groups start or end a sequence is computed for all groups and
+// selected per lane.
+constexpr size_t kSegPubBytes = 16 * 8;  // one published 4 x 4 h_out
+
+// lane (b, q) publishes / reads column q of a 4 x 4 block (word 4 i + j = h[i][j])
+__device__ __forceinline__ void seg_publish(uint64_t* w, v4f v) {
+  const int q = (int)(threadIdx.x & 3);
+  st_u64(w + 0 * 4 + q, pack_word(kMcTag, v.x));
+  st_u64(w + 1 * 4 + q, pack_word(kMcTag, v.y));
+  st_u64(w + 2 * 4 + q, pack_word(kMcTag, v.z));
+  st_u64(w + 3 * 4 + q, pack_word(kMcTag, v.w));
+}
+__device__ __forceinline__ bool seg_wait(const uint64_t* w, uint32_t* hdr, v4f& v) {
+  const int q = (int)(threadIdx.x & 3);
+  for (uint32_t spins = 0;; ++spins) {
+    const uint64_t a = ld_u64(w + 0 * 4 + q), b = ld_u64(w + 1 * 4 + q), c = ld_u64(w + 2 * 4 + q),
+                   d = ld_u64(w + 3 * 4 + q);
+    const bool ok = word_tag(a) == kMcTag && word_tag(b) == kMcTag && word_tag(c) == kMcTag &&
+                    word_tag(d) == kMcTag;
+    if (__ballot(!ok) == 0ull) {
+      v = v4f{word_val(a), word_val(b), word_val(c), word_val(d)};
+      return true;
+    }
+    if (spins > kSpinLimit) {
+      if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+__device__ __forceinline__ v4f shfl_up4(v4f x, int d) {
+  return v4f{__shfl_up(x.x, d, 64), __shfl_up(x.y, d, 64), __shfl_up(x.z, d, 64), __shfl_up(x.w, d, 64)};
+}
+__device__ __forceinline__ v4f sel4(bool c, v4f a, v4f b) {
+  return v4f{c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w};
+}
+
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+__global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
+  static_assert(S <= 32, "step masks are 32-bit");
+  using TL = Tile4;
+  __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
+  int64_t r;
+  int c;
+  tile_of_block<true>(a.rows, a.ntiles, r, c);
+  McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
+  const int b = TL::lrow();
+  const int64_t jb = (int64_t)c * (16 * S) + (int64_t)b * S;  // this group's first processing step
+  const int nb = (int)max((int64_t)0, min((int64_t)S, a.T - jb));
+
+  uint32_t firstm, lastm;  // per group
+  wk.masks(jb, nb, firstm, lastm);
+
+  // ---- load the group's S steps (as in k_mc_scan, per lane group)
+  v4f X[S], Y[S], H[BWD ? S : 1];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    X[s] = mc_zero();
+    Y[s] = mc_zero();
+    if constexpr (BWD) H[s] = mc_zero();
+    if (s < nb) {
+      const int64_t j = jb + s;
+      const int64_t t = wk.phys(j);
+      // FULL: every block is read as rows (one 16-byte load per lane) and
+      // turned into the layout it is used in below
+      Y[s] = FULL ? wk.sh.ldB_R(wk.blkB(a.B, t)) : wk.sh.ldB_D(wk.blkB(a.B, t));
+      if constexpr (!BWD) {
+        X[s] = wk.sh.ldA_R(wk.blkA(a.A, t));
+      } else {
+        if (j > 0) X[s] = FULL ? wk.sh.ldA_R(wk.blkA(a.A, wk.phys(j - 1))) : wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j - 1)));
+        if (j + 1 < a.T) H[s] = wk.sh.ldB_R(wk.blkB(a.hs, wk.phys(j + 1)));
+      }
+    }
+  }
+  wait_stage_loads();
+  if constexpr (FULL) {
+    // rows -> D layout (Y), and A -> A^T in R layout (the backward's X): the
+    // same per-group transpose through LDS
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      Y[s] = TL::d_to_r(s_t, Y[s]);
+      if constexpr (BWD) X[s] = TL::d_to_r(s_t, X[s]);
+    }
+  }
+  // sequence boundaries folded into the registers (forward: A h0 + B at a
+  // first step; backward: h_prev = h0 or 0 at a forward-first step)
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool f = BWD ? ((lastm >> s) & 1u) : ((firstm >> s) & 1u);
+    if (__ballot(f) == 0ull) continue;
+    v4f h0v = mc_zero();
+    if (f && a.h0) {
+      const int sk = wk.seg_of(jb + s);
+      h0v = BWD ? wk.sh.ldB_R(wk.h0p(sk)) : wk.sh.ldB_D(wk.h0p(sk));
+    }
+    wait_stage_loads();
+    if constexpr (!BWD) {
+      const v4f yf = TL::mm(X[s], h0v, Y[s]);
+      if (f && a.h0) Y[s] = yf;
+    } else {
+      if (f) H[s] = h0v;
+    }
+  }
+
+  // ---- group summary (a sequence's first step is hard)
+  v4f P = tile_ident<TL>(), Q = mc_zero();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool f = (firstm >> s) & 1u;
+    const v4f Pn = TL::mm(X[s], P, mc_zero()), Qn = TL::mm(X[s], Q, Y[s]);
+    P = sel4(f, mc_zero(), Pn);
+    Q = sel4(f, Y[s], Qn);
+  }
+
+  // ---- inclusive scan over the 16 groups: group b <- (group b) after (groups before)
+  bool hard = firstm != 0u;
+#pragma unroll
+  for (int k = 1; k < 16; k <<= 1) {
+    const v4f Pp = shfl_up4(P, 4 * k), Qp = shfl_up4(Q, 4 * k);
+    const bool hp = __shfl_up((int)hard, 4 * k, 64) != 0;
+    const v4f PR = TL::d_to_r(s_t, P);
+    const v4f Pn = TL::mm(PR, Pp, mc_zero()), Qn = TL::mm(PR, Qp, Q);
+    const bool take = b >= k && !hard;
+    P = sel4(take, Pn, P);
+    Q = sel4(take, Qn, Q);
+    hard = hard || (b >= k && hp);
+  }
+  // the wave is hard if group 15's inclusive summary is; it needs no carry-in
+  // if its first step starts a sequence
+  const bool whard = __shfl((int)hard, 60, 64) != 0;
+  const bool first0 = __shfl((int)(firstm & 1u), 0, 64) != 0;
+
+  // ---- carry-in from the wave before, h_out for the wave after
+  uint32_t* hdr = (uint32_t*)a.ws;
+  uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
+  const int64_t me = r * a.ntiles + c;
+  const bool publish = c + 1 < a.ntiles;
+  if (publish && whard && b == 15) seg_publish(pub + me * 16, Q);  // group 15's Q is the wave's h_out
+  const v4f PR = TL::d_to_r(s_t, P);
+  v4f hin = mc_zero();
+  if (!first0) {
+    if (!seg_wait(pub + (me - 1) * 16, hdr, hin)) hin = mc_zero();
+  }
+  // out_b = state after group b
+  v4f out = TL::mm(PR, hin, Q);
+  out = sel4(hard, Q, out);
+  if (publish && !whard && b == 15) seg_publish(pub + me * 16, out);
+  v4f h = shfl_up4(out, 4);
+  if (b == 0) h = hin;
+
+  // ---- apply from the registers
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool first = (firstm >> s) & 1u;
+    const v4f hn = TL::mm(X[s], h, Y[s]);
+    h = sel4(first, Y[s], hn);  // h holds lam in the backward
+    if constexpr (BWD) {
+      const v4f lamR = TL::d_to_r(s_t, h);
+      const v4f dA = TL::mm(lamR, H[s], mc_zero());
+      const v4f dAR = FULL ? TL::d_to_r(s_t, dA) : dA;  // FULL: stored as rows
+      if (s < nb) {
+        const int64_t t = wk.phys(jb + s);
+        if constexpr (FULL) {
+          *(v4f*)(wk.blkB(a.out0, t) + TL::dc() * 4) = lamR;  // dB = lam
+          *(v4f*)(wk.blkA(a.out1, t) + TL::dc() * 4) = dAR;
+        } else {
+          wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
+          wk.sh.stA_D(wk.blkA(a.out1, t), dA);
+        }
+      }
+      const bool l = ((lastm >> s) & 1u) && s < nb;
+      if (a.dh0 && __ballot(l) != 0ull) {
+        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
+        const v4f Ad = l ? wk.sh.ldA_D(wk.blkA(a.A, wk.phys(jb + s))) : mc_zero();
+        wait_stage_loads();
+        const v4f d = TL::mm(Ad, h, mc_zero());
+        if (l) wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(jb + s) * a.rows + r) * wk.sh.nb(), d);
+      }
+    } else {
+      if constexpr (FULL) {
+        const v4f hR = TL::d_to_r(s_t, h);
+        if (s < nb) *(v4f*)(wk.blkB(a.out0, wk.phys(jb + s)) + TL::dc() * 4) = hR;
+      } else {
+        if (s < nb) wk.sh.stB_D(wk.blkB(a.out0, wk.phys(jb + s)), h);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
 // Steps per chunk, from timing 8 / 16 / 32 at (16, 16), 512 rows, T = 4096:
@@ -411,31 +613,41 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
 // of 16, despite one wave per SIMD), the backward ties at 16 and 32 and takes
 // 16 (32 spills).
 constexpr int kChunkFwd = 32, kChunkBwd = 16;
+// Steps per lane group of the 4 x 4 row-segment kernel (a wave spans 16 x that).
+constexpr int kSegSteps = 8;
 
 static bool tile4_shape(int k, int v) { return k <= 4 && v <= 4; }
 
-int64_t matrix_core_chunks(int64_t T, bool bwd) {
-  const int64_t S = bwd ? kChunkBwd : kChunkFwd;
+int64_t matrix_core_chunks(int64_t T, bool bwd, int k, int v) {
+  const int64_t S = tile4_shape(k, v) ? 16 * kSegSteps : (bwd ? kChunkBwd : kChunkFwd);
   return (T + S - 1) / S;
 }
 
-// row groups of a call: 16 rows per wave on Tile4, one on Tile16
-static int64_t mc_groups(int64_t rows, int k, int v) { return tile4_shape(k, v) ? (rows + 15) / 16 : rows; }
-
 size_t matrix_core_ws_bytes(int64_t rows, int64_t T, int k, int v) {
-  const int64_t n = std::max(matrix_core_chunks(T, false), matrix_core_chunks(T, true));
-  return ws_desc_offset() + (size_t)(mc_groups(rows, k, v) * n) * kMcPubBytes;
+  const int64_t n = std::max(matrix_core_chunks(T, false, k, v), matrix_core_chunks(T, true, k, v));
+  return ws_desc_offset() + (size_t)(rows * n) * (tile4_shape(k, v) ? kSegPubBytes : kMcPubBytes);
 }
 
 template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
 static hipError_t launch_mc_dir(const MatArgs& a0, hipStream_t st) {
   MatArgs a = a0;
   a.ntiles = (int32_t)((a.T + S - 1) / S);
-  const int64_t n = mc_groups(a.rows, a.k, a.v) * a.ntiles;
+  const int64_t n = a.rows * a.ntiles;
   // fresh words (and header) for this call: a zero tag = not published
   const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kMcPubBytes, st);
   if (z != hipSuccess) return z;
   hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+static hipError_t launch_seg_dir(const MatArgs& a0, hipStream_t st) {
+  MatArgs a = a0;
+  a.ntiles = (int32_t)((a.T + 16 * S - 1) / (16 * S));
+  const int64_t n = a.rows * a.ntiles;
+  const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kSegPubBytes, st);
+  if (z != hipSuccess) return z;
+  hipLaunchKernelGGL((k_mc_rowseg<FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -451,11 +663,23 @@ static hipError_t launch_mc_shape(const MatArgs& a, bool bwd, hipStream_t st) {
   return vl ? launch_mc_dir<TL, FULL, false, false, true, SF>(a, st) : launch_mc_dir<TL, FULL, false, false, false, SF>(a, st);
 }
 
+template <bool FULL>
+static hipError_t launch_seg_shape(const MatArgs& a, bool bwd, hipStream_t st) {
+  constexpr int S = kSegSteps;
+  const bool rev = a.rev != 0, vl = a.cu != nullptr;
+  if (bwd) {
+    if (rev) return vl ? launch_seg_dir<FULL, true, true, true, S>(a, st) : launch_seg_dir<FULL, true, true, false, S>(a, st);
+    return vl ? launch_seg_dir<FULL, true, false, true, S>(a, st) : launch_seg_dir<FULL, true, false, false, S>(a, st);
+  }
+  if (rev) return vl ? launch_seg_dir<FULL, false, true, true, S>(a, st) : launch_seg_dir<FULL, false, true, false, S>(a, st);
+  return vl ? launch_seg_dir<FULL, false, false, true, S>(a, st) : launch_seg_dir<FULL, false, false, false, S>(a, st);
+}
+
 hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st) {
   if (a.k < 1 || a.k > 16 || a.v < 1 || a.v > 16) return hipErrorInvalidValue;
   if (tile4_shape(a.k, a.v)) {
-    if (a.k == 4 && a.v == 4) return launch_mc_shape<Tile4, true>(a, bwd, st);
-    return launch_mc_shape<Tile4, false>(a, bwd, st);
+    if (a.k == 4 && a.v == 4) return launch_seg_shape<true>(a, bwd, st);
+    return launch_seg_shape<false>(a, bwd, st);
   }
   if (a.k == 16 && a.v == 16) return launch_mc_shape<Tile16, true>(a, bwd, st);
   return launch_mc_shape<Tile16, false>(a, bwd, st);

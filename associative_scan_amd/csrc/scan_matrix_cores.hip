@@ -9,12 +9,12 @@
 // IEEE guard asks for at k = 16). Two register tiles:
 //   Tile16: one 16 x 16 block per wave (k or v above 4), products on
 //           v_mfma_f32_16x16x4_f32;
-//   Tile4 : sixteen 4 x 4 blocks per wave, one per row of a group of 16 rows
-//           (k, v <= 4), products on v_mfma_f32_4x4x1_16b_f32. Its per-row
-//           accesses are short (64 bytes of A per step), and on (4, 4) and
-//           (2, 1) it measured 1.2-6x slower than the VALU kernels, which keep
-//           (2, 1), (2, 2), (4, 1) and (4, 4); Tile4 serves the other shapes
-//           with k, v <= 4 (4x less padding than Tile16).
+//   Tile4 : sixteen 4 x 4 blocks per wave (k, v <= 4), products on
+//           v_mfma_f32_4x4x1_16b_f32, used by the row-segment kernel below
+//           (one row per wave, the 16 blocks in time).
+// Reading and writing the 16 x 16 blocks as rows with an LDS transpose per
+// block (as the 4 x 4 kernel does) measured no faster forward and 39% slower
+// backward, so Tile16 keeps its column-wise dword accesses.
 // Blocks smaller than the tile are zero-padded in registers: rows and columns
 // past k (or v) load as 0 and are never stored, and a zero-padded A and B keep
 // the padding of h, the adjoint and the chunk summaries at 0, so the padded
@@ -30,8 +30,9 @@
 // next step's operand without moving data between lanes; the R layout of X is
 // the D layout of X^T.
 //
-// One kernel per call: a wave owns S steps of one row (Tile16) or of 16 rows
-// (Tile4), carries chained from chunk to chunk through the workspace (below).
+// One kernel per call, carries chained from wave to wave through the
+// workspace: k_mc_scan (Tile16) gives a wave S steps of one row; k_mc_rowseg
+// (Tile4) gives a wave 16 S steps of one row, S per group of 4 lanes.
 // Forward element (X, Y) = (A_t, B_t); backward element = (A of the previous
 // step in processing order, transposed; dy_t). A sequence's first step in
 // processing order is hard: forward h = A h0 + B, backward lam = dy.

@@ -184,6 +184,8 @@ MSCAN_API mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_
  * the backward returns dz = dg * f'(z) in place of dg (resp. dlog_a):
  *   sigmoid      : dz = dg * g (1 - g)
  *   -softplus    : dz = dlog_a * (-sigmoid(z))
+ * A reset in logit form is z = -inf for the sigmoid gate (g = 0) and
+ * z = +inf for the -softplus gate (log a = -inf).
  * Arguments, layouts, workspace and errors are those of scan_fwd / scan_bwd /
  * scan_log_fwd / scan_log_bwd; z has the gate's type (fp32 or bf16 for the
  * linear scan, fp32 for the log-space scan). A gate kind other than the one

@@ -187,8 +187,8 @@ MSCAN_API mscan_status scan_log_bwd(const mscan_problem* prob, const float* log_
  * A reset in logit form is z = -inf for the sigmoid gate (g = 0) and
  * z = +inf for the -softplus gate (log a = -inf).
  * Arguments, layouts, workspace and errors are those of scan_fwd / scan_bwd /
- * scan_log_fwd / scan_log_bwd; z has the gate's type (fp32 or bf16 for the
- * linear scan, fp32 for the log-space scan). A gate kind other than the one
+ * scan_log_fwd / scan_log_bwd; z has the gate's type (fp32, bf16 or fp16
+ * for the linear scan, fp32 for the log-space scan). A gate kind other than the one
  * listed for the entry point returns MSCAN_ERR_UNSUPPORTED.                 */
 MSCAN_API mscan_status scan_fwd_gated(const mscan_problem* prob, int in_dtype, int gate /* MSCAN_GATE_SIGMOID */,
                             const void* z, const void* x, const float* h0, float* h, void* ws,

@@ -52,9 +52,12 @@ size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
   return mscan::ws_desc_offset() + (size_t)p->rows * (size_t)nt * (size_t)words * sizeof(uint64_t);
 }
 
+// A launch's grid counts work-items in 32 bits: with up to 256 threads per
+// workgroup, at most 2^24 - 1 workgroups. (Every problem whose arrays fit in
+// HBM stays far below that.)
 mscan_status check_grid(const mscan_problem* p, int64_t tiles_per_row) {
   const double blocks = (double)p->rows * (double)tiles_per_row;
-  if (blocks > 4294967295.0) return MSCAN_ERR_UNSUPPORTED;  // 32-bit tile ids / grid size
+  if (blocks * 256.0 > 4294967295.0) return MSCAN_ERR_UNSUPPORTED;
   return MSCAN_OK;
 }
 

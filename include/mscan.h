@@ -52,9 +52,10 @@
  *  Errors.     Arguments are validated on the host before any HIP call:
  *              MSCAN_ERR_INVALID (null required pointer, bad sizes, misaligned
  *              pointer, nseg inconsistent with cu_seqlens), MSCAN_ERR_UNSUPPORTED
- *              (dtype or matrix shape outside the supported envelope; never
- *              silently masked, as the minGRU page's kernel envelope raises
- *              rather than miscomputes), MSCAN_ERR_WORKSPACE (ws_bytes too
+ *              (dtype or matrix shape outside the supported envelope, or more
+ *              than 2^24 - 1 tiles in one call; never silently masked, as the
+ *              minGRU page's kernel envelope raises rather than
+ *              miscomputes), MSCAN_ERR_WORKSPACE (ws_bytes too
  *              small), MSCAN_ERR_HIP (a launch failed; mscan_last_hip_error()
  *              gives the HIP error text). Nothing is enqueued on any error.
  *              There is no fallback path.

@@ -185,3 +185,16 @@ def test_matrix_outside_envelope_unsupported(m, kv):
     assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), k, v, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, None) == 2
     assert m.lib.matrix_affine_scan_bwd(ctypes.byref(p), k, v, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
                                         1 << 20, None) == 2
+
+
+def test_grid_beyond_one_launch_is_unsupported(m):
+    """rows x tiles beyond what one launch can address is refused on the host
+    (never launched): 2^20 rows of 2^16 elements are 2^24 tiles of 4096."""
+    p = _prob(m, rows=1 << 20, T=1 << 16)
+    assert m.lib.scan_fwd(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == 2
+    assert m.lib.matrix_affine_scan_fwd(ctypes.byref(_prob(m, rows=1 << 22, T=1 << 16)), 16, 16, FAKE, FAKE, None,
+                                        FAKE, FAKE, 1 << 40, None) == 2
+    # one tile fewer per row is accepted as far as the grid goes (then needs its workspace)
+    q = _prob(m, rows=(1 << 20) - 1, T=1 << 16)
+    assert m.lib.scan_fwd(ctypes.byref(q), 0, FAKE, FAKE, None, FAKE, None, 0, None) == 3
+

@@ -547,13 +547,13 @@ def test_matrix_k1_is_scalar(oracle_lib):
         assert np.array_equal(hm[..., 0, 0], hs)
 
 
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (2, 3)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (2, 3), (16, 16), (8, 2), (1, 16), (16, 1)])
 def test_matrix_brute_force_products(oracle_lib, kv):
     """h_t = (A_t...A_s) h0 + sum_u (A_t...A_{u+1}) B_u with numpy matmul, every segment."""
     k, v = kv
-    r = _rng(15 + k)
+    r = _rng(15 + k + 100 * v)
     T = 20
-    A = r.standard_normal((2, T, k, k)) * 0.6
+    A = r.standard_normal((2, T, k, k)) * (0.6 if k <= 4 else 1.2 / np.sqrt(k))
     B = r.standard_normal((2, T, k, v))
     cu = np.array([0, 7, 20], dtype=np.int32)
     h0 = r.standard_normal((2, 2, k, v))
@@ -610,12 +610,12 @@ def test_matrix_reset_gives_B(oracle_lib):
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-@pytest.mark.parametrize("kv", [(2, 1), (4, 4)])
+@pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16), (8, 2), (1, 4)])
 def test_matrix_adjoint_dot_product(oracle_lib, kv, reverse):
     k, v = kv
-    r = _rng(20 + k)
+    r = _rng(20 + k + 100 * v)
     T = 60
-    A = r.standard_normal((3, T, k, k)) * 0.5
+    A = r.standard_normal((3, T, k, k)) * (0.5 if k <= 4 else 1.0 / np.sqrt(k))
     B = r.standard_normal((3, T, k, v))
     cu = np.array([0, 13, 13, 60], dtype=np.int32)
     h0 = r.standard_normal((3, 3, k, v))
@@ -636,6 +636,38 @@ def test_matrix_adjoint_dot_product(oracle_lib, kv, reverse):
     lhs = np.sum(dy * hd)
     rhs = np.sum(dA * Ad) + np.sum(dB * Bd) + np.sum(dh0 * h0d)
     assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
+
+
+def test_matrix_block_diagonal_splits(oracle_lib):
+    """A block-diagonal 16x16 transition (four 4x4 blocks) acting on a state
+    whose rows split the same way is four independent 4x4 scans; v columns of
+    the state are v independent scans with the same A (forward and adjoint)."""
+    r = _rng(77)
+    T = 40
+    blocks = r.standard_normal((2, T, 4, 4, 4)) * 0.5  # [row, t, block, 4, 4]
+    A = np.zeros((2, T, 16, 16))
+    for b in range(4):
+        A[:, :, 4 * b:4 * b + 4, 4 * b:4 * b + 4] = blocks[:, :, b]
+    B = r.standard_normal((2, T, 16, 3))
+    cu = np.array([0, 15, 40], dtype=np.int32)
+    h0 = r.standard_normal((2, 2, 16, 3))
+    dy = r.standard_normal(B.shape)
+    for reverse in (False, True):
+        h = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, cu_seqlens=cu, reverse=reverse)
+        dA, dB, dh0 = oracle_lib.matrix_affine_scan_bwd(A, h, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+        for b in range(4):
+            sl = slice(4 * b, 4 * b + 4)
+            hb = oracle_lib.matrix_affine_scan_fwd(blocks[:, :, b], B[:, :, sl], h0=h0[:, :, sl], cu_seqlens=cu,
+                                                   reverse=reverse)
+            np.testing.assert_allclose(h[:, :, sl], hb, rtol=1e-13, atol=1e-13)
+            dAb, dBb, dh0b = oracle_lib.matrix_affine_scan_bwd(blocks[:, :, b], hb, dy[:, :, sl], h0=h0[:, :, sl],
+                                                               cu_seqlens=cu, reverse=reverse)
+            np.testing.assert_allclose(dA[:, :, sl, sl], dAb, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dB[:, :, sl], dBb, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dh0[:, :, sl], dh0b, rtol=1e-12, atol=1e-12)
+        for c in range(3):
+            hc = oracle_lib.matrix_affine_scan_fwd(A, B[..., c:c + 1], h0=h0[..., c:c + 1], cu_seqlens=cu, reverse=reverse)
+            np.testing.assert_allclose(h[..., c:c + 1], hc, rtol=1e-13, atol=1e-13)
 
 
 def test_matrix_finite_differences(oracle_lib):

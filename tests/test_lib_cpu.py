@@ -161,7 +161,7 @@ def test_matrix_core_workspace_always_required(m):
     # call: header (128), then per chunk and row the published state after it
     # as tagged 8-byte words, sized for the larger chunk count. k or v above 4:
     # chunks of 32 (forward) / 16 (backward) steps, a padded 16 x 16 state (256
-    # words); k, v <= 4: spans of 16 x 8 steps, a padded 4 x 4 state (16 words).
+    # words); k, v <= 4: spans of 16 x 16 steps, a padded 4 x 4 state (16 words).
     p = _prob(m, rows=5, T=100)
     need16 = 128 + 5 * 7 * 256 * 8
     for k, v in ((16, 16), (8, 8), (1, 16), (16, 1), (4, 8)):
@@ -169,7 +169,7 @@ def test_matrix_core_workspace_always_required(m):
         assert m.workspace_bytes(p, m.OP_MATRIX_BWD, k, v) == need16
     for k, v in ((4, 4), (2, 4), (4, 2), (1, 2), (1, 4)):
         assert m.workspace_bytes(p, m.OP_MATRIX_FWD, k, v) == 128 + 5 * 1 * 16 * 8
-    assert m.workspace_bytes(_prob(m, rows=33, T=300), m.OP_MATRIX_BWD, 4, 4) == 128 + 33 * 3 * 16 * 8
+    assert m.workspace_bytes(_prob(m, rows=33, T=300), m.OP_MATRIX_BWD, 4, 4) == 128 + 33 * 2 * 16 * 8
     # args (fwd): prob, k, v, A, B, h0, h, ws, ws_bytes, stream
     assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 16, 16, FAKE, FAKE, None, FAKE, None, 0, None) == 3
     assert m.lib.matrix_affine_scan_fwd(ctypes.byref(p), 8, 2, FAKE, FAKE, None, FAKE, FAKE, need16 - 4, None) == 3

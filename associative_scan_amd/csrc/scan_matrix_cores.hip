@@ -49,8 +49,7 @@ __device__ __forceinline__ v4f mc_zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
 // register tiles
 // ---------------------------------------------------------------------------
 struct Tile16 {
-  static constexpr int E = 16, RPW = 1;  // tile edge, rows per wave
-  __device__ static __forceinline__ int lrow() { return 0; }
+  static constexpr int E = 16;  // tile edge
   __device__ static __forceinline__ int dr0() { return 4 * (int)((threadIdx.x >> 4) & 3); }
   __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 15); }
   // acc + M P with M in R layout and P in D layout; result in D layout
@@ -76,8 +75,8 @@ struct Tile16 {
 };
 
 struct Tile4 {
-  static constexpr int E = 4, RPW = 16;
-  __device__ static __forceinline__ int lrow() { return (int)(threadIdx.x >> 2); }
+  static constexpr int E = 4;
+  __device__ static __forceinline__ int lrow() { return (int)(threadIdx.x >> 2); }  // lane group (block)
   __device__ static __forceinline__ int dr0() { return 0; }
   __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 3); }
   __device__ static __forceinline__ v4f mm(v4f mR, v4f pD, v4f acc) {
@@ -243,7 +242,7 @@ struct McWalk {
 // ---------------------------------------------------------------------------
 // single pass: chunk held in registers, carries chained through the workspace
 // ---------------------------------------------------------------------------
-// A wave owns S steps of its rows. It loads the chunk's transition and
+// A wave owns S steps of one row. It loads the chunk's transition and
 // injection blocks once into registers, walks them for the chunk summary
 // (P, Q), takes its carry-in from the chunk before it, publishes the state
 // after the chunk (h_out = P h_in + Q) and applies the carry from the same
@@ -287,17 +286,15 @@ __device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, v4f& v
   }
 }
 
+// Tile16 only: a wave owns S steps of one row.
 template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
 __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   static_assert(S <= 32, "step masks are 32-bit");
   __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
-  const int64_t ngroups = (a.rows + TL::RPW - 1) / TL::RPW;
-  int64_t g;
+  int64_t r;
   int c;
-  tile_of_block<true>(ngroups, a.ntiles, g, c);
-  const int64_t r = g * TL::RPW + TL::lrow();
-  const bool valid = r < a.rows;  // Tile4: rows past the end compute on zeros, store nothing
-  McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, valid ? r : 0);
+  tile_of_block<true>(a.rows, a.ntiles, r, c);
+  McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
   const int64_t j0 = (int64_t)c * S;
   const int n = (int)min((int64_t)S, a.T - j0);
 
@@ -315,7 +312,7 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
     X[s] = mc_zero();
     Y[s] = mc_zero();
     if constexpr (BWD) H[s] = mc_zero();
-    if (s < n && valid) {
+    if (s < n) {
       const int64_t j = j0 + s;
       const int64_t t = wk.phys(j);
       Y[s] = wk.sh.ldB_D(wk.blkB(a.B, t));
@@ -338,10 +335,9 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
       if (((BWD ? lastm : firstm) >> s) & 1u) {
         const int sk = wk.seg_of(j0 + s);
         if constexpr (!BWD) {
-          const v4f h0D = valid ? wk.sh.ldB_D(wk.h0p(sk)) : mc_zero();
-          Y[s] = TL::mm(X[s], h0D, Y[s]);
+          Y[s] = TL::mm(X[s], wk.sh.ldB_D(wk.h0p(sk)), Y[s]);
         } else {
-          H[s] = valid ? wk.sh.ldB_R(wk.h0p(sk)) : mc_zero();
+          H[s] = wk.sh.ldB_R(wk.h0p(sk));
         }
       }
     }
@@ -366,7 +362,7 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   // ---- carry-in from the chunk before, h_out for the chunk after
   uint32_t* hdr = (uint32_t*)a.ws;
   uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
-  const int64_t me = g * a.ntiles + c;
+  const int64_t me = r * a.ntiles + c;
   const bool publish = c + 1 < a.ntiles;
   if (publish && hard) mc_publish(pub + me * 256, Q);  // h_out = Q whatever the carry-in
   const v4f PR = (publish && !hard) ? TL::d_to_r(s_t, P) : mc_zero();  // off the chain
@@ -386,7 +382,7 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
     if constexpr (BWD) {
       // dA_t = lam h_prev^T (the transpose is a whole-wave operation)
       const v4f dA = TL::mm(TL::d_to_r(s_t, h), H[s], mc_zero());
-      if (s < n && valid) {
+      if (s < n) {
         const int64_t j = j0 + s;
         const int64_t t = wk.phys(j);
         wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
@@ -395,12 +391,11 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
       if (((lastm >> s) & 1u) && a.dh0 && s < n) {
         // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
         const int64_t j = j0 + s;
-        const v4f Ad = valid ? wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j))) : mc_zero();
-        const v4f d = TL::mm(Ad, h, mc_zero());
-        if (valid) wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), d);
+        const v4f d = TL::mm(wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j))), h, mc_zero());
+        wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), d);
       }
     } else {
-      if (s < n && valid) wk.sh.stB_D(wk.blkB(a.out0, wk.phys(j0 + s)), h);
+      if (s < n) wk.sh.stB_D(wk.blkB(a.out0, wk.phys(j0 + s)), h);
     }
   }
 }

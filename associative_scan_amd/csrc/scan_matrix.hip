@@ -556,20 +556,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
 // ---------------------------------------------------------------------------
 template <int K, int V>
 struct MatCfg;
-// (waves per workgroup, steps per lane) for forward / backward, from timing
-// sweeps at 4096 rows x T = 8192
-template <> struct MatCfg<2, 1> { static constexpr int W = 4, EF = 4, EB = 4; };
-template <> struct MatCfg<2, 2> { static constexpr int W = 4, EF = 4, EB = 4; };
-template <> struct MatCfg<4, 1> { static constexpr int W = 2, EF = 4, EB = 4; };
+// waves per workgroup and steps per lane, forward (WF, EF) and backward
+// (WB, EB), from timing sweeps at 4096 rows x T = 8192
+template <> struct MatCfg<2, 1> { static constexpr int WF = 8, EF = 4, WB = 4, EB = 4; };
+template <> struct MatCfg<2, 2> { static constexpr int WF = 4, EF = 4, WB = 4, EB = 4; };
+template <> struct MatCfg<4, 1> { static constexpr int WF = 1, EF = 4, WB = 2, EB = 2; };
 
 template <int K, int V>
 int64_t matrix_tile_steps(bool bwd) {
-  return (int64_t)MatCfg<K, V>::W * 64 * (bwd ? MatCfg<K, V>::EB : MatCfg<K, V>::EF);
+  return bwd ? (int64_t)MatCfg<K, V>::WB * 64 * MatCfg<K, V>::EB
+             : (int64_t)MatCfg<K, V>::WF * 64 * MatCfg<K, V>::EF;
 }
 
 template <int K, int V, bool BWD, bool REV>
 static hipError_t launch_mat(const MatArgs& a0, hipStream_t st) {
-  constexpr int W = MatCfg<K, V>::W, E = BWD ? MatCfg<K, V>::EB : MatCfg<K, V>::EF;
+  constexpr int W = BWD ? MatCfg<K, V>::WB : MatCfg<K, V>::WF;
+  constexpr int E = BWD ? MatCfg<K, V>::EB : MatCfg<K, V>::EF;
   MatArgs a = a0;
   a.ntiles = (int32_t)((a.T + W * 64 * E - 1) / (W * 64 * E));
   const bool lookback = scalar_uses_lookback(a.rows, a.ntiles);

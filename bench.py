@@ -36,7 +36,8 @@ BYTES_FWD, BYTES_BWD = 12, 20  # algorithmic bytes per element, fp32
 # Kernel-level forward+backward time the associative-scan-triton README reports
 # for this exact workload on an H100 80GB (other hardware; context only).
 PAGE_FWDBWD_MS = {4096: 0.602, 65536: 9.212}
-KERNEL_SOURCES = ["associative_scan_amd/csrc/scan_scalar.hip", "associative_scan_amd/csrc/mscan_device.hpp"]
+KERNEL_SOURCES = ["associative_scan_amd/csrc/scan_scalar_kernel.hpp", "associative_scan_amd/csrc/scan_scalar.hip",
+                  "associative_scan_amd/csrc/mscan_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scalar_B8_C1536_T4096.json")
 
 

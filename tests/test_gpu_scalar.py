@@ -261,6 +261,76 @@ def test_fp16_inputs(m, oracle_lib, T, stride):
             close(dh0, rh0, TAU_BWD, "dh0")
 
 
+SHORT_T = [1, 200, 256, 257, 253, 700, 1021, 1024, 1025, 1500, 2045, 2048, 2049]
+
+
+def _inputs(r, rows, stride, dt, gated):
+    """(fp32 values the kernel sees for g, x; the device tensors) with g in
+    (0, 1) or, gated, logits z ~ N(2, 1) with resets z = -inf."""
+    if gated:
+        g32 = (r.standard_normal((rows, stride)) + 2.0).astype(np.float32)
+        g32[r.random((rows, stride)) < 0.01] = -np.inf
+    else:
+        g32 = r.uniform(0, 1, (rows, stride)).astype(np.float32)
+    x32 = r.standard_normal((rows, stride)).astype(np.float32)
+    if dt == "bf16":
+        gb, xb = gen.bf16_round(g32).reshape(rows, stride), gen.bf16_round(x32).reshape(rows, stride)
+        return (gen.bf16_bits_to_f32(gb).reshape(rows, stride), gen.bf16_bits_to_f32(xb).reshape(rows, stride),
+                _bf16(gb), _bf16(xb))
+    if dt == "fp16":
+        g16, x16 = g32.astype(np.float16), x32.astype(np.float16)
+        return (g16.astype(np.float32), x16.astype(np.float32),
+                torch.from_numpy(g16).to(DEV), torch.from_numpy(x16).to(DEV))
+    return g32, x32, _t(g32), _t(x32)
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16", "fp16"])
+@pytest.mark.parametrize("T", SHORT_T)
+def test_short_row_tiles(m, oracle_lib, dt, T):
+    """Rows that fit one tile of 256, 1024 or 2048 elements (their own smaller
+    workgroups), lengths on both sides of each tile size, rows starting at every
+    vector offset, packed sequences with h0, gate values and gate logits, both
+    directions, forward and backward."""
+    r = np.random.default_rng(700 + T + 10_000 * ("fp32", "bf16", "fp16").index(dt))
+    rows = 7
+    for gated in (False, True):
+        fwd, bwd = (m.scan_fwd_gated, m.scan_bwd_gated) if gated else (m.scan_fwd, m.scan_bwd)
+        ofwd, obwd = ((oracle_lib.scan_fwd_gated, oracle_lib.scan_bwd_gated) if gated
+                      else (oracle_lib.scan_fwd, oracle_lib.scan_bwd))
+        for stride in (T, T + 3):
+            g, x, gt, xt = _inputs(r, rows, stride, dt, gated)
+            g, x, gt, xt = g[:, :T], x[:, :T], gt[:, :T], xt[:, :T]
+            nseg = int(r.integers(1, 5))
+            cu = gen.segments_random(r, T, nseg) if nseg > 1 else None
+            cu_t = None if cu is None else _t(cu, torch.int32)
+            h0 = r.standard_normal((nseg, rows)).astype(np.float32)
+            for rev in (False, True):
+                out = torch.full((rows, stride), 7.0, device=DEV)
+                h = fwd(gt, xt, h0=_t(h0), cu_seqlens=cu_t, reverse=rev, out=out[:, :T])
+                href = ofwd(g, x, h0=h0, cu_seqlens=cu, reverse=rev)
+                close(h, href, TAU_FWD, f"h stride {stride} rev {rev} gated {gated}")
+                assert torch.all(out[:, T:] == 7.0), "wrote outside the rows"
+                if stride != T:
+                    continue
+                dy = r.standard_normal((rows, T)).astype(np.float32)
+                d = bwd(gt, h.contiguous(), _t(dy), h0=_t(h0), cu_seqlens=cu_t, reverse=rev)
+                rd = obwd(g, href, dy, h0=h0, cu_seqlens=cu, reverse=rev)
+                for got, ref, nm in zip(d, rd, ("dx", "dg", "dh0")):
+                    close(got, ref, TAU_BWD, f"{nm} rev {rev} gated {gated}")
+
+
+@pytest.mark.parametrize("T", [256, 1024, 2048])
+def test_short_row_tiles_exact(m, oracle_lib, T):
+    """Bit-exact results on the short-row tiles (exact-mode inputs)."""
+    r = np.random.default_rng(900 + T)
+    g, x, dy = gen.exact_mode(r, (5, T))
+    cu = gen.segments_random(r, T, 3, allow_empty=True)
+    h0 = r.integers(-1, 2, (3, 5)).astype(np.float32)
+    for rev in (False, True):
+        run_case(m, oracle_lib, g, x, dy, h0=h0, cu=cu, reverse=rev, check=exact)
+        run_case(m, oracle_lib, g, x, dy, h0=h0[0], reverse=rev, check=exact)
+
+
 def test_workspace_reuse_across_calls(m, oracle_lib):
     """Consecutive multi-tile calls of different sizes share one workspace."""
     r = np.random.default_rng(9)

@@ -106,8 +106,14 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(device):
+    """The current HIP stream of `device` as an integer handle."""
+    if _raw_stream is not None:  # no Stream object per call
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _rows_view(t: torch.Tensor, name: str, tail: int = 0):
@@ -117,6 +123,13 @@ def _rows_view(t: torch.Tensor, name: str, tail: int = 0):
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dim() < 1 + tail:
         raise ValueError(f"{name} needs at least {1 + tail} dims")
+    n = t.numel()
+    if n and t.is_contiguous():  # the common case, without the per-axis walk
+        T = int(t.shape[t.dim() - 1 - tail])
+        block = 1
+        for d in t.shape[t.dim() - tail:]:
+            block *= int(d)
+        return n // (T * block), T, T
     inner = t.shape[t.dim() - 1 - tail:]
     T = int(inner[0])
     block = 1
@@ -250,7 +263,7 @@ def _scan_fwd(g, x, h0, cu_seqlens, reverse, out, gate):
     if rows == 0 or T == 0:
         return h
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     need = workspace_bytes(prob, OP_SCAN_FWD)
     ws = _workspace(dev, sh, need)
     if gate == GATE_NONE:
@@ -295,7 +308,7 @@ def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
             dh0.zero_()
         return dx, dg, dh0
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_BWD))
     if gate == GATE_NONE:
         _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
@@ -330,7 +343,7 @@ def _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, gate):
     if rows == 0 or T == 0:
         return h
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_FWD))
     if gate == GATE_NONE:
         _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
@@ -373,7 +386,7 @@ def _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, ga
             dlh0.zero_()
         return dla, dlb, dlh0
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_BWD))
     if gate == GATE_NONE:
         _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
@@ -410,7 +423,7 @@ def matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False):
     if rows == 0 or T == 0:
         return h
     prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_FWD, k, v))
     _check("matrix_affine_scan_fwd", lib.matrix_affine_scan_fwd(
         ctypes.byref(prob), k, v, _ptr(A), _ptr(B), _ptr(h0), _ptr(h), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
@@ -433,7 +446,7 @@ def matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False, ne
             dh0.zero_()
         return dA, dB, dh0
     prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
-    sh = torch.cuda.current_stream(dev).cuda_stream
+    sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_BWD, k, v))
     _check("matrix_affine_scan_bwd", lib.matrix_affine_scan_bwd(
         ctypes.byref(prob), k, v, _ptr(A), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dA), _ptr(dB), _ptr(dh0),

@@ -471,3 +471,27 @@ def test_varlen_bidir_full(m, oracle_lib, varlen_full):
         close(dx, rx, TAU_BWD, f"{name} dx")
         close(dg, rg, TAU_BWD, f"{name} dg")
         close(dh0, rh0, TAU_BWD, f"{name} dh0")
+
+
+def test_runs_on_the_current_stream(m, oracle_lib):
+    """Calls made under a side stream launch on that stream: the handle the
+    binding passes is the side stream's, and results produced and consumed on
+    it match the oracle."""
+    r = np.random.default_rng(77)
+    g = r.uniform(0, 1, (6, 9000)).astype(np.float32)
+    x = r.standard_normal((6, 9000)).astype(np.float32)
+    dy = r.standard_normal((6, 9000)).astype(np.float32)
+    s = torch.cuda.Stream()
+    dev = torch.device(DEV)
+    assert m._stream_handle(dev) == torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.stream(s):
+        assert m._stream_handle(dev) == s.cuda_stream
+        gt, xt, dyt = _t(g) * 1.0, _t(x) * 1.0, _t(dy) * 1.0  # produced on s
+        h = m.scan_fwd(gt, xt)
+        dx, dg, _ = m.scan_bwd(gt, h, dyt)
+    s.synchronize()
+    href = oracle_lib.scan_fwd(g, x)
+    close(h, href, TAU_FWD, "h")
+    rx, rg, _ = oracle_lib.scan_bwd(g, href, dy)
+    close(dx, rx, TAU_BWD, "dx")
+    close(dg, rg, TAU_BWD, "dg")

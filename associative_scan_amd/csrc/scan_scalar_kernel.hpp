@@ -309,6 +309,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     const int64_t wlo = REV ? urow - jt0 - (int64_t)(w + 1) * WREG : jt0 + (int64_t)w * WREG;
     const int xblk = REV ? 63 - l : l;
     float* xr = s_x[XP ? w : 0];
+    // every array's EL elements of sub-chunk s from vector-aligned padded u0
+    auto load_vectors = [&](int s, int64_t u0) {
+      load_span<Tin, EL>(gp + base + u0, Lg[s]);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) Lg[s][e] = gate_value<GATE, LOGB>(Lg[s][e]);
+      if constexpr (!BWD) {
+        load_span<Tin, EL>((const Tin*)a.b + base + u0, Lb[s]);
+      } else {
+        load_span<float, EL>((const float*)a.b + base + u0, Lb[s]);
+        load_span<float, EL>(a.hs + base + u0, Lh[s]);
+        if constexpr (LOGB) load_span<float, EL>(a.lb + base + u0, Lx[s]);
+      }
+    };
     if (XP && interior) {
       if constexpr (XP) {
         SX::load((const float*)gp + base + wlo, xr, SX::FLOATS, true);
@@ -323,24 +336,20 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         if constexpr (BWD) SX::read_block(xr + 2 * SX::FLOATS, xblk, Lh[0]);
         if constexpr (LOGB) SX::read_block(xr + 3 * SX::FLOATS, xblk, Lx[0]);
       }
+    } else if (interior) {
+      // straight-line: every vector of the tile in flight before the first use
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) load_vectors(s, span_lo(s));
     } else {
-      // Vector loads for every lane span inside the row; element loads with
-      // bounds only for the spans that straddle a row end (a partial tile
-      // keeps nearly all of its traffic in 16-byte accesses).
+      // A partial tile (a row end inside it): vector loads for every lane span
+      // inside the row, element loads with bounds only for the spans that
+      // straddle a row end. (Kept apart from the interior branch: a per-lane
+      // condition there cost 5-50% on the look-back kernels.)
 #pragma unroll
       for (int s = 0; s < SUBS; ++s) {
         const int64_t u0 = span_lo(s);
-        if (interior || (u0 >= lead && u0 + EL <= lead + T)) {
-          load_span<Tin, EL>(gp + base + u0, Lg[s]);
-#pragma unroll
-          for (int e = 0; e < EL; ++e) Lg[s][e] = gate_value<GATE, LOGB>(Lg[s][e]);
-          if constexpr (!BWD) {
-            load_span<Tin, EL>((const Tin*)a.b + base + u0, Lb[s]);
-          } else {
-            load_span<float, EL>((const float*)a.b + base + u0, Lb[s]);
-            load_span<float, EL>(a.hs + base + u0, Lh[s]);
-            if constexpr (LOGB) load_span<float, EL>(a.lb + base + u0, Lx[s]);
-          }
+        if (u0 >= lead && u0 + EL <= lead + T) {
+          load_vectors(s, u0);
         } else {
 #pragma unroll
           for (int e = 0; e < EL; ++e) {
@@ -632,7 +641,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           SX::store(a.out0 + base + wlo, xr, SX::FLOATS, true);
           if constexpr (BWD) SX::store(a.out1 + base + wlo, xr + SX::FLOATS, SX::FLOATS, true);
         }
-      } else if (interior || (u0 >= lead && u0 + EL <= lead + T)) {
+      } else if (interior) {
+        store_span<EL>(a.out0 + base + u0, o0);
+        if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
+      } else if (u0 >= lead && u0 + EL <= lead + T) {  // a lane span inside the row
         store_span<EL>(a.out0 + base + u0, o0);
         if constexpr (BWD) store_span<EL>(a.out1 + base + u0, o1);
       } else {

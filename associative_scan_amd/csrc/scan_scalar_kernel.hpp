@@ -266,31 +266,56 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       } else {
         seg = SegSlice{a.cu, n, 0};
       }
-    } else {
-      // just the entries that cover this tile
-      const int64_t jt0 = (int64_t)c_first * TILE;
-      const int64_t ut_lo = REV ? urow - jt0 - TILE : jt0;
-      const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
+    }
+  }
+  // Look-back mode: just the entries that cover this tile. A table of at most
+  // 64 entries is read whole into wave 0's lanes (one entry each) before the
+  // tile's data loads are issued, and sliced after them, so its only global
+  // load overlaps the data; a longer table is searched after the data loads.
+  const int ncu = a.nseg + 1;
+  int32_t cu_l = 0;
+  if constexpr (VARLEN && MODE == kLookback) {
+    if (ncu <= 64 && w == 0 && l < ncu) cu_l = a.cu[l];
+  }
+  auto lookback_slice = [&]() {
+    const int64_t jt0 = (int64_t)c_first * TILE;
+    const int64_t ut_lo = REV ? urow - jt0 - TILE : jt0;
+    const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
+    if (ncu <= 64) {
       if (w == 0) {
         int ka = 0, n = 0;
         if (plo < phi) {
-          ka = max(wave_count_le(a.cu, a.nseg + 1, plo) - 1, 0);
-          const int kb = min(wave_count_le(a.cu, a.nseg + 1, phi - 1), a.nseg);
+          // entries <= key, counted over the lanes' entries
+          ka = max(__popcll(__ballot(l < ncu && (int64_t)cu_l <= plo)) - 1, 0);
+          const int kb = min(__popcll(__ballot(l < ncu && (int64_t)cu_l <= phi - 1)), a.nseg);
           n = max(kb - ka + 1, 1);
         }
+        if (l >= ka && l < ka + n) s_cu[l - ka] = cu_l;
         if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
       }
       __syncthreads();
-      const int n = s_cu_n, k0 = s_cu_k0;
-      if (n <= kCuSlice) {
-        for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
-        __syncthreads();
-        seg = SegSlice{s_cu, n, k0};
-      } else {
-        seg = SegSlice{a.cu + k0, n, k0};
-      }
+      seg = SegSlice{s_cu, s_cu_n, s_cu_k0};
+      return;
     }
-  }
+    if (w == 0) {
+      int ka = 0, n = 0;
+      if (plo < phi) {
+        ka = max(wave_count_le(a.cu, ncu, plo) - 1, 0);
+        const int kb = min(wave_count_le(a.cu, ncu, phi - 1), a.nseg);
+        n = max(kb - ka + 1, 1);
+      }
+      if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
+    }
+    __syncthreads();
+    const int n = s_cu_n, k0 = s_cu_k0;
+    if (n <= kCuSlice) {
+      for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
+      __syncthreads();
+      seg = SegSlice{s_cu, n, k0};
+    } else {
+      seg = SegSlice{a.cu + k0, n, k0};
+    }
+  };
 
   C carry = Ops::cident();  // state entering the current tile
   for (int c = c_first; c <= c_last; ++c) {
@@ -367,6 +392,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         }
       }
     }
+    if constexpr (VARLEN && MODE == kLookback) lookback_slice();
     if constexpr (LOGB) {
       // b = e^{log b} (a = e^{log a} was taken on load, 0 for log a = -inf)
 #pragma unroll

@@ -14,7 +14,9 @@
 //           (one row per wave, the 16 blocks in time).
 // Reading and writing the 16 x 16 blocks as rows with an LDS transpose per
 // block (as the 4 x 4 kernel does) measured no faster forward and 39% slower
-// backward, so Tile16 keeps its column-wise dword accesses.
+// backward, and changing the layout of row accesses on the matrix cores
+// (a product with the identity per block) 1.6x / 1.8x slower, so Tile16
+// keeps its column-wise dword accesses.
 // Blocks smaller than the tile are zero-padded in registers: rows and columns
 // past k (or v) load as 0 and are never stored, and a zero-padded A and B keep
 // the padding of h, the adjoint and the chunk summaries at 0, so the padded

@@ -108,7 +108,8 @@ typedef enum {
 
 typedef struct {
   int64_t rows;               /* independent rows (e.g. B*C), >= 1                       */
-  int64_t T;                  /* time steps per row (packed tokens for varlen), >= 1    */
+  int64_t T;                  /* time steps per row (packed tokens for varlen),         *
+                               * 1 <= T <= 2^31 - 1 (cu_seqlens offsets are int32)       */
   int64_t row_stride;         /* elements (steps for matrices) between rows, >= T       */
   const int32_t* cu_seqlens;  /* device, nseg+1 offsets; NULL = one sequence            */
   int32_t nseg;               /* number of sequences (1 when cu_seqlens is NULL)        */

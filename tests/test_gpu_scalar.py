@@ -495,3 +495,42 @@ def test_runs_on_the_current_stream(m, oracle_lib):
     rx, rg, _ = oracle_lib.scan_bwd(g, href, dy)
     close(dx, rx, TAU_BWD, "dx")
     close(dg, rg, TAU_BWD, "dg")
+
+
+@pytest.mark.timeout(400)
+def test_row_of_maximum_length(m, oracle_lib):
+    """One row of T = 2^31 - 1 elements, the largest T the library accepts
+    (8 GiB per array: 64-bit byte offsets, half a million look-back tiles).
+    Resets every 1000 steps and x = dy = 1 make every state and adjoint a small
+    integer, exact in any association order: h_t = t mod 1000 + 1, lam_t =
+    steps to the next reset or the row end, dg_t = h_{t-1} lam_t (h_{-1} = 0).
+    Checked over the whole row on the device in slices, and against the oracle
+    on a window that starts at a reset."""
+    T = 2**31 - 1
+    free, _ = torch.cuda.mem_get_info()
+    if free < 64 * 2**30:
+        pytest.skip("needs 64 GiB of free device memory")
+    g = torch.ones(T, device=DEV)
+    g[::1000] = 0.0
+    x = torch.ones(T, device=DEV)
+    h = m.scan_fwd(g, x)
+    dx, dg, dh0 = m.scan_bwd(g, h, x)
+    del x
+    step = 2**28
+    for lo in range(0, T, step):
+        hi = min(lo + step, T)
+        t = torch.arange(lo, hi, device=DEV, dtype=torch.int64)
+        assert torch.equal(h[lo:hi], (t % 1000 + 1).float()), f"h slice at {lo}"
+        lam = torch.minimum(1000 - t % 1000, T - t).float()
+        assert torch.equal(dx[lo:hi], lam), f"dx slice at {lo}"
+        hprev = torch.where(t % 1000 == 0, 1000.0, (t % 1000).float())  # h_{t-1}
+        if lo == 0:
+            hprev[0] = 0.0  # no h0
+        assert torch.equal(dg[lo:hi], hprev * lam), f"dg slice at {lo}"
+        del t, lam, hprev
+    assert float(dh0.item()) == 0.0  # g_0 = 0
+    # the oracle on a window from the last reset to the row end
+    w0 = ((T - 1) // 1000) * 1000
+    gw = g[w0:].cpu().numpy()[None, :]
+    href = oracle_lib.scan_fwd(gw, np.ones_like(gw))
+    exact(h[w0:][None, :], href, "h window")

@@ -72,6 +72,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced: valida
 
 @pytest.mark.parametrize("case", [
     dict(rows=0), dict(T=0), dict(stride=50, T=100), dict(nseg=2), dict(reverse=2), dict(nseg=0),
+    dict(T=2**31, stride=2**31),  # beyond int32 cu_seqlens offsets
 ])
 def test_scan_fwd_rejects_bad_problem(m, case):
     p = _prob(m, **case)

@@ -388,3 +388,41 @@ def test_matrix_cumprod(m, k, reverse):
         fd = (loss(A64 + e) - loss(A64 - e)) / 2e-6
         assert abs(g[row, t, i, j] - fd) <= 1e-3 * (1 + abs(fd)), (row, t, i, j, g[row, t, i, j], fd)
 
+
+
+@pytest.mark.timeout(400)
+def test_matrix16_row_beyond_2_31_elements(m, oracle_lib):
+    """One 16x16 row of T = 2^23 + 5 steps: 2^31 + 1280 floats per array
+    (64-bit element offsets on the matrix cores, 262145 chained chunks).
+    A = I with A = 0 every 1000 steps, B = dy = all-ones blocks: h_t =
+    (t mod 1000 + 1) J, lam_t = L_t J with L_t the steps to the next reset or
+    the row end, dA_t = 16 L_t h_{t-1} J (J the all-ones block), every value an
+    integer below 2^24, so exact. Checked over the whole row in slices and
+    against the oracle on a window that starts at a reset."""
+    T, k = 2**23 + 5, 16
+    free, _ = torch.cuda.mem_get_info()
+    if free < 96 * 2**30:
+        pytest.skip("needs 96 GiB of free device memory")
+    A = torch.eye(k, device=DEV).expand(T, k, k).contiguous()
+    A[::1000] = 0.0
+    B = torch.ones((T, k, k), device=DEV)
+    h = m.matrix_affine_scan_fwd(A, B)
+    dA, dB, dh0 = m.matrix_affine_scan_bwd(A, h, B)
+    step = 2**20
+    for lo in range(0, T, step):
+        hi = min(lo + step, T)
+        t = torch.arange(lo, hi, device=DEV, dtype=torch.int64)
+        hv = (t % 1000 + 1).float()
+        assert torch.equal(h[lo:hi], hv[:, None, None].expand(-1, k, k)), f"h slice at {lo}"
+        L = torch.minimum(1000 - t % 1000, T - t).float()
+        assert torch.equal(dB[lo:hi], L[:, None, None].expand(-1, k, k)), f"dB slice at {lo}"
+        hprev = torch.where(t % 1000 == 0, 1000.0, (t % 1000).float())
+        if lo == 0:
+            hprev[0] = 0.0  # no h0
+        assert torch.equal(dA[lo:hi], (16.0 * L * hprev)[:, None, None].expand(-1, k, k)), f"dA slice at {lo}"
+        del t, hv, L, hprev
+    assert torch.count_nonzero(dh0).item() == 0  # A_0 = 0
+    w0 = ((T - 1) // 1000) * 1000
+    Aw, Bw = A[w0:].cpu().numpy()[None], B[w0:].cpu().numpy()[None]
+    href = oracle_lib.matrix_affine_scan_fwd(Aw, Bw)
+    assert np.array_equal(h[w0:].cpu().double().numpy()[None], href), "h window"

@@ -559,7 +559,7 @@ struct MatCfg;
 // waves per workgroup and steps per lane, forward (WF, EF) and backward
 // (WB, EB), from timing sweeps at 4096 rows x T = 8192
 template <> struct MatCfg<2, 1> { static constexpr int WF = 8, EF = 4, WB = 4, EB = 4; };
-template <> struct MatCfg<2, 2> { static constexpr int WF = 4, EF = 4, WB = 4, EB = 4; };
+template <> struct MatCfg<2, 2> { static constexpr int WF = 4, EF = 4, WB = 4, EB = 2; };
 template <> struct MatCfg<4, 1> { static constexpr int WF = 1, EF = 4, WB = 2, EB = 2; };
 
 template <int K, int V>

@@ -4,8 +4,9 @@
 
 namespace mscan {
 
-
-// Tile shape, every input type: 4 waves x 4 sub-chunks x 64 lanes x 4 elements.
+// Tile shape, every input type: 4 waves x 4 sub-chunks x 64 lanes x 4 elements
+// (the linear scan's rows of at most 2048 elements take the smaller
+// one-per-row shapes of scan_scalar_short.hip instead).
 // (8192-element tiles for the 16-bit forward measured within run-to-run noise,
 // +-8% on the packed bf16 workload.)
 int64_t scalar_tile_elems(int) { return 4 * 4 * 64 * 4; }

@@ -37,13 +37,18 @@
 //   a wave    = SUBS independent 64-lane DPP scans chained through lane 63,
 //   the waves = chained through LDS.
 // Across the tiles of a row, two modes:
-//   row loop : one workgroup walks its row tile by tile and carries the state
-//              in registers; used when a row fits in one tile (no workspace,
-//              no inter-workgroup traffic);
+//   one tile : a row that fits one tile, one workgroup per row (no workspace,
+//              no inter-workgroup traffic; the launcher guarantees the fit);
 //   look-back: one workgroup per tile; the tiles of a row chain by decoupled
 //              look-back through the workspace. Used whenever a row spans
-//              several tiles: it keeps more bytes in flight per CU than the
-//              row loop and measured faster at every benchmark row count.
+//              several tiles: it keeps more bytes in flight per CU than
+//              walking a row's tiles in one workgroup (an earlier mode) and
+//              measured faster at every benchmark row count.
+// The tile body below is written as a loop over a workgroup's tiles, which
+// runs exactly once in both modes; with a constant trip count in the one-tile
+// mode the compiler drops the loop, and with it the waits for loads of a
+// previous iteration that its back edge made it assume (in the generated
+// code: a wait for the backward's halo loads before the tile's own loads).
 // Rows whose start is not 16-byte aligned are handled by aligning vector
 // groups to absolute addresses and masking the elements outside the row.
 #pragma once
@@ -231,8 +236,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   int c_first, c_last;
   if constexpr (MODE == kRowLoop) {
     r = blockIdx.x;
-    c_first = 0;
-    c_last = a.ntiles - 1;
+    c_first = c_last = 0;  // the row fits one tile
   } else {
     int c;
     tile_of_block<kTileMajor>(a.rows, a.ntiles, r, c);
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   const bool has_h0 = h0p != nullptr;
   // initial state as the backward uses it (h_prev of a sequence's first step)
   auto h0val = [&](int64_t i) -> float { return LOGB ? __expf(h0p[i]) : h0p[i]; };
-  const float h0row = (!VARLEN && has_h0) ? h0val(r) : 0.f;
+  float h0row = 0.f;  // loaded with each tile's data (below)
 
   Workspace ws{};
   if constexpr (MODE == kLookback) ws = ws_view(a.ws);
@@ -347,6 +351,21 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         if constexpr (LOGB) load_span<float, EL>(a.lb + base + u0, Lx[s]);
       }
     };
+    // Backward halo, one value per wave: the gate before the wave's span and
+    // the forward state after it (processing order). Every lane loads the same
+    // in-row element (index clamped, result masked), issued ahead of the tile's
+    // vectors: loaded where they are used, after the shuffles that wait for
+    // the tile, they cost each workgroup a second memory round trip.
+    float halo_g = 0.f, halo_h = 0.f;
+    bool halo_g_ok = false, halo_h_ok = false;
+    if constexpr (BWD) {
+      const int64_t jg = jt0 + (int64_t)w * WREG - 1, jh = jt0 + (int64_t)(w + 1) * WREG;
+      const int64_t tg = (REV ? urow - 1 - jg : jg) - lead, th = (REV ? urow - 1 - jh : jh) - lead;
+      halo_g_ok = jg >= 0 && tg >= 0 && tg < T;
+      halo_h_ok = th >= 0 && th < T;
+      halo_g = InTraits<Tin>::load1(gp + rowoff + (halo_g_ok ? tg : 0));
+      halo_h = a.hs[rowoff + (halo_h_ok ? th : 0)];
+    }
     if (XP && interior) {
       if constexpr (XP) {
         SX::load((const float*)gp + base + wlo, xr, SX::FLOATS, true);
@@ -392,6 +411,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         }
       }
     }
+    if constexpr (!VARLEN) {
+      if (has_h0) h0row = h0val(r);  // after the tile's loads are issued
+    }
     if constexpr (VARLEN && MODE == kLookback) lookback_slice();
     if constexpr (LOGB) {
       // b = e^{log b} (a = e^{log a} was taken on load, 0 for log a = -inf)
@@ -420,8 +442,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 
     // ---- backward: shift gates forward and states backward by one element
     if constexpr (BWD) {
-      // padded coordinate of processing element j of this row
-      auto u_of = [&](int64_t j) -> int64_t { return REV ? urow - 1 - j : j; };
 #pragma unroll
       for (int s = 0; s < SUBS; ++s) {
         float gprev = __shfl_up(G[s][EL - 1], 1, 64);
@@ -430,17 +450,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           const float gl = readlane_f(G[s - 1][EL - 1], 63);
           if (l == 0) gprev = gl;
         } else if (l == 0) {
-          const int64_t j = jt0 + (int64_t)w * WREG - 1;  // element before this wave's span
-          const int64_t t = u_of(j) - lead;
-          gprev = (j >= 0 && t >= 0 && t < T) ? gate_value<GATE, LOGB>(InTraits<Tin>::load1(gp + rowoff + t)) : 0.f;
+          gprev = halo_g_ok ? gate_value<GATE, LOGB>(halo_g) : 0.f;  // element before this wave's span
         }
         if (s + 1 < SUBS) {
           const float hn = readlane_f(N[s + 1][0], 0);
           if (l == 63) hnext = hn;
         } else if (l == 63) {
-          const int64_t j = jt0 + (int64_t)(w + 1) * WREG;  // element after this wave's span
-          const int64_t t = u_of(j) - lead;
-          hnext = (t >= 0 && t < T) ? a.hs[rowoff + t] : 0.f;
+          hnext = halo_h_ok ? halo_h : 0.f;  // element after this wave's span
         }
 #pragma unroll
         for (int e = EL - 1; e > 0; --e) A[s][e] = G[s][e - 1];

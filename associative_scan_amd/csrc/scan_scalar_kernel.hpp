@@ -366,6 +366,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       halo_g = InTraits<Tin>::load1(gp + rowoff + (halo_g_ok ? tg : 0));
       halo_h = a.hs[rowoff + (halo_h_ok ? th : 0)];
     }
+    // the row's initial state (a wave-uniform address: a scalar load, which
+    // no wait for the tile's vector loads holds back)
+    if constexpr (!VARLEN) {
+      if (has_h0) h0row = h0val(r);
+    }
     if (XP && interior) {
       if constexpr (XP) {
         SX::load((const float*)gp + base + wlo, xr, SX::FLOATS, true);
@@ -410,9 +415,6 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           }
         }
       }
-    }
-    if constexpr (!VARLEN) {
-      if (has_h0) h0row = h0val(r);  // after the tile's loads are issued
     }
     if constexpr (VARLEN && MODE == kLookback) lookback_slice();
     if constexpr (LOGB) {

@@ -23,8 +23,9 @@
 //     leave LDS with coalesced 16-byte stores.
 // Inside a tile the steps are summarised per lane as (P, Q) = (product of the
 // A's, accumulated B's), scanned across the wave with DPP and across waves
-// through LDS; across tiles the row-loop / look-back modes of the scalar
-// kernels apply unchanged (see scan_scalar.hip).
+// through LDS; across tiles the scalar kernels' two modes apply unchanged
+// (a row that fits one tile on its own, longer rows chained by look-back;
+// see scan_scalar_kernel.hpp).
 //
 // Tiles are aligned to the row start in both directions; with `reverse` the
 // row is processed from its last tile down, each tile from its last window,

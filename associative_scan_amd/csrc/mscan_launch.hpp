@@ -33,6 +33,7 @@ bool scalar_uses_lookback(int64_t rows, int64_t ntiles);
 // rows that fit one tile of at most 2048 elements: a smaller workgroup per row
 bool scalar_short_rows(int64_t T, int64_t stride);
 hipError_t launch_scalar_short(const ScalarArgs& a, int in_dtype, int gate, bool bwd, hipStream_t st);
+hipError_t launch_log_short(const ScalarArgs& a, int gate, bool bwd, hipStream_t st);
 hipError_t launch_scalar(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st);
 // Log-space forward (g = log a, b = log b, h0 = log h0; fp32).
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st);

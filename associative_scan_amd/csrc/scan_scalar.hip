@@ -5,8 +5,8 @@
 namespace mscan {
 
 // Tile shape, every input type: 4 waves x 4 sub-chunks x 64 lanes x 4 elements
-// (the linear scan's rows of at most 2048 elements take the smaller
-// one-per-row shapes of scan_scalar_short.hip instead).
+// (rows of at most 2048 elements take the smaller one-per-row shapes of
+// scan_scalar_short.hip instead).
 // (8192-element tiles for the 16-bit forward measured within run-to-run noise,
 // +-8% on the packed bf16 workload.)
 int64_t scalar_tile_elems(int) { return 4 * 4 * 64 * 4; }
@@ -65,18 +65,21 @@ hipError_t launch_scalar_sigmoid(const ScalarArgs& a, int in_dtype, bool bwd, hi
 // on dense rows and 13% on packed ones. (The memory-bound linear scans are
 // 6-11% slower that way and keep 4-element lanes.)
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
+  if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNone, false, st);
   return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNone, true>(a, st)
                : launch_cfg<LogOps, float, false, false, 4, 1, 4, false, kGateNone, true>(a, st);
 }
 
 // Log-space backward: the fp32 adjoint scan with exponentiated gates.
 hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
+  if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNone, true, st);
   return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true>(a, st)
                : launch_cfg<LinOps, float, true, false, 4, 4, 1, true>(a, st);
 }
 
 // Log-space scan with log a = -softplus(z): forward and backward.
 hipError_t launch_log_softplus(const ScalarArgs& a, bool bwd, hipStream_t st) {
+  if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNegSoftplus, bwd, st);
   if (bwd) return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true, kGateNegSoftplus>(a, st)
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, true, kGateNegSoftplus>(a, st);
   return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNegSoftplus, true>(a, st)

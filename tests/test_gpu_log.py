@@ -185,3 +185,37 @@ def test_log_autograd_wrapper(m, oracle_lib):
     close(la_t.grad, ra, TAU_GRAD, "dlog_a")
     close(lb_t.grad, rb, TAU_GRAD, "dlog_b")
     close(lh0_t.grad, rh0.reshape(-1), TAU_GRAD, "dlog_h0")
+
+
+@pytest.mark.parametrize("T", [1, 100, 256, 257, 1000, 1024, 1025, 2047, 2048, 2049])
+def test_log_short_row_tiles(m, oracle_lib, T):
+    """Rows that fit one tile of 256, 1024 or 2048 elements (their own smaller
+    workgroups): forward and backward, plain and from -softplus logits, with
+    packed sequences, h0 and resets (log a = -inf, logits +inf), both
+    directions."""
+    r = np.random.default_rng(3000 + T)
+    rows = 6
+    for gated in (False, True):
+        fwd, bwd = (m.scan_log_fwd_gated, m.scan_log_bwd_gated) if gated else (m.scan_log_fwd, m.scan_log_bwd)
+        ofwd, obwd = ((oracle_lib.scan_log_fwd_gated, oracle_lib.scan_log_bwd_gated) if gated
+                      else (oracle_lib.scan_log_fwd, oracle_lib.scan_log_bwd))
+        if gated:
+            la = r.standard_normal((rows, T)).astype(np.float32)
+            la[r.random((rows, T)) < 0.01] = np.inf  # log a = -softplus(+inf) = -inf
+        else:
+            la, _ = _inputs(r, rows, T)
+            la[r.random((rows, T)) < 0.01] = -np.inf
+        lb = r.standard_normal((rows, T)).astype(np.float32)
+        nseg = int(r.integers(1, 5))
+        cu = gen.segments_random(r, T, nseg) if nseg > 1 else None
+        cu_t = None if cu is None else _t(cu, torch.int32)
+        lh0 = r.standard_normal((nseg, rows)).astype(np.float32)
+        for rev in (False, True):
+            h = fwd(_t(la), _t(lb), _t(lh0), cu_seqlens=cu_t, reverse=rev)
+            href = ofwd(la, lb, log_h0=lh0, cu_seqlens=cu, reverse=rev)
+            close(h, href, TAU_LOG, f"h rev {rev} gated {gated}")
+            dy = r.standard_normal((rows, T)).astype(np.float32)
+            d = bwd(_t(la), _t(lb), h, _t(dy), _t(lh0), cu_seqlens=cu_t, reverse=rev)
+            rd = obwd(la, lb, href, dy, log_h0=lh0, cu_seqlens=cu, reverse=rev)
+            for got, ref, nm in zip(d, rd, ("dlog_a", "dlog_b", "dlog_h0")):
+                close(got, ref, TAU_LOG, f"{nm} rev {rev} gated {gated}")

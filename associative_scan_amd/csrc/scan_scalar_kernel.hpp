@@ -216,11 +216,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   // coalesced 16-byte accesses.
   static_assert(!XP || (SUBS == 1 && EL == 16 && sizeof(Tin) == 4), "staged windows are fp32, 16 per lane");
   using SX = Stage<1, EL>;
-  // Look-back dispatch order (see tile_of_block), from timing each workload:
-  // dense linear rows stream memory best row-major (tile-major cost ~10% at
-  // T = 16384); packed sequences and the log-space kernels resolve their
-  // look-back faster tile-major (4-10%).
-  constexpr bool kTileMajor = VARLEN || LOGB || !std::is_same<Ops, LinOps>::value;
+  // Look-back dispatch order (see tile_of_block), from timing each workload
+  // (packed: C = 1536 x 65536 tokens in 16 sequences): dense linear rows
+  // stream memory best row-major (tile-major cost ~10% at T = 16384), and so
+  // do the packed linear backward (tile-major 5-7% slower) and the packed fp32
+  // forward (4%); the packed 16-bit forward (row-major 8% slower) and the
+  // log-space kernels resolve their look-back faster tile-major.
+  constexpr bool kTileMajor = (VARLEN && !BWD && sizeof(Tin) == 2) || LOGB || !std::is_same<Ops, LinOps>::value;
   constexpr int NXR = BWD ? (LOGB ? 4 : 3) : 2;  // staged arrays per wave
   __shared__ __attribute__((aligned(16))) float s_x[XP ? WAVES : 1][XP ? NXR * SX::FLOATS : 4];
 

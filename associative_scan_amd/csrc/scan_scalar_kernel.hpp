@@ -42,8 +42,8 @@
 //   look-back: one workgroup per tile; the tiles of a row chain by decoupled
 //              look-back through the workspace. Used whenever a row spans
 //              several tiles: it keeps more bytes in flight per CU than
-//              walking a row's tiles in one workgroup (an earlier mode) and
-//              measured faster at every benchmark row count.
+//              walking a row's tiles in one workgroup, which measured slower
+//              at every benchmark row count.
 // The tile body below is written as a loop over a workgroup's tiles, which
 // runs exactly once in both modes; with a constant trip count in the one-tile
 // mode the compiler drops the loop, and with it the waits for loads of a
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   SegSlice seg{nullptr, 0, 0};
   if constexpr (VARLEN) {
     if constexpr (MODE == kRowLoop) {
-      // every tile of the row needs the whole table: cache it once
+      // the row's whole table, cached once
       const int n = a.nseg + 1;
       if (n <= kCuSlice) {
         for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[i];

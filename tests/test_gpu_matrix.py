@@ -426,3 +426,44 @@ def test_matrix16_row_beyond_2_31_elements(m, oracle_lib):
     Aw, Bw = A[w0:].cpu().numpy()[None], B[w0:].cpu().numpy()[None]
     href = oracle_lib.matrix_affine_scan_fwd(Aw, Bw)
     assert np.array_equal(h[w0:].cpu().double().numpy()[None], href), "h window"
+
+
+@pytest.mark.parametrize("k", [2, 4, 16])
+def test_matrix_graph_capture_replays(m, oracle_lib, k):
+    """Matrix forward + backward (VALU and matrix-core kernels, chained chunks)
+    captured in a HIP graph and replayed with new inputs, eager calls between
+    replays; every replay matches the oracle."""
+    r = np.random.default_rng(4343 + k)
+    rows, T = 3, 3000
+    A0 = (r.standard_normal((rows, T, k, k)) * (0.9 / np.sqrt(k))).astype(np.float32)
+    B0 = r.standard_normal((rows, T, k, k)).astype(np.float32)
+    dy = r.standard_normal((rows, T, k, k)).astype(np.float32)
+    At, Bt, dyt = _t(A0), _t(B0), _t(dy)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            hw = m.matrix_affine_scan_fwd(At, Bt)
+            m.matrix_affine_scan_bwd(At, hw, dyt)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        h = m.matrix_affine_scan_fwd(At, Bt)
+        dA, dB, _ = m.matrix_affine_scan_bwd(At, h, dyt)
+    for rep in range(3):
+        A = (r.standard_normal((rows, T, k, k)) * (0.9 / np.sqrt(k))).astype(np.float32)
+        B = r.standard_normal((rows, T, k, k)).astype(np.float32)
+        At.copy_(_t(A))
+        Bt.copy_(_t(B))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        href = oracle_lib.matrix_affine_scan_fwd(A, B)
+        close(h, href, TAU_FWD, f"h replay {rep}")
+        rA, rB, _ = oracle_lib.matrix_affine_scan_bwd(A, href, dy)
+        close(dA, rA, TAU_BWD, f"dA replay {rep}")
+        close(dB, rB, TAU_BWD, f"dB replay {rep}")
+        he = m.matrix_affine_scan_fwd(At, Bt)
+        torch.cuda.synchronize()
+        close(he, href, TAU_FWD, f"eager h after replay {rep}")

@@ -534,3 +534,48 @@ def test_row_of_maximum_length(m, oracle_lib):
     gw = g[w0:].cpu().numpy()[None, :]
     href = oracle_lib.scan_fwd(gw, np.ones_like(gw))
     exact(h[w0:][None, :], href, "h window")
+
+
+def test_graph_capture_replays(m, oracle_lib):
+    """A forward + backward captured in a HIP graph (look-back tiles, packed
+    sequences, h0: the workspace clearing is a kernel, not a memset node) and
+    replayed several times, with new inputs copied in and eager calls and
+    synchronisations between replays; every replay matches the oracle and the
+    eager result."""
+    r = np.random.default_rng(4242)
+    rows, T, nseg = 5, 9000, 3
+    cu = gen.segments_random(r, T, nseg)
+    g0 = r.uniform(0, 1, (rows, T)).astype(np.float32)
+    x0 = r.standard_normal((rows, T)).astype(np.float32)
+    dy0 = r.standard_normal((rows, T)).astype(np.float32)
+    h00 = r.standard_normal((nseg, rows)).astype(np.float32)
+    gt, xt, dyt, h0t, cut = _t(g0), _t(x0), _t(dy0), _t(h00), _t(cu, torch.int32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            hw = m.scan_fwd(gt, xt, h0=h0t, cu_seqlens=cut)
+            m.scan_bwd(gt, hw, dyt, h0=h0t, cu_seqlens=cut)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        h = m.scan_fwd(gt, xt, h0=h0t, cu_seqlens=cut)
+        dx, dg, dh0 = m.scan_bwd(gt, h, dyt, h0=h0t, cu_seqlens=cut)
+    for rep in range(4):
+        g = r.uniform(0, 1, (rows, T)).astype(np.float32)
+        x = r.standard_normal((rows, T)).astype(np.float32)
+        gt.copy_(_t(g))
+        xt.copy_(_t(x))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        href = oracle_lib.scan_fwd(g, x, h0=h00, cu_seqlens=cu)
+        close(h, href, TAU_FWD, f"h replay {rep}")
+        rx, rg, rh0 = oracle_lib.scan_bwd(g, href, dy0, h0=h00, cu_seqlens=cu)
+        close(dx, rx, TAU_BWD, f"dx replay {rep}")
+        close(dg, rg, TAU_BWD, f"dg replay {rep}")
+        close(dh0, rh0, TAU_BWD, f"dh0 replay {rep}")
+        he = m.scan_fwd(gt, xt, h0=h0t, cu_seqlens=cut)  # eager work between replays
+        torch.cuda.synchronize()
+        close(he, href, TAU_FWD, f"eager h after replay {rep}")

@@ -173,13 +173,16 @@ __device__ __forceinline__ float sigmoid_f(float z) { return __frcp_rn(1.f + __e
 // and without losing its tail for z << 0. log1p(u): for u < 1/16 the series
 // u - u^2/2 + u^3/3 - u^4/4 + u^5/5 (truncation below u^6/6 < 1e-8 relative);
 // otherwise log(1 + u), whose rounding of 1 + u costs at most ~1e-6 relative
-// there. Both branches are a few VALU ops, where log1pf's range reduction
-// doubled the time of the (VALU-bound) log-space forward.
+// there, taken as ln 2 times the hardware base-2 logarithm: 1 + u lies in
+// (1, 2], where that instruction needs none of the denormal and special-value
+// handling a general logf wraps around it. Both branches are a few VALU ops,
+// where log1pf's range reduction doubled the time of the (VALU-bound)
+// log-space forward.
 __device__ __forceinline__ float softplus_f(float z) {
   const float u = __expf(-fabsf(z));
   const float series = u * __builtin_fmaf(-u, __builtin_fmaf(-u, __builtin_fmaf(-u, __builtin_fmaf(-u, 0.2f, 0.25f),
                                                                                1.f / 3.f), 0.5f), 1.f);
-  const float lg = __logf(1.f + u);
+  const float lg = __builtin_amdgcn_logf(1.f + u) * 0.693147180559945f;
   return fmaxf(z, 0.f) + (u < 0.0625f ? series : lg);
 }
 

@@ -103,7 +103,8 @@ lib = _load()
 # marshalling helpers
 # ---------------------------------------------------------------------------
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for the c_void_p parameters
+    return None if t is None else t.data_ptr()
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -190,6 +191,19 @@ def workspace_bytes(prob: Problem, op: int, k: int = 1, v: int = 1) -> int:
     return int(lib.mscan_workspace_bytes(ctypes.byref(prob), op, k, v))
 
 
+_WS_HEADER_BYTES = 128  # what a scalar-layout op asks for when its rows need no look-back
+
+
+def _scalar_ws(dev, sh, prob, op):
+    """(pointer, bytes) of the workspace a scalar-layout op needs: none when
+    every row fits one tile (the library then never reads it)."""
+    need = workspace_bytes(prob, op)
+    if need <= _WS_HEADER_BYTES:
+        return None, 0
+    ws = _workspace(dev, sh, need)
+    return ws.data_ptr(), ws.numel()
+
+
 def _segments(cu_seqlens, device, T):
     if cu_seqlens is None:
         return None, 1
@@ -249,29 +263,32 @@ def _scan_fwd(g, x, h0, cu_seqlens, reverse, out, gate):
     if g.shape != x.shape or g.dtype != x.dtype:
         raise ValueError("g and x must have the same shape and dtype")
     rows, T, stride = _rows_view(g, "g")
-    if _rows_view(x, "x")[2] != stride:
+    if not (x.is_cuda and x.is_contiguous() and stride == T) and _rows_view(x, "x")[2] != stride:
         raise ValueError("g and x must share the row stride")
     dt = _in_dtype(g, "g")
     dev = g.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     h0 = _h0(h0, nseg, rows, ())
-    h = torch.empty(g.shape, dtype=torch.float32, device=dev) if out is None else out
-    if stride != T and out is None:
-        raise ValueError("strided rows need an explicit `out` with the same row stride")
-    if h.shape != g.shape or _rows_view(h, "out")[2] != stride:
-        raise ValueError("out must match g's shape and row stride")
+    if out is None:
+        if stride != T:
+            raise ValueError("strided rows need an explicit `out` with the same row stride")
+        h = torch.empty(g.shape, dtype=torch.float32, device=dev)  # contiguous: stride T
+    else:
+        h = out
+        if h.shape != g.shape or _rows_view(h, "out")[2] != stride:
+            raise ValueError("out must match g's shape and row stride")
+        if h.dtype != torch.float32:
+            raise ValueError("out must be float32")
     if rows == 0 or T == 0:
         return h
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
-    need = workspace_bytes(prob, OP_SCAN_FWD)
-    ws = _workspace(dev, sh, need)
+    wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_FWD)
     if gate == GATE_NONE:
-        _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
-                                        _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+        _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h), wsp, wsn, sh))
     else:
         _check("scan_fwd_gated", lib.scan_fwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
-                                                    _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+                                                    wsp, wsn, sh))
     return h
 
 
@@ -291,9 +308,10 @@ def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
     if g.shape != h.shape or dy.shape != h.shape:
         raise ValueError("g, h and dy must have the same shape")
     rows, T, stride = _rows_view(g, "g")
-    for t, n in ((h, "h"), (dy, "dy")):
-        if _rows_view(t, n)[2] != stride:
-            raise ValueError("g, h and dy must share the row stride")
+    if not (h.is_cuda and dy.is_cuda and h.is_contiguous() and dy.is_contiguous() and stride == T):
+        for t, n in ((h, "h"), (dy, "dy")):
+            if _rows_view(t, n)[2] != stride:
+                raise ValueError("g, h and dy must share the row stride")
     if stride != T:
         raise ValueError("scan_bwd takes contiguous rows")
     dt = _in_dtype(g, "g")
@@ -309,14 +327,13 @@ def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
         return dx, dg, dh0
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
-    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_BWD))
+    wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_BWD)
     if gate == GATE_NONE:
         _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
-                                        _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+                                        _ptr(dg), _ptr(dh0), wsp, wsn, sh))
     else:
         _check("scan_bwd_gated", lib.scan_bwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0),
-                                                    _ptr(dx), _ptr(dg), _ptr(dh0), _ptr(ws), ws.numel(),
-                                                    ctypes.c_void_p(sh)))
+                                                    _ptr(dx), _ptr(dg), _ptr(dh0), wsp, wsn, sh))
     return dx, dg, dh0
 
 

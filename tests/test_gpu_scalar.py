@@ -579,3 +579,21 @@ def test_graph_capture_replays(m, oracle_lib):
         he = m.scan_fwd(gt, xt, h0=h0t, cu_seqlens=cut)  # eager work between replays
         torch.cuda.synchronize()
         close(he, href, TAU_FWD, f"eager h after replay {rep}")
+
+
+def test_binding_rejects_bad_out_and_host_tensors(m):
+    """The binding refuses an `out` that is not fp32 or has another shape, and
+    host tensors anywhere, before anything reaches the library."""
+    g = torch.rand((3, 100), device=DEV)
+    x = torch.randn((3, 100), device=DEV)
+    with pytest.raises(ValueError):
+        m.scan_fwd(g, x, out=torch.empty((3, 100), device=DEV, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        m.scan_fwd(g, x, out=torch.empty((3, 99), device=DEV))
+    with pytest.raises(ValueError):
+        m.scan_fwd(g, x.cpu())
+    h = m.scan_fwd(g, x)
+    with pytest.raises(ValueError):
+        m.scan_bwd(g, h.cpu(), x)
+    with pytest.raises(ValueError):
+        m.scan_bwd(g, h, x.cpu())

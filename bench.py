@@ -33,9 +33,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "GB/s & % HBM peak, scalar scan fwd/fwd+bwd B=8 C=1536 T=4K–64K"
 BYTES_FWD, BYTES_BWD = 12, 20  # algorithmic bytes per element, fp32
-# Kernel-level forward+backward time the associative-scan-triton README reports
-# for this exact workload on an H100 80GB (other hardware; context only).
-PAGE_FWDBWD_MS = {4096: 0.602, 65536: 9.212}
+# Kernel-level forward+backward times the associative-scan-triton README reports
+# for this workload (B=8, C=1536) on an H100 80GB, per T ("performance",
+# kernel-level table; other hardware, context only).
+PAGE_FWDBWD_MS = {128: 0.027, 256: 0.043, 512: 0.077, 1024: 0.161, 2048: 0.306, 4096: 0.602,
+                  8192: 1.186, 16384: 2.322, 32768: 4.602, 65536: 9.212}
 KERNEL_SOURCES = ["associative_scan_amd/csrc/scan_scalar_kernel.hpp", "associative_scan_amd/csrc/scan_scalar.hip",
                   "associative_scan_amd/csrc/mscan_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scalar_B8_C1536_T4096.json")

@@ -361,14 +361,13 @@ def _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, gate):
         return h
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
-    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_FWD))
+    wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_LOG_FWD)
     if gate == GATE_NONE:
         _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
-                                                _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+                                                wsp, wsn, sh))
     else:
         _check("scan_log_fwd_gated", lib.scan_log_fwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b),
-                                                            _ptr(log_h0), _ptr(h), _ptr(ws), ws.numel(),
-                                                            ctypes.c_void_p(sh)))
+                                                            _ptr(log_h0), _ptr(h), wsp, wsn, sh))
     return h
 
 
@@ -404,15 +403,14 @@ def _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, ga
         return dla, dlb, dlh0
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
-    ws = _workspace(dev, sh, workspace_bytes(prob, OP_SCAN_LOG_BWD))
+    wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_LOG_BWD)
     if gate == GATE_NONE:
         _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
-                                                _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), _ptr(ws), ws.numel(),
-                                                ctypes.c_void_p(sh)))
+                                                _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), wsp, wsn, sh))
     else:
         _check("scan_log_bwd_gated", lib.scan_log_bwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b), _ptr(h),
                                                             _ptr(dy), _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0),
-                                                            _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+                                                            wsp, wsn, sh))
     return dla, dlb, dlh0
 
 

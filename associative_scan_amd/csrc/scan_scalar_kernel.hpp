@@ -343,6 +343,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     const int64_t wlo = REV ? urow - jt0 - (int64_t)(w + 1) * WREG : jt0 + (int64_t)w * WREG;
     const int xblk = REV ? 63 - l : l;
     float* xr = s_x[XP ? w : 0];
+    // XP: the staged path serves every wave whose whole window lies in the
+    // row (a wave-uniform test), so a partial tile sends only its straddling
+    // window down the element path (log-space forward, 8192 rows of T = 8000:
+    // 209 -> 161 us; of T = 7000: 176 -> 155 us)
+    const bool xstage = XP && (interior || (wlo >= lead && wlo + WREG <= lead + T));
     // every array's EL elements of sub-chunk s from vector-aligned padded u0
     auto load_vectors = [&](int s, int64_t u0) {
       load_span<Tin, EL>(gp + base + u0, Lg[s]);
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     if constexpr (!VARLEN) {
       if (has_h0) h0row = h0val(r);
     }
-    if (XP && interior) {
+    if (xstage) {
       if constexpr (XP) {
         SX::load((const float*)gp + base + wlo, xr, SX::FLOATS, true);
         SX::load((const float*)a.b + base + wlo, xr + SX::FLOATS, SX::FLOATS, true);
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             o1[P_(e)] = (O[s][e] * N[s][e]) * G[s][e];    // dlog_a = lam * h_prev * a
         }
       }
-      if (XP && interior) {
+      if (xstage) {
         if constexpr (XP) {
           wave_lds_sync();
           SX::write_block(xr, xblk, o0);

@@ -197,9 +197,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     r = blockIdx.x;
     c = 0;
   } else {
-    // tile-major, except the (2,1) backward (6-word descriptors), which
-    // streams faster row-major (0.341 vs 0.360 ms at 4096 rows x T = 8192)
-    tile_of_block<!(BWD && K * K + K * V <= 6)>(a.rows, a.ntiles, r, c);
+    // tile-major, except the k = 2 backward, which streams faster row-major
+    // (4096 rows x T = 8192: (2,1) 0.341 vs 0.360 ms, (2,2) 0.491 vs 0.546 ms;
+    // the (4,1) backward is 19% slower that way)
+    tile_of_block<!(BWD && K == 2)>(a.rows, a.ntiles, r, c);
   }
   const int64_t T = a.T;
   const int64_t row0 = r * a.stride;  // first step of the row

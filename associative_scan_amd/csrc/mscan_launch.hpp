@@ -66,7 +66,7 @@ struct MatArgs {
                         // VALU kernels take them as template parameters)
 };
 
-// (k, v) served by the VALU kernels (scan_matrix.hip): (2,1), (2,2), (4,1), (4,4).
+// (k, v) served by the VALU kernels (scan_matrix.hip): (2,1), (2,2), (4,1).
 bool matrix_valu_shape(int k, int v);
 // (k, v) served by the matrix-core kernels (scan_matrix_cores.hip): every
 // other pair of the envelope k, v in {1, 2, 4, 8, 16} except (1, 1), the

@@ -38,6 +38,15 @@
  *    multiplies h0 by its own gate: h_s = g_s * h0 + x_s.
  *  - reverse != 0 runs every segment from its last element down to its
  *    first: h_t = g_t * h_{t+1} + x_t, with h0 entering at the last element.
+ *  - A zero transition (g_t = 0, log a_t = -inf, or a k x k A_t whose entries
+ *    are all zero) is a reset: it erases everything before t, so h_t = x_t
+ *    exactly, whatever the state before it holds, Inf and NaN included ("Our
+ *    RG-LRU GPU audit", "Exact real chunk algebra": encoding a reset as
+ *    a_t = 0 wipes out whatever came before it). For finite states this is the arithmetic
+ *    value of g_t * h + x_t; for a non-finite state it is the reading that
+ *    makes a reset inside a sequence behave as a sequence start does. The
+ *    adjoints follow: no gradient flows through a reset (lam_{t-1} gets no
+ *    g_t * lam_t term, and dh0 = 0 when the segment's first step is a reset).
  */
 #include <math.h>
 #include <stddef.h>
@@ -53,7 +62,10 @@ static int64_t seg_end(const int32_t* cu, int32_t s, int64_t T) { return cu ? (i
  * Scalar forward: per segment [b, e) of row r,
  *   causal : h_b = g_b*h0 + x_b,          h_t = g_t*h_{t-1} + x_t  (b < t < e)
  *   reverse: h_{e-1} = g_{e-1}*h0 + x_{e-1}, h_t = g_t*h_{t+1} + x_t (b <= t < e-1)
+ * with a zero gate a reset: h_t = x_t (see the conventions above).
  * ------------------------------------------------------------------------- */
+static double lin_step(double g, double state, double x) { return g == 0.0 ? x : g * state + x; }
+
 API void oracle_scan_fwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
                          int32_t reverse, const double* g, const double* x, const double* h0, double* h) {
   if (!cu) nseg = 1;
@@ -66,9 +78,9 @@ API void oracle_scan_fwd(int64_t rows, int64_t T, int64_t row_stride, const int3
       double* hr = h + r * row_stride;
       double state = h0 ? h0[(int64_t)s * rows + r] : 0.0;
       if (!reverse) {
-        for (int64_t t = b; t < e; ++t) { state = gr[t] * state + xr[t]; hr[t] = state; }
+        for (int64_t t = b; t < e; ++t) { state = lin_step(gr[t], state, xr[t]); hr[t] = state; }
       } else {
-        for (int64_t t = e - 1; t >= b; --t) { state = gr[t] * state + xr[t]; hr[t] = state; }
+        for (int64_t t = e - 1; t >= b; --t) { state = lin_step(gr[t], state, xr[t]); hr[t] = state; }
       }
     }
   }
@@ -82,8 +94,12 @@ API void oracle_scan_fwd(int64_t rows, int64_t T, int64_t row_stride, const int3
  *   reverse: lam_b = dy_b;  lam_t = dy_t + g_{t-1}*lam_{t-1}
  *            dx_t = lam_t;  dg_t = lam_t * h_{t+1}  (h_e := h0, or 0)
  *            dh0  = g_{e-1} * lam_{e-1}
+ * A zero gate is a reset, so nothing flows through it: the g*lam term (of
+ * lam and of dh0) is absent where the gate is 0.
  * dh0 may be NULL; an empty segment writes dh0 = 0.
  * ------------------------------------------------------------------------- */
+static double through(double g, double lam) { return g == 0.0 ? 0.0 : g * lam; }
+
 API void oracle_scan_bwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
                          int32_t reverse, const double* g, const double* h, const double* dy,
                          const double* h0, double* dx, double* dg, double* dh0) {
@@ -101,20 +117,20 @@ API void oracle_scan_bwd(int64_t rows, int64_t T, int64_t row_stride, const int3
       }
       if (!reverse) {
         for (int64_t t = e - 1; t >= b; --t) {
-          lam = dy[o + t] + gnext * lam;
+          lam = dy[o + t] + through(gnext, lam);
           dx[o + t] = lam;
           dg[o + t] = lam * (t > b ? h[o + t - 1] : init);
           gnext = g[o + t];
         }
-        if (dh0) dh0[(int64_t)s * rows + r] = g[o + b] * lam;
+        if (dh0) dh0[(int64_t)s * rows + r] = through(g[o + b], lam);
       } else {
         for (int64_t t = b; t < e; ++t) {
-          lam = dy[o + t] + gnext * lam;
+          lam = dy[o + t] + through(gnext, lam);
           dx[o + t] = lam;
           dg[o + t] = lam * (t < e - 1 ? h[o + t + 1] : init);
           gnext = g[o + t];
         }
-        if (dh0) dh0[(int64_t)s * rows + r] = g[o + e - 1] * lam;
+        if (dh0) dh0[(int64_t)s * rows + r] = through(g[o + e - 1], lam);
       }
     }
   }
@@ -176,8 +192,9 @@ API void oracle_scan_log_fwd(int64_t rows, int64_t T, int64_t row_stride, const 
  *   dlog_b_t   = lam_t * b_t
  *   dlog_a_t   = lam_t * a_t * h_{t-1}         (h_{b-1} := h0)
  *   dlog_h0    = lam_b * a_b * h0              (b = the segment's forward-first step)
- * reverse mirrors the neighbours as in oracle_scan_bwd. dlog_h0 may be NULL;
- * an empty segment writes 0.
+ * with no a*lam term through a reset a = 0 (log_a = -inf), as in
+ * oracle_scan_bwd. reverse mirrors the neighbours as in oracle_scan_bwd.
+ * dlog_h0 may be NULL; an empty segment writes 0.
  * ------------------------------------------------------------------------- */
 API void oracle_scan_log_bwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
                              int32_t reverse, const double* log_a, const double* log_b, const double* h,
@@ -199,14 +216,14 @@ API void oracle_scan_log_bwd(int64_t rows, int64_t T, int64_t row_stride, const 
       for (int64_t i = n - 1; i >= 0; --i) {
         const int64_t t = reverse ? e - 1 - i : b + i; /* walk opposite to the forward */
         const double at = exp(log_a[o + t]);
-        lam = dy[o + t] + anext * lam;
+        lam = dy[o + t] + through(anext, lam);
         dlog_b[o + t] = lam * exp(log_b[o + t]);
         const double hprev = (i == 0) ? h0 : h[o + (reverse ? t + 1 : t - 1)];
         dlog_a[o + t] = lam * at * hprev;
         anext = at;
         tfirst = t;
       }
-      if (dlog_h0) dlog_h0[(int64_t)s * rows + r] = lam * exp(log_a[o + tfirst]) * h0;
+      if (dlog_h0) dlog_h0[(int64_t)s * rows + r] = through(exp(log_a[o + tfirst]), lam) * h0;
     }
   }
 }
@@ -214,10 +231,17 @@ API void oracle_scan_log_bwd(int64_t rows, int64_t T, int64_t row_stride, const 
 /* ---------------------------------------------------------------------------
  * Matrix-affine forward: h_t = A_t h_{t-1} + B_t with A_t k x k, B_t and h_t
  * k x v (left multiplication, row-major blocks). Same segment / h0 / reverse
- * rules as the scalar scan; h0 is [nseg][rows][k][v].
+ * rules as the scalar scan; h0 is [nseg][rows][k][v]. An all-zero A_t is a
+ * reset: h_t = B_t.
  * A is [rows][T][k][k] and B, h are [rows][T][k][v] with row_stride counted in
  * time steps.
  * ------------------------------------------------------------------------- */
+static int all_zero(const double* M, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (M[i] != 0.0) return 0;
+  return 1;
+}
+
 API void oracle_matrix_fwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
                            int32_t reverse, int32_t k, int32_t v, const double* A, const double* B,
                            const double* h0, double* h) {
@@ -233,10 +257,12 @@ API void oracle_matrix_fwd(int64_t rows, int64_t T, int64_t row_stride, const in
         const int64_t t = reverse ? e - 1 - i : b + i;
         const double* At = A + (r * row_stride + t) * kk;
         const double* Bt = B + (r * row_stride + t) * kv;
+        const int reset = all_zero(At, kk);
         for (int p = 0; p < k; ++p)
           for (int q = 0; q < v; ++q) {
             double acc = Bt[p * v + q];
-            for (int j = 0; j < k; ++j) acc += At[p * k + j] * st[j * v + q];
+            if (!reset)
+              for (int j = 0; j < k; ++j) acc += At[p * k + j] * st[j * v + q];
             nx[p * v + q] = acc;
           }
         memcpy(st, nx, sizeof(double) * kv);
@@ -252,7 +278,8 @@ API void oracle_matrix_fwd(int64_t rows, int64_t T, int64_t row_stride, const in
  *            dB_t = lam_t;  dA_t = lam_t h_{t-1}^T  (h_{b-1} := h0, or 0)
  *            dh0 = A_b^T lam_b
  *   reverse: mirrored (A_{t-1}, h_{t+1}, dh0 = A_{e-1}^T lam_{e-1}).
- * dh0 may be NULL.
+ * Nothing flows through an all-zero A (a reset): no A^T lam term there, in
+ * lam or in dh0. dh0 may be NULL.
  * ------------------------------------------------------------------------- */
 API void oracle_matrix_bwd(int64_t rows, int64_t T, int64_t row_stride, const int32_t* cu, int32_t nseg,
                            int32_t reverse, int32_t k, int32_t v, const double* A, const double* h,
@@ -278,7 +305,7 @@ API void oracle_matrix_bwd(int64_t rows, int64_t T, int64_t row_stride, const in
         for (int p = 0; p < k; ++p)
           for (int q = 0; q < v; ++q) {
             double acc = dyt[p * v + q];
-            if (Anext)
+            if (Anext && !all_zero(Anext, kk))
               for (int j = 0; j < k; ++j) acc += Anext[j * k + p] * lam[j * v + q];
             nl[p * v + q] = acc;
           }
@@ -300,10 +327,12 @@ API void oracle_matrix_bwd(int64_t rows, int64_t T, int64_t row_stride, const in
       }
       if (dh0) {
         const double* Af = A + (r * row_stride + tfirst) * kk;
+        const int reset = all_zero(Af, kk);
         for (int p = 0; p < k; ++p)
           for (int q = 0; q < v; ++q) {
             double acc = 0.0;
-            for (int j = 0; j < k; ++j) acc += Af[j * k + p] * lam[j * v + q];
+            if (!reset)
+              for (int j = 0; j < k; ++j) acc += Af[j * k + p] * lam[j * v + q];
             dh0[((int64_t)s * rows + r) * kv + p * v + q] = acc;
           }
       }

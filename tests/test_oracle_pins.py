@@ -692,3 +692,152 @@ def test_matrix_finite_differences(oracle_lib):
     M[0, 0, 1, 0] -= eps
     fd = (L(A, B, P) - L(A, B, M)) / (2 * eps)
     assert abs(fd - dh0[0, 0, 1, 0]) < 1e-6 * max(1, abs(fd))
+
+
+# ---------------------------------------------------------------------------
+# a reset (zero transition) wipes out a non-finite prefix
+# ("Our RG-LRU GPU audit", "Exact real chunk algebra": a reset is a_t = 0)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_reset_clears_nonfinite_prefix(oracle_lib, reverse):
+    """Constant gate a with one zero at p and NaN / +-Inf tokens before it: from
+    p on the result is scipy.signal.lfilter of the tokens from p (a fresh start),
+    and before p it is lfilter of the poisoned tokens (non-finite from the first
+    poison on)."""
+    o = oracle_lib
+    T, p, a = 300, 170, 0.75
+    rng = _rng(41 + reverse)
+    x = rng.standard_normal(T)
+    g = np.full(T, a)
+    x[40], x[90], x[120] = np.nan, np.inf, -np.inf
+    g[p] = 0.0
+    if reverse:  # time runs backwards: flip the data so the same positions apply
+        h = o.scan_fwd(g[::-1].copy(), x[::-1].copy(), reverse=True)[::-1]
+    else:
+        h = o.scan_fwd(g, x)
+    after = scipy.signal.lfilter([1.0], [1.0, -a], x[p:])
+    assert np.array_equal(h[p:], after)
+    assert np.all(np.isnan(h[40:p]))
+    np.testing.assert_allclose(h[:40], scipy.signal.lfilter([1.0], [1.0, -a], x[:40]), rtol=1e-13, atol=0)
+
+
+def test_reset_at_sequence_start_ignores_nonfinite_h0(oracle_lib):
+    """A zero gate on a sequence's first step drops h0, even a NaN or Inf h0:
+    the a = 0 special case gives h = x exactly, dx = dy, dh0 = 0."""
+    o = oracle_lib
+    rng = _rng(43)
+    x = rng.standard_normal((3, 50))
+    dy = rng.standard_normal((3, 50))
+    g = np.zeros((3, 50))
+    h0 = np.array([np.nan, np.inf, -np.inf])
+    for rev in (False, True):
+        h = o.scan_fwd(g, x, h0=h0, reverse=rev)
+        assert np.array_equal(h, x)
+        dx, dg, dh0 = o.scan_bwd(g, h, dy, h0=h0, reverse=rev)
+        assert np.array_equal(dx, dy)
+        assert np.array_equal(dh0, np.zeros((1, 3)))
+        # dg_t = lam_t * h_{t-1}: h0 enters only the sequence's first step
+        first = 49 if rev else 0
+        assert np.all(np.isnan(dg[:, first]) | np.isinf(dg[:, first]))
+        rest = np.delete(dg, first, axis=1)
+        assert np.all(np.isfinite(rest))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_reset_stops_nonfinite_adjoint(oracle_lib, reverse):
+    """Backward with a constant gate a and one zero gate at p (causal): a NaN
+    gradient entering after p never reaches t < p, where lam is the reversed
+    lfilter of dy (the adjoint recurrence lam_t = dy_t + a lam_{t+1}) over
+    [0, p) alone."""
+    o = oracle_lib
+    T, p, a = 200, 120, 0.5
+    rng = _rng(47 + reverse)
+    x = rng.standard_normal(T)
+    dy = rng.standard_normal(T)
+    g = np.full(T, a)
+    g[p] = 0.0
+    dy[150] = np.nan
+    if reverse:
+        gg, xx, dd = g[::-1].copy(), x[::-1].copy(), dy[::-1].copy()
+        h = o.scan_fwd(gg, xx, reverse=True)
+        dx, dg, dh0 = o.scan_bwd(gg, h, dd, reverse=True)
+        dx = dx[::-1]
+    else:
+        h = o.scan_fwd(g, x)
+        dx, dg, dh0 = o.scan_bwd(g, h, dy)
+    lam_before = scipy.signal.lfilter([1.0], [1.0, -a], dy[:p][::-1])[::-1]
+    np.testing.assert_allclose(dx[:p], lam_before, rtol=1e-13, atol=1e-15)
+    assert np.all(np.isnan(dx[p:151]))
+    assert np.all(np.isfinite(dx[151:]))
+
+
+def test_reset_equals_sequence_split_with_nonfinite_data(oracle_lib):
+    """Inside one sequence, a zero gate at p gives, from p on, exactly what a
+    sequence starting at p gives (h0 = 0); the two take different paths through
+    the oracle (a gate value against a cu_seqlens boundary)."""
+    o = oracle_lib
+    rng = _rng(53)
+    T, p = 400, 230
+    g = rng.uniform(0.2, 1.0, (4, T))
+    x = rng.standard_normal((4, T))
+    dy = rng.standard_normal((4, T))
+    x[:, 100] = np.nan
+    x[1, 50] = np.inf
+    g[:, p] = 0.0
+    h_reset = o.scan_fwd(g, x)
+    h_split = o.scan_fwd(g, x, cu_seqlens=[0, p, T])
+    assert np.array_equal(h_reset[:, p:], h_split[:, p:])
+    # the adjoint of the suffix agrees too, and the prefix's is NaN-free
+    dy[:, 350] = np.nan
+    dx_r, dg_r, _ = o.scan_bwd(g, h_reset, dy)
+    dx_s, dg_s, _ = o.scan_bwd(g, h_split, dy, cu_seqlens=[0, p, T])
+    assert np.array_equal(dx_r, dx_s, equal_nan=True)
+    assert np.all(np.isfinite(dx_r[:, :p]))
+
+
+def test_log_reset_drops_h0_and_prefix(oracle_lib):
+    """log a = -inf on a sequence's first step drops log_h0 (h = e^{log b}
+    exactly there), and the matching linear adjoint has no dlog_h0."""
+    o = oracle_lib
+    rng = _rng(59)
+    la = -np.log1p(np.exp(rng.standard_normal((2, 60))))
+    lb = rng.standard_normal((2, 60))
+    la[:, 0] = -np.inf
+    lh0 = np.array([3.0, -2.0])
+    h = o.scan_log_fwd(la, lb, log_h0=lh0)
+    h_nol = o.scan_log_fwd(la, lb)
+    assert np.array_equal(h, h_nol)
+    assert np.array_equal(h[:, 0], np.exp(lb[:, 0]))
+    dy = rng.standard_normal((2, 60))
+    _, _, dlh0 = o.scan_log_bwd(la, lb, h, dy, log_h0=lh0)
+    assert np.array_equal(dlh0, np.zeros((1, 2)))
+
+
+def test_matrix_reset_clears_nan_prefix(oracle_lib):
+    """k = 2 rotations r Rot(theta) with NaN injections and an all-zero A at p:
+    from p on the state equals the complex scan z_t = r e^{i theta} z_{t-1} + B
+    of the steps from p (scipy.signal.lfilter with a complex coefficient), and
+    the adjoint's lam for t < p equals the reversed lfilter with the conjugate
+    coefficient."""
+    o = oracle_lib
+    T, p = 160, 90
+    rng = _rng(61)
+    r, th = 0.8, 0.7
+    A = np.tile(r * np.array([[math.cos(th), -math.sin(th)], [math.sin(th), math.cos(th)]]), (T, 1, 1))
+    A[p] = 0.0
+    B = rng.standard_normal((T, 2, 1))
+    B[30, 0, 0] = np.nan
+    h = o.matrix_affine_scan_fwd(A[None], B[None])[0]
+    z = scipy.signal.lfilter([1.0], [1.0, -r * complex(math.cos(th), math.sin(th))], B[p:, 0, 0] + 1j * B[p:, 1, 0])
+    np.testing.assert_allclose(h[p:, 0, 0], z.real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(h[p:, 1, 0], z.imag, rtol=1e-12, atol=1e-12)
+    assert np.isnan(h[30, 0, 0]) and np.isfinite(h[30, 1, 0])  # the NaN enters one entry
+    assert np.all(np.isnan(h[31:p]))  # and the next rotation spreads it over the state
+    dy = rng.standard_normal((T, 2, 1))
+    dy[120, 1, 0] = np.nan
+    dA, dB, dh0 = o.matrix_affine_scan_bwd(A[None], h[None], dy[None])
+    lam = scipy.signal.lfilter([1.0], [1.0, -r * complex(math.cos(th), -math.sin(th))],
+                               (dy[:p, 0, 0] + 1j * dy[:p, 1, 0])[::-1])[::-1]
+    np.testing.assert_allclose(dB[0, :p, 0, 0], lam.real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dB[0, :p, 1, 0], lam.imag, rtol=1e-12, atol=1e-12)
+    assert np.all(np.isfinite(dh0))

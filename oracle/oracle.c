@@ -223,7 +223,10 @@ API void oracle_scan_log_bwd(int64_t rows, int64_t T, int64_t row_stride, const 
         anext = at;
         tfirst = t;
       }
-      if (dlog_h0) dlog_h0[(int64_t)s * rows + r] = through(exp(log_a[o + tfirst]), lam) * h0;
+      if (dlog_h0) {
+        const double af = exp(log_a[o + tfirst]);
+        dlog_h0[(int64_t)s * rows + r] = (af == 0.0) ? 0.0 : af * lam * h0; /* none through a reset */
+      }
     }
   }
 }

@@ -811,6 +811,11 @@ def test_log_reset_drops_h0_and_prefix(oracle_lib):
     dy = rng.standard_normal((2, 60))
     _, _, dlh0 = o.scan_log_bwd(la, lb, h, dy, log_h0=lh0)
     assert np.array_equal(dlh0, np.zeros((1, 2)))
+    # a NaN or Inf log_h0 is dropped the same way, value and gradient
+    bad = np.array([np.nan, np.inf])
+    assert np.array_equal(o.scan_log_fwd(la, lb, log_h0=bad), h_nol)
+    _, _, dlh0 = o.scan_log_bwd(la, lb, h, dy, log_h0=bad)
+    assert np.array_equal(dlh0, np.zeros((1, 2)))
 
 
 def test_matrix_reset_clears_nan_prefix(oracle_lib):

@@ -36,7 +36,7 @@ __all__ = [
     "scan_fwd_gated", "scan_bwd_gated", "scan_log_fwd_gated", "scan_log_bwd_gated",
     "scan_causal", "scan_bidirectional_branched", "scan_log", "matrix_scan", "GATE_SIGMOID", "GATE_NEG_SOFTPLUS",
     "workspace_bytes", "OP_SCAN_FWD", "OP_SCAN_BWD", "OP_SCAN_LOG_FWD", "OP_MATRIX_FWD", "OP_MATRIX_BWD",
-    "OP_SCAN_LOG_BWD",
+    "OP_SCAN_LOG_BWD", "set_debug", "debug_enabled", "workspace_error", "stream_ceiling", "release_capture_workspaces",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +45,8 @@ library_path = os.path.join(_HERE, "libmscan.so")
 OP_SCAN_FWD, OP_SCAN_BWD, OP_SCAN_LOG_FWD, OP_MATRIX_FWD, OP_MATRIX_BWD, OP_SCAN_LOG_BWD = range(6)
 _F32, _BF16, _F16 = 0, 1, 2
 GATE_NONE, GATE_SIGMOID, GATE_NEG_SOFTPLUS = 0, 1, 2
-_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error"}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small", 4: "HIP error",
+           5: "a look-back wait gave up"}
 
 
 class MscanError(RuntimeError):
@@ -83,6 +84,10 @@ def _load():
         "scan_log_bwd_gated": (i32, [P, i32, p, p, p, p, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_fwd": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_bwd": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "mscan_workspace_error": (i32, [p, sz, p, p]),
+        "mscan_stream_ceiling": (i32, [ctypes.POINTER(p), i32, ctypes.POINTER(p), i32, sz, p]),
+        "mscan_debug_partial_fwd": (i32, [P, i32, i32, p, p, p, p, sz, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,
+                                          p]),
         "mscan_status_string": (ctypes.c_char_p, [i32]),
         "mscan_last_hip_error": (ctypes.c_char_p, []),
         "mscan_abi_version": (i32, []),
@@ -168,12 +173,41 @@ def _rows_view(t: torch.Tensor, name: str, tail: int = 0):
     return rows, T, stride_el // block
 
 
+def _out_rows(shape, rows, T, stride, dev, tail=()):
+    """An uninitialised fp32 tensor of `shape` whose rows lie `stride` steps
+    apart (a view into a [rows, stride, *tail] buffer), matching the row stride
+    the C ABI applies to every array of a call."""
+    if stride == T:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    buf = torch.empty((rows, stride) + tuple(tail), dtype=torch.float32, device=dev)
+    return buf[:, :T].view(shape)
+
+
 _ws_lock = threading.Lock()
 _ws_cache = {}
+_capture_ws = []  # workspaces of calls recorded into HIP graphs: kept for the graphs' replays
+
+
+def release_capture_workspaces() -> None:
+    """Drop the workspaces held for calls recorded into HIP graphs. Call only
+    once no graph captured through this binding will be replayed again."""
+    with _ws_lock:
+        _capture_ws.clear()
 
 
 def _workspace(device, stream_handle, nbytes):
-    """A zero-initialised workspace of at least nbytes for (device, stream)."""
+    """A workspace of at least nbytes for (device, stream). Eager calls share
+    one cached buffer per (device, stream), grown as needed. A call recorded
+    into a HIP graph gets a buffer of its own that is never released (until
+    release_capture_workspaces): a graph's replays write the buffer whose
+    address it recorded, so it must outlive the graph and must not be shared
+    with eager calls or with other graphs, which may be replayed concurrently
+    or need a larger buffer later."""
+    if torch.cuda.is_current_stream_capturing():
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)  # the graph's memory pool
+        with _ws_lock:
+            _capture_ws.append(buf)
+        return buf
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     with _ws_lock:
         buf = _ws_cache.get(key)
@@ -204,6 +238,78 @@ def _scalar_ws(dev, sh, prob, op):
     return ws.data_ptr(), ws.numel()
 
 
+# ---------------------------------------------------------------------------
+# debug mode
+# ---------------------------------------------------------------------------
+_DEBUG = [os.environ.get("MSCAN_DEBUG", "") not in ("", "0")]
+
+
+def set_debug(on: bool = True) -> None:
+    """Debug mode. The contents of cu_seqlens are validated on the host before
+    each call (cu[0] = 0, cu[-1] = T, nondecreasing), and after each call that
+    chained tiles through a workspace the workspace's error word is read (which
+    synchronises the stream): a look-back wait that gave up raises MscanError
+    with status 5 instead of leaving NaN in the outputs unnoticed. Off by
+    default, since it synchronises every call; MSCAN_DEBUG=1 in the environment
+    turns it on at import. Calls made while a HIP graph is being captured skip
+    both checks (a capture allows no host copy or synchronisation)."""
+    _DEBUG[0] = bool(on)
+
+
+def debug_enabled() -> bool:
+    return _DEBUG[0]
+
+
+def _validate_cu_host(cu, T):
+    """Host check of cu_seqlens contents (debug mode): the flash-attn
+    convention, cu[0] = 0, cu[-1] = T, nondecreasing."""
+    import numpy as np
+    cu = np.asarray(cu)
+    if cu.ndim != 1 or cu.size < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
+    if int(cu[0]) != 0 or int(cu[-1]) != T:
+        raise ValueError(f"cu_seqlens must start at 0 and end at T={T} (got {int(cu[0])} ... {int(cu[-1])})")
+    bad = np.nonzero(np.diff(cu.astype(np.int64)) < 0)[0]
+    if bad.size:
+        raise ValueError(f"cu_seqlens must be nondecreasing (cu[{bad[0]}] = {int(cu[bad[0]])} > "
+                         f"cu[{bad[0] + 1}] = {int(cu[bad[0] + 1])})")
+
+
+def _read_ws_error(wsp, wsn, device, stream_handle) -> int:
+    """The workspace's error word as an mscan status (0, or 5 when a look-back
+    wait of the last call that chained tiles through it gave up); waits for the
+    work queued on the stream before it."""
+    flag = torch.zeros(1, dtype=torch.int32, device=device)
+    _check("mscan_workspace_error", lib.mscan_workspace_error(wsp, wsn, flag.data_ptr(), stream_handle))
+    return int(flag.item())
+
+
+def _raise_if_tripped(fn, wsp, wsn, device, stream_handle):
+    code = _read_ws_error(wsp, wsn, device, stream_handle)
+    if code != 0:
+        raise MscanError(fn, code, "outputs that needed the missing carry are NaN")
+
+
+def stream_ceiling(srcs, dsts) -> None:
+    """Enqueue the streaming diagnostic kernel (mscan_stream_ceiling): reads
+    every tensor of `srcs`, writes every tensor of `dsts` (contiguous fp32 GPU
+    tensors of one size, a multiple of 4 elements)."""
+    n = srcs[0].numel()
+    for t in list(srcs) + list(dsts):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+            raise ValueError("stream_ceiling takes contiguous fp32 GPU tensors of one size")
+    P = ctypes.c_void_p
+    sa = (P * len(srcs))(*[t.data_ptr() for t in srcs])
+    da = (P * len(dsts))(*[t.data_ptr() for t in dsts])
+    _check("mscan_stream_ceiling", lib.mscan_stream_ceiling(sa, len(srcs), da, len(dsts), n,
+                                                            _stream_handle(srcs[0].device)))
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """mscan status of a workspace tensor's error word (see mscan_workspace_error)."""
+    return _read_ws_error(ws.data_ptr(), ws.numel() * ws.element_size(), ws.device, _stream_handle(ws.device))
+
+
 def _segments(cu_seqlens, device, T):
     if cu_seqlens is None:
         return None, 1
@@ -215,6 +321,8 @@ def _segments(cu_seqlens, device, T):
         raise ValueError("cu_seqlens must be contiguous")
     if cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens needs at least two entries")
+    if _DEBUG[0] and not torch.cuda.is_current_stream_capturing():  # no host copy inside a graph capture
+        _validate_cu_host(cu_seqlens.cpu().numpy(), T)
     return cu_seqlens, cu_seqlens.numel() - 1
 
 
@@ -231,9 +339,14 @@ def _h0(h0, nseg, rows, tail, name="h0"):
     return h0
 
 
-def _check(fn, status):
+def _check(fn, status, ws=None):
+    """Raise on a failed call; in debug mode also when a call that chained
+    tiles through the workspace ws = (ptr, bytes, device, stream) had a wait
+    give up."""
     if status != 0:
         raise MscanError(fn, status, lib.mscan_last_hip_error().decode() if status == 4 else "")
+    if ws is not None and ws[0] and _DEBUG[0] and not torch.cuda.is_current_stream_capturing():
+        _raise_if_tripped(fn, *ws)
 
 
 def _in_dtype(t, name):
@@ -285,10 +398,11 @@ def _scan_fwd(g, x, h0, cu_seqlens, reverse, out, gate):
     sh = _stream_handle(dev)
     wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_FWD)
     if gate == GATE_NONE:
-        _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h), wsp, wsn, sh))
+        _check("scan_fwd", lib.scan_fwd(ctypes.byref(prob), dt, _ptr(g), _ptr(x), _ptr(h0), _ptr(h), wsp, wsn, sh),
+               (wsp, wsn, dev, sh))
     else:
         _check("scan_fwd_gated", lib.scan_fwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(x), _ptr(h0), _ptr(h),
-                                                    wsp, wsn, sh))
+                                                    wsp, wsn, sh), (wsp, wsn, dev, sh))
     return h
 
 
@@ -312,14 +426,13 @@ def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
         for t, n in ((h, "h"), (dy, "dy")):
             if _rows_view(t, n)[2] != stride:
                 raise ValueError("g, h and dy must share the row stride")
-    if stride != T:
-        raise ValueError("scan_bwd takes contiguous rows")
     dt = _in_dtype(g, "g")
     dev = g.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     h0 = _h0(h0, nseg, rows, ())
-    dx = torch.empty(h.shape, dtype=torch.float32, device=dev)
-    dg = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    # strided rows: the gradients share the inputs' row stride
+    dx = _out_rows(h.shape, rows, T, stride, dev)
+    dg = _out_rows(h.shape, rows, T, stride, dev)
     dh0 = torch.empty((nseg, rows), dtype=torch.float32, device=dev) if need_dh0 else None
     if rows == 0 or T == 0:
         if dh0 is not None:
@@ -330,10 +443,10 @@ def _scan_bwd(g, h, dy, h0, cu_seqlens, reverse, need_dh0, gate):
     wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_BWD)
     if gate == GATE_NONE:
         _check("scan_bwd", lib.scan_bwd(ctypes.byref(prob), dt, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dx),
-                                        _ptr(dg), _ptr(dh0), wsp, wsn, sh))
+                                        _ptr(dg), _ptr(dh0), wsp, wsn, sh), (wsp, wsn, dev, sh))
     else:
         _check("scan_bwd_gated", lib.scan_bwd_gated(ctypes.byref(prob), dt, gate, _ptr(g), _ptr(h), _ptr(dy), _ptr(h0),
-                                                    _ptr(dx), _ptr(dg), _ptr(dh0), wsp, wsn, sh))
+                                                    _ptr(dx), _ptr(dg), _ptr(dh0), wsp, wsn, sh), (wsp, wsn, dev, sh))
     return dx, dg, dh0
 
 
@@ -351,12 +464,12 @@ def _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, gate):
     if log_a.shape != log_b.shape or log_a.dtype != torch.float32 or log_b.dtype != torch.float32:
         raise ValueError("log_a and log_b must be float32 tensors of one shape")
     rows, T, stride = _rows_view(log_a, "log_a")
-    if _rows_view(log_b, "log_b")[2] != stride or stride != T:
-        raise ValueError("scan_log_fwd takes contiguous rows")
+    if _rows_view(log_b, "log_b")[2] != stride:
+        raise ValueError("log_a and log_b must share the row stride")
     dev = log_a.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     log_h0 = _h0(log_h0, nseg, rows, (), "log_h0")
-    h = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
+    h = _out_rows(log_a.shape, rows, T, stride, dev)
     if rows == 0 or T == 0:
         return h
     prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
@@ -364,10 +477,10 @@ def _scan_log_fwd(log_a, log_b, log_h0, cu_seqlens, reverse, gate):
     wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_LOG_FWD)
     if gate == GATE_NONE:
         _check("scan_log_fwd", lib.scan_log_fwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(log_h0), _ptr(h),
-                                                wsp, wsn, sh))
+                                                wsp, wsn, sh), (wsp, wsn, dev, sh))
     else:
         _check("scan_log_fwd_gated", lib.scan_log_fwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b),
-                                                            _ptr(log_h0), _ptr(h), wsp, wsn, sh))
+                                                            _ptr(log_h0), _ptr(h), wsp, wsn, sh), (wsp, wsn, dev, sh))
     return h
 
 
@@ -389,13 +502,11 @@ def _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, ga
     for t, n in ((log_b, "log_b"), (h, "h"), (dy, "dy")):
         if _rows_view(t, n)[2] != stride:
             raise ValueError("log_a, log_b, h and dy must share the row stride")
-    if stride != T:
-        raise ValueError("scan_log_bwd takes contiguous rows")
     dev = log_a.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     log_h0 = _h0(log_h0, nseg, rows, (), "log_h0")
-    dla = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
-    dlb = torch.empty(log_a.shape, dtype=torch.float32, device=dev)
+    dla = _out_rows(log_a.shape, rows, T, stride, dev)
+    dlb = _out_rows(log_a.shape, rows, T, stride, dev)
     dlh0 = torch.empty((nseg, rows), dtype=torch.float32, device=dev) if need_dh0 else None
     if rows == 0 or T == 0:
         if dlh0 is not None:
@@ -406,11 +517,12 @@ def _scan_log_bwd(log_a, log_b, h, dy, log_h0, cu_seqlens, reverse, need_dh0, ga
     wsp, wsn = _scalar_ws(dev, sh, prob, OP_SCAN_LOG_BWD)
     if gate == GATE_NONE:
         _check("scan_log_bwd", lib.scan_log_bwd(ctypes.byref(prob), _ptr(log_a), _ptr(log_b), _ptr(h), _ptr(dy),
-                                                _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), wsp, wsn, sh))
+                                                _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0), wsp, wsn, sh),
+               (wsp, wsn, dev, sh))
     else:
         _check("scan_log_bwd_gated", lib.scan_log_bwd_gated(ctypes.byref(prob), gate, _ptr(log_a), _ptr(log_b), _ptr(h),
                                                             _ptr(dy), _ptr(log_h0), _ptr(dla), _ptr(dlb), _ptr(dlh0),
-                                                            wsp, wsn, sh))
+                                                            wsp, wsn, sh), (wsp, wsn, dev, sh))
     return dla, dlb, dlh0
 
 
@@ -423,49 +535,52 @@ def _mat_dims(A, Bh, nameB):
     if A.shape[-2] != k or Bh.shape[-2] != k or A.shape[:-2] != Bh.shape[:-2]:
         raise ValueError(f"A must be [..., T, k, k] and {nameB} [..., T, k, v] with matching leading axes")
     rows, T, stride = _rows_view(A, "A", tail=2)
-    if _rows_view(Bh, nameB, tail=2)[2] != stride or stride != T:
-        raise ValueError("matrix scans take contiguous rows")
-    return rows, T, k, v
+    if _rows_view(Bh, nameB, tail=2)[2] != stride:
+        raise ValueError(f"A and {nameB} must share the row stride (in time steps)")
+    return rows, T, stride, k, v
 
 
 def matrix_affine_scan_fwd(A, B, h0=None, cu_seqlens=None, reverse=False):
     """h_t = A_t h_{t-1} + B_t with k x k transitions and k x v states."""
-    rows, T, k, v = _mat_dims(A, B, "B")
+    rows, T, stride, k, v = _mat_dims(A, B, "B")
     dev = A.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     h0 = _h0(h0, nseg, rows, (k, v))
-    h = torch.empty(B.shape, dtype=torch.float32, device=dev)
+    h = _out_rows(B.shape, rows, T, stride, dev, (k, v))
     if rows == 0 or T == 0:
         return h
-    prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_FWD, k, v))
     _check("matrix_affine_scan_fwd", lib.matrix_affine_scan_fwd(
-        ctypes.byref(prob), k, v, _ptr(A), _ptr(B), _ptr(h0), _ptr(h), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+        ctypes.byref(prob), k, v, _ptr(A), _ptr(B), _ptr(h0), _ptr(h), _ptr(ws), ws.numel(), ctypes.c_void_p(sh)),
+        (_ptr(ws), ws.numel(), dev, sh))
     return h
 
 
 def matrix_affine_scan_bwd(A, h, dy, h0=None, cu_seqlens=None, reverse=False, need_dh0=True):
     """Adjoint of matrix_affine_scan_fwd: (dA, dB, dh0)."""
-    rows, T, k, v = _mat_dims(A, h, "h")
+    rows, T, stride, k, v = _mat_dims(A, h, "h")
     if dy.shape != h.shape or dy.dtype != torch.float32:
         raise ValueError("dy must match h")
+    if _rows_view(dy, "dy", tail=2)[2] != stride:
+        raise ValueError("A, h and dy must share the row stride (in time steps)")
     dev = A.device
     cu, nseg = _segments(cu_seqlens, dev, T)
     h0 = _h0(h0, nseg, rows, (k, v))
-    dA = torch.empty(A.shape, dtype=torch.float32, device=dev)
-    dB = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    dA = _out_rows(A.shape, rows, T, stride, dev, (k, k))
+    dB = _out_rows(h.shape, rows, T, stride, dev, (k, v))
     dh0 = torch.empty((nseg, rows, k, v), dtype=torch.float32, device=dev) if need_dh0 else None
     if rows == 0 or T == 0:
         if dh0 is not None:
             dh0.zero_()
         return dA, dB, dh0
-    prob = Problem(rows, T, T, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
+    prob = Problem(rows, T, stride, cu.data_ptr() if cu is not None else None, nseg, int(bool(reverse)))
     sh = _stream_handle(dev)
     ws = _workspace(dev, sh, workspace_bytes(prob, OP_MATRIX_BWD, k, v))
     _check("matrix_affine_scan_bwd", lib.matrix_affine_scan_bwd(
         ctypes.byref(prob), k, v, _ptr(A), _ptr(h), _ptr(dy), _ptr(h0), _ptr(dA), _ptr(dB), _ptr(dh0),
-        _ptr(ws), ws.numel(), ctypes.c_void_p(sh)))
+        _ptr(ws), ws.numel(), ctypes.c_void_p(sh)), (_ptr(ws), ws.numel(), dev, sh))
     return dA, dB, dh0
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+
 #include "mscan.h"
 #include "mscan_device.hpp"
 #include "mscan_launch.hpp"
@@ -373,6 +374,92 @@ mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, con
   return hip_status(mscan::launch_matrix(a, k, v, true, st));
 }
 
+mscan_status mscan_stream_ceiling(const float* const* src, int nsrc, float* const* dst, int ndst, size_t n,
+                                  void* stream) {
+  if (!src || !dst || nsrc < 1 || nsrc > 4 || ndst < 1 || ndst > 3 || n == 0 || (n & 3u)) return MSCAN_ERR_INVALID;
+  for (int i = 0; i < nsrc; ++i)
+    if (!src[i] || !aligned16(src[i])) return MSCAN_ERR_INVALID;
+  for (int i = 0; i < ndst; ++i)
+    if (!dst[i] || !aligned16(dst[i])) return MSCAN_ERR_INVALID;
+  const bool mix = (nsrc == 1 && ndst == 1) || (nsrc == 2 && ndst == 1) || (nsrc == 3 && ndst == 1) ||
+                   (nsrc == 1 && ndst == 2) || (nsrc == 2 && ndst == 2) || (nsrc == 3 && ndst == 2) ||
+                   (nsrc == 4 && ndst == 2) || (nsrc == 4 && ndst == 3);
+  if (!mix) return MSCAN_ERR_UNSUPPORTED;
+  return hip_status(mscan::launch_stream(src, nsrc, dst, ndst, n / 4, (hipStream_t)stream));
+}
+
+mscan_status mscan_workspace_error(const void* ws, size_t ws_bytes, int32_t* flag_out, void* stream) {
+  if (!ws || !aligned16(ws) || ws_bytes < mscan::kWsHeaderBytes || !flag_out || ((uintptr_t)flag_out & 3u))
+    return MSCAN_ERR_INVALID;
+  return hip_status(mscan::launch_read_error(ws, flag_out, (hipStream_t)stream));
+}
+
+mscan_status mscan_debug_partial_fwd(const mscan_problem* prob, int k, int v, const float* a, const float* b,
+                                     float* out, void* ws, size_t ws_bytes, int64_t first_block, int64_t nblocks,
+                                     uint32_t spin_limit, void* stream) {
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (!matrix_shape_ok(k, v)) return MSCAN_ERR_UNSUPPORTED;
+  if (!a || !b || !out || !aligned16(a) || !aligned16(b) || !aligned16(out)) return MSCAN_ERR_INVALID;
+  if (!ws || !aligned16(ws)) return MSCAN_ERR_WORKSPACE;
+  // the call's grid, which must chain tiles (else there is no wait to run out)
+  const bool scalar = k == 1 && v == 1;
+  int64_t per_row = 0;
+  bool chained = false;
+  size_t need = 0;
+  if (scalar) {
+    per_row = scalar_tiles_for(prob, MSCAN_F32);
+    chained = !mscan::scalar_short_rows(prob->T, prob->row_stride) && mscan::scalar_uses_lookback(prob->rows, per_row);
+    need = scalar_ws_bytes(prob, 3, false);
+  } else if (mscan::matrix_core_shape(k, v)) {
+    per_row = mscan::matrix_core_chunks(prob->T, false, k, v);
+    chained = true;
+    need = matrix_ws_bytes(prob, k, v);
+  } else {
+    per_row = mscan::matrix_tiles(prob->T, k, v, false);
+    chained = mscan::scalar_uses_lookback(prob->rows, per_row);
+    need = matrix_ws_bytes(prob, k, v);
+  }
+  if (!chained) return MSCAN_ERR_UNSUPPORTED;
+  if ((s = check_grid(prob, per_row)) != MSCAN_OK) return s;
+  if (ws_bytes < need) return MSCAN_ERR_WORKSPACE;
+  const int64_t total = prob->rows * per_row;
+  if (first_block < 0 || nblocks < 1 || first_block + nblocks > total) return MSCAN_ERR_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  if (scalar) {
+    mscan::ScalarArgs sa{};
+    sa.g = a;
+    sa.b = b;
+    sa.out0 = out;
+    sa.cu = prob->cu_seqlens;
+    sa.nseg = prob->nseg;
+    sa.rev = prob->reverse;
+    sa.rows = prob->rows;
+    sa.T = prob->T;
+    sa.stride = prob->row_stride;
+    sa.ws = ws;
+    sa.blk0 = (uint32_t)first_block;
+    sa.nblk = (uint32_t)nblocks;
+    sa.spin = spin_limit;
+    return hip_status(mscan::launch_scalar(sa, MSCAN_F32, false, st));
+  }
+  mscan::MatArgs ma{};
+  ma.A = a;
+  ma.B = b;
+  ma.out0 = out;
+  ma.cu = prob->cu_seqlens;
+  ma.nseg = prob->nseg;
+  ma.rev = prob->reverse;
+  ma.rows = prob->rows;
+  ma.T = prob->T;
+  ma.stride = prob->row_stride;
+  ma.ws = ws;
+  ma.blk0 = (uint32_t)first_block;
+  ma.nblk = (uint32_t)nblocks;
+  ma.spin = spin_limit;
+  return hip_status(mscan::launch_matrix(ma, k, v, false, st));
+}
+
 const char* mscan_status_string(int status) {
   switch (status) {
     case MSCAN_OK: return "ok";
@@ -380,6 +467,7 @@ const char* mscan_status_string(int status) {
     case MSCAN_ERR_UNSUPPORTED: return "unsupported configuration";
     case MSCAN_ERR_WORKSPACE: return "workspace missing or too small";
     case MSCAN_ERR_HIP: return "HIP launch error";
+    case MSCAN_ERR_TIMEOUT: return "a look-back wait gave up (outputs that needed the missing carry are NaN)";
     default: return "unknown status";
   }
 }

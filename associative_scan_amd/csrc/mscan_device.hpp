@@ -10,13 +10,20 @@
 //
 // Zero transitions. A zero P is treated as "erases everything before": the
 // composition keeps the later map unchanged instead of multiplying an earlier
-// Q by zero. For finite data this is exactly the arithmetic result. It also
-// makes sequence starts hard boundaries (they enter the scan as P = 0), so a
-// NaN or Inf in one packed sequence can never reach the next one.
+// Q by zero. That is how a reset a_t = 0 is defined ("Our RG-LRU GPU audit",
+// "Exact real chunk algebra": a reset is encoded as a zero transition and
+// leaves nothing of the prefix), Inf or NaN before it included; for finite
+// data it is also the arithmetic result. It makes sequence starts hard
+// boundaries too (they enter the scan as P = 0), so a NaN or Inf in one
+// packed sequence can never reach the next one. (A product of nonzero gates
+// that underflows to 0 is treated the same way; for a finite prefix that is
+// again the arithmetic result.)
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mscan_launch.hpp"
 
 namespace mscan {
 
@@ -203,6 +210,7 @@ __device__ __forceinline__ float lin_apply(float P, float Q, float h) {
 // of any shape, can look valid.
 // ---------------------------------------------------------------------------
 enum : int { kHdrError = 3, kHdrWords = 32 };
+static_assert(kHdrError == kHdrErrorWord && kHdrWords * 4 == kWsHeaderBytes, "workspace header layout");
 enum : uint32_t { kTagAgg = 1, kTagIncl = 2 };
 
 __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
@@ -238,9 +246,14 @@ __device__ __forceinline__ Workspace ws_view(void* ws) {
   return w;
 }
 
-// Upper bound on look-back polls before a wave gives up (then the header's
-// error word is set and the carry is taken as zero, so the kernel still ends).
+// Upper bound on look-back polls before a wave gives up. A wait can only run
+// out if a predecessor never publishes (a launch that runs part of a grid, or
+// a workspace shared by calls that overlap); the wave then sets the header's
+// error word and takes a NaN carry, so the kernel still ends and every output
+// that depended on the missing carry reads NaN instead of a plausible wrong
+// value. A call may ask for a smaller limit (0 = this default).
 constexpr uint32_t kSpinLimit = 1u << 22;
+__device__ __forceinline__ uint32_t spin_limit(uint32_t requested) { return requested ? requested : kSpinLimit; }
 
 // ---------------------------------------------------------------------------
 // Scan "ops": one summary type S (a map from the state before a span to the
@@ -267,9 +280,10 @@ struct LinOps {
   __device__ static __forceinline__ S of_carry(const C& c) { return S{{0.f, c.v[0]}}; }
   __device__ static __forceinline__ C carry_of_hard(const S& s) { return C{{s.v[1]}}; }
   __device__ static __forceinline__ S elem(float a, float b) { return S{{a, b}}; }
-  // a sequence's first step with h0 injected, as a hard step (a', b')
+  // a sequence's first step with h0 injected, as a hard step (a', b'); a
+  // zero gate there is a reset and drops h0
   __device__ static __forceinline__ void first_ab(float& a, float& b, float h0, bool) {
-    b = __builtin_fmaf(a, h0, b);
+    b = (a != 0.f) ? __builtin_fmaf(a, h0, b) : b;
     a = 0.f;
   }
   __device__ static __forceinline__ float out(const C& c) { return c.v[0]; }
@@ -325,9 +339,10 @@ struct LogOps {
   __device__ static __forceinline__ S of_carry(const C& c) { return S{{-__builtin_inff(), c.v[0], c.v[1]}}; }
   __device__ static __forceinline__ C carry_of_hard(const S& s) { return C{{s.v[1], s.v[2]}}; }
   __device__ static __forceinline__ S elem(float a, float b) { return S{{a, b, 1.f}}; }
-  // a sequence's first step with log h0 injected, as a hard step (-inf, b')
+  // a sequence's first step with log h0 injected, as a hard step (-inf, b');
+  // log a = -inf there is a reset and drops h0
   __device__ static __forceinline__ void first_ab(float& a, float& b, float h0, bool has_h0) {
-    if (has_h0) {
+    if (has_h0 && a != -__builtin_inff()) {
       float m, s;
       lse_pair(a + h0, 1.f, b, 1.f, m, s);
       b = (m == -__builtin_inff()) ? m : m + __logf(s);
@@ -370,9 +385,11 @@ __device__ __forceinline__ void scan_step(typename Ops::S& x, bool valid) {
 //              T >= 16384.)
 // Either way a tile waits only on lower-numbered blocks of its own row, which
 // were dispatched earlier, so the look-back always makes progress.
+// blk0: index of this launch's first block in the call's numbering (nonzero
+// only when a launch runs part of the grid).
 template <bool TILE_MAJOR>
-__device__ __forceinline__ void tile_of_block(int64_t rows, int ntiles, int64_t& r, int& c) {
-  const uint32_t b = blockIdx.x;
+__device__ __forceinline__ void tile_of_block(int64_t rows, int ntiles, uint32_t blk0, int64_t& r, int& c) {
+  const uint32_t b = blockIdx.x + blk0;
   if constexpr (TILE_MAJOR) {
     const uint32_t q = b / (uint32_t)rows;
     c = (int)q;
@@ -391,7 +408,7 @@ __device__ __forceinline__ void tile_of_block(int64_t rows, int ntiles, int64_t&
 // is `row_desc`.
 // ---------------------------------------------------------------------------
 template <class Ops, bool FAST = false>
-__device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c) {
+__device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t* row_desc, int c, uint32_t limit) {
   using S = typename Ops::S;
   constexpr int ND = Ops::NS + Ops::NC;
   const int l = lane_id();
@@ -473,9 +490,12 @@ __device__ __forceinline__ typename Ops::C lookback(Workspace w, const uint64_t*
       const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1ull);
       const uint64_t not_ready = __ballot(!ready) & need;
       if (not_ready == 0) break;
-      if (++spins > kSpinLimit) {
+      if (++spins > limit) {
         if (l == 0) st_u32(w.hdr + kHdrError, 1u);
-        return Ops::cident();
+        typename Ops::C bad;
+#pragma unroll
+        for (int i = 0; i < Ops::NC; ++i) bad.v[i] = __builtin_nanf("");
+        return bad;
       }
       __builtin_amdgcn_s_sleep(1);
     }

@@ -22,6 +22,10 @@ struct ScalarArgs {
   int64_t rows, T, stride;
   int32_t ntiles;       // tiles per row (set by the launcher)
   void* ws;             // workspace (only used when ntiles > 1)
+  // partial launches (a test hook; 0 in every normal call): run blocks
+  // [blk0, blk0 + nblk) of the call's grid, with look-back waits giving up
+  // after `spin` polls (0 = the default limit)
+  uint32_t blk0, nblk, spin;
 };
 
 // Elements per tile of the scalar kernels, and tiles per row for a given T.
@@ -64,7 +68,11 @@ struct MatArgs {
   void* ws;
   int32_t k, v;         // block sizes (read by the matrix-core kernels; the
                         // VALU kernels take them as template parameters)
+  uint32_t blk0, nblk, spin;  // partial launches, as for ScalarArgs
 };
+
+// Grid of a chained call: the whole grid, or the part a partial launch asks for.
+inline unsigned launch_blocks(uint64_t total, uint32_t nblk) { return (unsigned)(nblk ? nblk : total); }
 
 // (k, v) served by the VALU kernels (scan_matrix.hip): (2,1), (2,2), (4,1).
 bool matrix_valu_shape(int k, int v);
@@ -86,7 +94,15 @@ hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st);
 // callers may capture it in a graph).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 
-// Workspace header bytes (control words) ahead of the per-tile descriptors.
+// Workspace header bytes (control words) ahead of the per-tile descriptors,
+// and the header word a kernel sets when one of its waits gives up.
 constexpr size_t kWsHeaderBytes = 128;
+constexpr int kHdrErrorWord = 3;
+// Copy the error word as an mscan status (0 or 5) to *dst, on `st`.
+hipError_t launch_read_error(const void* ws, int32_t* dst, hipStream_t st);
+// Streaming diagnostic: read nsrc arrays, write ndst arrays of n4 16-byte
+// units each ((nsrc, ndst) in {(1,1), (2,1), (3,1), (1,2), (2,2), (3,2),
+// (4,2), (4,3)}).
+hipError_t launch_stream(const float* const* src, int nsrc, float* const* dst, int ndst, size_t n4, hipStream_t st);
 
 }  // namespace mscan

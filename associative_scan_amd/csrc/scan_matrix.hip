@@ -200,7 +200,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     // tile-major, except the k = 2 backward, which streams faster row-major
     // (4096 rows x T = 8192: (2,1) 0.341 vs 0.360 ms, (2,2) 0.491 vs 0.546 ms;
     // the (4,1) backward is 19% slower that way)
-    tile_of_block<!(BWD && K == 2)>(a.rows, a.ntiles, r, c);
+    tile_of_block<!(BWD && K == 2)>(a.rows, a.ntiles, a.blk0, r, c);
   }
   const int64_t T = a.T;
   const int64_t row0 = r * a.stride;  // first step of the row
@@ -329,11 +329,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
         SA::get(stA, s, X);
         SB::get(stB, s, Y);
         if (first) {
-          float h0v[KV], y[KV];
-          load_h0(segk[e], h0v);
-          Ops::template mul<V>(X, h0v, Y, y);
+          // A h0 + B, or B alone where A = 0 (a reset drops h0)
+          if (!Ops::zero_k(X)) {
+            float h0v[KV], y[KV];
+            load_h0(segk[e], h0v);
+            Ops::template mul<V>(X, h0v, Y, y);
 #pragma unroll
-          for (int i = 0; i < KV; ++i) Y[i] = y[i];
+            for (int i = 0; i < KV; ++i) Y[i] = y[i];
+          }
 #pragma unroll
           for (int i = 0; i < KK; ++i) X[i] = 0.f;
         }
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
             }
           }
         }
-        if (c > 0) carry = lookback<Ops, true>(ws, rd, c);
+        if (c > 0) carry = lookback<Ops, true>(ws, rd, c, spin_limit(a.spin));
         if (l == 0) {
           if (!hard) {
             const S tagg = (WAVES > 1) ? tile_agg() : wagg;
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
         if constexpr (!BWD) {
           float X[KK];
           SA::get(stA, s, X);
-          if (first) {
+          if (first && !Ops::zero_k(X)) {
             float h0v[KV], y[KV];
             load_h0(segk[e], h0v);
             Ops::template mul<V>(X, h0v, Y, y);
@@ -531,8 +534,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
           SB::put(stB, s, st.v);  // dB = lam over dy
           SA::put(stA, s, dA);    // dA over A
           if (a.dh0 && (lastm & (1u << e))) {
-            // dh0 = A_s^T lam_s
+            // dh0 = A_s^T lam_s (0 where A_s = 0: nothing flows through a reset)
             float* dst = a.dh0 + ((int64_t)segk[e] * a.rows + r) * KV;
+            const bool reset = Ops::zero_k(Aown);
 #pragma unroll
             for (int p = 0; p < K; ++p)
 #pragma unroll
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int q = 0; q < K; ++q) acc = __builtin_fmaf(Aown[q * K + p], st.v[q * V + u], acc);
-                dst[p * V + u] = acc;
+                dst[p * V + u] = reset ? 0.f : acc;
               }
           }
         }
@@ -590,7 +594,7 @@ static hipError_t launch_mat(const MatArgs& a0, hipStream_t st) {
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(MatOps<K, V>::NS + MatOps<K, V>::NC);
     const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
     if (z != hipSuccess) return z;
-    const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
+    const dim3 grid(launch_blocks((uint64_t)a.rows * (uint64_t)a.ntiles, a.nblk));
     if (varlen) hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, true, kMatLookback, W, E>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_matrix<K, V, BWD, REV, false, kMatLookback, W, E>), grid, block, 0, st, a);
   }

@@ -4,9 +4,12 @@
 // page's kernel envelope is k, v in {1, 2, 4, 8, 16}), and its reverse adjoint
 // (same page, "Autograd integration and the reversed-scan backward").
 //
-// Each step is one or two small dense products, run on the matrix cores in
-// IEEE fp32 (fp32 inputs, fp32 accumulation: the precision the page's TF32 /
-// IEEE guard asks for at k = 16). Two register tiles:
+// Each step is one or two small dense products, run on the matrix cores with
+// fp32 operands and fp32 accumulation (no reduced-precision input rounding, as
+// the page's TF32 / IEEE guard asks at k = 16; the accumulation inside one
+// instruction is the matrix core's, not a chain of separately rounded FMAs,
+// so results agree with the VALU kernels to rounding, not bit for bit).
+// Two register tiles:
 //   Tile16: one 16 x 16 block per wave (k or v above 4), products on
 //           v_mfma_f32_16x16x4_f32;
 //   Tile4 : sixteen 4 x 4 blocks per wave (k, v <= 4), products on
@@ -37,7 +40,10 @@
 // (Tile4) gives a wave 16 S steps of one row, S per group of 4 lanes.
 // Forward element (X, Y) = (A_t, B_t); backward element = (A of the previous
 // step in processing order, transposed; dy_t). A sequence's first step in
-// processing order is hard: forward h = A h0 + B, backward lam = dy.
+// processing order is hard: forward h = A h0 + B, backward lam = dy. So is a
+// step whose X is all zero (a reset, "Our RG-LRU GPU audit", "Exact real chunk
+// algebra"): it takes Y alone, whatever the state before it holds (Inf and NaN
+// included), and a reset on a sequence's first step drops h0 (and gets no dh0).
 #include <algorithm>
 
 #include "mscan_device.hpp"
@@ -46,12 +52,21 @@
 namespace mscan {
 
 __device__ __forceinline__ v4f mc_zero() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ v4f mc_nan() {
+  const float q = __builtin_nanf("");
+  return v4f{q, q, q, q};
+}
+
+// whether any of this lane's four values is nonzero
+__device__ __forceinline__ bool mc_nonzero(v4f x) { return x.x != 0.f || x.y != 0.f || x.z != 0.f || x.w != 0.f; }
 
 // ---------------------------------------------------------------------------
 // register tiles
 // ---------------------------------------------------------------------------
 struct Tile16 {
   static constexpr int E = 16;  // tile edge
+  // the block is all zero (wave-uniform: the wave holds the whole block)
+  __device__ static __forceinline__ bool zero(v4f x) { return __ballot(mc_nonzero(x)) == 0ull; }
   __device__ static __forceinline__ int dr0() { return 4 * (int)((threadIdx.x >> 4) & 3); }
   __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 15); }
   // acc + M P with M in R layout and P in D layout; result in D layout
@@ -79,6 +94,10 @@ struct Tile16 {
 struct Tile4 {
   static constexpr int E = 4;
   __device__ static __forceinline__ int lrow() { return (int)(threadIdx.x >> 2); }  // lane group (block)
+  // this lane group's block is all zero (uniform across the group)
+  __device__ static __forceinline__ bool zero(v4f x) {
+    return ((__ballot(mc_nonzero(x)) >> (4 * lrow())) & 0xfull) == 0ull;
+  }
   __device__ static __forceinline__ int dr0() { return 0; }
   __device__ static __forceinline__ int dc() { return (int)(threadIdx.x & 3); }
   __device__ static __forceinline__ v4f mm(v4f mR, v4f pD, v4f acc) {
@@ -274,8 +293,8 @@ __device__ __forceinline__ void mc_publish(uint64_t* w, v4f v) {
   st_u64(p + 3 * 64, pack_word(kMcTag, v.w));
 }
 // h_out of a chunk once every lane sees all four of its words published;
-// false after the spin limit (then the header's error word is set)
-__device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, v4f& v) {
+// false after `limit` polls (then the header's error word is set)
+__device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, uint32_t limit, v4f& v) {
   const uint64_t* p = w + threadIdx.x;
   for (uint32_t spins = 0;; ++spins) {
     const uint64_t a = ld_u64(p + 0 * 64), b = ld_u64(p + 1 * 64), c = ld_u64(p + 2 * 64), d = ld_u64(p + 3 * 64);
@@ -285,7 +304,7 @@ __device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, v4f& v
       v = v4f{word_val(a), word_val(b), word_val(c), word_val(d)};
       return true;
     }
-    if (spins > kSpinLimit) {
+    if (spins > limit) {
       if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
       return false;
     }
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
   int64_t r;
   int c;
-  tile_of_block<true>(a.rows, a.ntiles, r, c);
+  tile_of_block<true>(a.rows, a.ntiles, a.blk0, r, c);
   McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
   const int64_t j0 = (int64_t)c * S;
   const int n = (int)min((int64_t)S, a.T - j0);
@@ -334,15 +353,17 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   wait_stage_loads();
   // Sequence boundaries, folded into the registers so that the step loops
   // below hold no loads (a load in them would make every step wait for the
-  // stores before it): forward, a first step's value A h0 + B; backward, the
-  // h_prev of a sequence's forward-first step is h0.
-  if (a.h0 && (BWD ? lastm : firstm)) {
+  // stores before it): forward, a first step's value A h0 + B (B alone at a
+  // reset, an all-zero A); backward, the h_prev of a sequence's forward-first
+  // step is h0.
+  const uint32_t foldm = BWD ? lastm : firstm;
+  if (a.h0 && foldm) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      if (((BWD ? lastm : firstm) >> s) & 1u) {
+      if ((foldm >> s) & 1u) {
         const int sk = wk.seg_of(j0 + s);
         if constexpr (!BWD) {
-          Y[s] = TL::mm(X[s], wk.sh.ldB_D(wk.h0p(sk)), Y[s]);
+          if (!TL::zero(X[s])) Y[s] = TL::mm(X[s], wk.sh.ldB_D(wk.h0p(sk)), Y[s]);
         } else {
           H[s] = wk.sh.ldB_R(wk.h0p(sk));
         }
@@ -355,16 +376,20 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
       if ((lastm >> s) & 1u) H[s] = mc_zero();
   }
 
-  // ---- chunk summary (a sequence's first step is hard: P = 0, Q = its value)
-  const bool hard = firstm != 0u, first0 = (firstm & 1u) != 0u;
+  // ---- chunk summary (a sequence's first step and a reset, a step in the row
+  // whose transition operand is all zero, are hard: P = 0, Q = its value)
+  uint32_t zerom = 0u;
   v4f P = tile_ident<TL>(), Q = mc_zero();
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool f = (firstm >> s) & 1u;
+    zerom |= (uint32_t)(s < n && TL::zero(X[s])) << s;
+    const bool f = ((firstm | zerom) >> s) & 1u;
     const v4f Pn = TL::mm(X[s], P, mc_zero()), Qn = TL::mm(X[s], Q, Y[s]);
     P = f ? mc_zero() : Pn;
     Q = f ? Y[s] : Qn;
   }
+  const uint32_t hardm = firstm | zerom;
+  const bool hard = hardm != 0u, first0 = (hardm & 1u) != 0u;
 
   // ---- carry-in from the chunk before, h_out for the chunk after
   uint32_t* hdr = (uint32_t*)a.ws;
@@ -375,7 +400,8 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   const v4f PR = (publish && !hard) ? TL::d_to_r(s_t, P) : mc_zero();  // off the chain
   v4f hin = mc_zero();
   if (!first0) {
-    if (!mc_wait(pub + (me - 1) * 256, hdr, hin)) hin = mc_zero();
+    // a wait that gave up leaves NaN, never a plausible wrong carry
+    if (!mc_wait(pub + (me - 1) * 256, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
   }
   if (publish && !hard) mc_publish(pub + me * 256, TL::mm(PR, hin, Q));
 
@@ -383,7 +409,7 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   v4f h = hin;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool first = (firstm >> s) & 1u;
+    const bool first = (hardm >> s) & 1u;
     const v4f hn = TL::mm(X[s], h, Y[s]);
     h = first ? Y[s] : hn;  // h holds lam in the backward
     if constexpr (BWD) {
@@ -396,10 +422,12 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
         wk.sh.stA_D(wk.blkA(a.out1, t), dA);
       }
       if (((lastm >> s) & 1u) && a.dh0 && s < n) {
-        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
+        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout); 0 where
+        // A_s = 0: nothing flows through a reset
         const int64_t j = j0 + s;
-        const v4f d = TL::mm(wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j))), h, mc_zero());
-        wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), d);
+        const v4f As = wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j)));
+        const v4f d = TL::mm(As, h, mc_zero());
+        wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(j) * a.rows + r) * wk.sh.nb(), TL::zero(As) ? mc_zero() : d);
       }
     } else {
       if (s < n) wk.sh.stB_D(wk.blkB(a.out0, wk.phys(j0 + s)), h);
@@ -431,7 +459,7 @@ __device__ __forceinline__ void seg_publish(uint64_t* w, v4f v) {
   st_u64(w + 2 * 4 + q, pack_word(kMcTag, v.z));
   st_u64(w + 3 * 4 + q, pack_word(kMcTag, v.w));
 }
-__device__ __forceinline__ bool seg_wait(const uint64_t* w, uint32_t* hdr, v4f& v) {
+__device__ __forceinline__ bool seg_wait(const uint64_t* w, uint32_t* hdr, uint32_t limit, v4f& v) {
   const int q = (int)(threadIdx.x & 3);
   for (uint32_t spins = 0;; ++spins) {
     const uint64_t a = ld_u64(w + 0 * 4 + q), b = ld_u64(w + 1 * 4 + q), c = ld_u64(w + 2 * 4 + q),
@@ -442,7 +470,7 @@ __device__ __forceinline__ bool seg_wait(const uint64_t* w, uint32_t* hdr, v4f& 
       v = v4f{word_val(a), word_val(b), word_val(c), word_val(d)};
       return true;
     }
-    if (spins > kSpinLimit) {
+    if (spins > limit) {
       if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
       return false;
     }
@@ -463,7 +491,7 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
   __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
   int64_t r;
   int c;
-  tile_of_block<true>(a.rows, a.ntiles, r, c);
+  tile_of_block<true>(a.rows, a.ntiles, a.blk0, r, c);
   McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
   const int b = TL::lrow();
   const int64_t jb = (int64_t)c * (16 * S) + (int64_t)b * S;  // this group's first processing step
@@ -504,10 +532,12 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
     }
   }
   // sequence boundaries folded into the registers (forward: A h0 + B at a
-  // first step; backward: h_prev = h0 or 0 at a forward-first step)
+  // first step, B alone at a reset, an all-zero A; backward: h_prev = h0 or 0
+  // at a forward-first step)
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool f = BWD ? ((lastm >> s) & 1u) : ((firstm >> s) & 1u);
+    const bool z = BWD ? false : TL::zero(X[s]);  // whole wave: the test is a ballot
+    const bool f = BWD ? ((lastm >> s) & 1u) : (((firstm >> s) & 1u) && !z);
     if (__ballot(f) == 0ull) continue;
     v4f h0v = mc_zero();
     if (f && a.h0) {
@@ -523,18 +553,22 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
     }
   }
 
-  // ---- group summary (a sequence's first step is hard)
+  // ---- group summary (a sequence's first step and a reset, a step in the row
+  // whose transition operand is all zero, are hard)
+  uint32_t zerom = 0u;
   v4f P = tile_ident<TL>(), Q = mc_zero();
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool f = (firstm >> s) & 1u;
+    zerom |= (uint32_t)(s < nb && TL::zero(X[s])) << s;
+    const bool f = ((firstm | zerom) >> s) & 1u;
     const v4f Pn = TL::mm(X[s], P, mc_zero()), Qn = TL::mm(X[s], Q, Y[s]);
     P = sel4(f, mc_zero(), Pn);
     Q = sel4(f, Y[s], Qn);
   }
+  const uint32_t hardm = firstm | zerom;
 
   // ---- inclusive scan over the 16 groups: group b <- (group b) after (groups before)
-  bool hard = firstm != 0u;
+  bool hard = hardm != 0u;
 #pragma unroll
   for (int k = 1; k < 16; k <<= 1) {
     const v4f Pp = shfl_up4(P, 4 * k), Qp = shfl_up4(Q, 4 * k);
@@ -549,7 +583,7 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
   // the wave is hard if group 15's inclusive summary is; it needs no carry-in
   // if its first step starts a sequence
   const bool whard = __shfl((int)hard, 60, 64) != 0;
-  const bool first0 = __shfl((int)(firstm & 1u), 0, 64) != 0;
+  const bool first0 = __shfl((int)(hardm & 1u), 0, 64) != 0;
 
   // ---- carry-in from the wave before, h_out for the wave after
   uint32_t* hdr = (uint32_t*)a.ws;
@@ -560,7 +594,7 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
   const v4f PR = TL::d_to_r(s_t, P);
   v4f hin = mc_zero();
   if (!first0) {
-    if (!seg_wait(pub + (me - 1) * 16, hdr, hin)) hin = mc_zero();
+    if (!seg_wait(pub + (me - 1) * 16, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
   }
   // out_b = state after group b
   v4f out = TL::mm(PR, hin, Q);
@@ -572,7 +606,7 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
   // ---- apply from the registers
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const bool first = (firstm >> s) & 1u;
+    const bool first = (hardm >> s) & 1u;
     const v4f hn = TL::mm(X[s], h, Y[s]);
     h = sel4(first, Y[s], hn);  // h holds lam in the backward
     if constexpr (BWD) {
@@ -591,11 +625,13 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
       }
       const bool l = ((lastm >> s) & 1u) && s < nb;
       if (a.dh0 && __ballot(l) != 0ull) {
-        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout)
+        // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout); 0 where
+        // A_s = 0: nothing flows through a reset
         const v4f Ad = l ? wk.sh.ldA_D(wk.blkA(a.A, wk.phys(jb + s))) : mc_zero();
         wait_stage_loads();
         const v4f d = TL::mm(Ad, h, mc_zero());
-        if (l) wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(jb + s) * a.rows + r) * wk.sh.nb(), d);
+        const bool reset = TL::zero(Ad);
+        if (l) wk.sh.stB_D(a.dh0 + ((int64_t)wk.seg_of(jb + s) * a.rows + r) * wk.sh.nb(), reset ? mc_zero() : d);
       }
     } else {
       if constexpr (FULL) {
@@ -642,7 +678,8 @@ static hipError_t launch_mc_dir(const MatArgs& a0, hipStream_t st) {
   // fresh words (and header) for this call: a zero tag = not published
   const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kMcPubBytes, st);
   if (z != hipSuccess) return z;
-  hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S>), dim3(launch_blocks((uint64_t)n, a.nblk)), dim3(64), 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -653,7 +690,8 @@ static hipError_t launch_seg_dir(const MatArgs& a0, hipStream_t st) {
   const int64_t n = a.rows * a.ntiles;
   const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kSegPubBytes, st);
   if (z != hipSuccess) return z;
-  hipLaunchKernelGGL((k_mc_rowseg<FULL, BWD, REV, VARLEN, S>), dim3((unsigned)n), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((k_mc_rowseg<FULL, BWD, REV, VARLEN, S>), dim3(launch_blocks((uint64_t)n, a.nblk)), dim3(64), 0,
+                     st, a);
   return hipGetLastError();
 }
 

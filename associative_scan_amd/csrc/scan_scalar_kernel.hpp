@@ -244,7 +244,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     c_first = c_last = 0;  // the row fits one tile
   } else {
     int c;
-    tile_of_block<kTileMajor>(a.rows, a.ntiles, r, c);
+    tile_of_block<kTileMajor>(a.rows, a.ntiles, a.blk0, r, c);
     c_first = c_last = c;
   }
   const int64_t T = a.T;
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             for (int i = 0; i < NC; ++i) st_u64(my + NS + i, pack_word(tagI, inc.v[i]));
           }
         }
-        if (c > 0) carry = lookback<Ops, kTileMajor>(ws, rd, c);
+        if (c > 0) carry = lookback<Ops, kTileMajor>(ws, rd, c, spin_limit(a.spin));
         if (l == 0) {
           if (!hard) {
             const C inc = Ops::apply(tagg, carry);
@@ -720,8 +720,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             const int64_t t = u0 + P_(e) - lead;
             int sk = 0;
             if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
-            // dh0 = g * lam; log space: dlog_h0 = a * lam * h0 (N holds h0 there)
-            a.dh0[(int64_t)sk * a.rows + r] = LOGB ? (G[s][e] * O[s][e]) * N[s][e] : G[s][e] * O[s][e];
+            // dh0 = g * lam; log space: dlog_h0 = a * lam * h0 (N holds h0 there);
+            // nothing reaches h0 through a zero gate (a reset)
+            const float gl = G[s][e] * O[s][e];
+            a.dh0[(int64_t)sk * a.rows + r] = (G[s][e] != 0.f) ? (LOGB ? gl * N[s][e] : gl) : 0.f;
           }
         }
       }
@@ -751,7 +753,7 @@ static hipError_t launch_cfg(const ScalarArgs& a0, hipStream_t st) {
     const size_t words = (size_t)a.rows * (size_t)a.ntiles * (size_t)(Ops::NS + Ops::NC);
     const hipError_t z = launch_zero(a.ws, ws_desc_offset() + words * sizeof(uint64_t), st);
     if (z != hipSuccess) return z;
-    const dim3 grid((unsigned)((uint64_t)a.rows * (uint64_t)a.ntiles));
+    const dim3 grid(launch_blocks((uint64_t)a.rows * (uint64_t)a.ntiles, a.nblk));
     if (varlen) hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, true, kLookback, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_scalar<Ops, Tin, BWD, REV, false, kLookback, WAVES, SUBS, GPL, LOGB, GATE, XP>), grid, block, 0, st, a);
   }

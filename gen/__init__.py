@@ -217,13 +217,14 @@ def logspace(B: int = 8, D: int = 1024, T: int = 8192, cfg_id: int = 4):
             "log_b": _draw(sb, (R, T), _n01).reshape(B, D, T)}
 
 
-def matrix_rot2(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 / 2048, cfg_id: int = 51):
+def matrix_rot2(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 / 2048, cfg_id: int = 51,
+                rows=None):
     """k=2, v=1 rotation family, fp32, layout [B*N, T, 2, 2] / [B*N, T, 2, 1].
 
     Tensors (spawn order): A (r ~ U(0.5,1) and theta ~ U(-pi,pi) from one
     stream per block: A_t = r_t * [[cos, -sin], [sin, cos]]), B ~ N(0,1),
     reset mask i.i.d. per (lane, t) with probability p_reset -> A = 0,
-    dy ~ N(0,1).
+    dy ~ N(0,1). With ``rows`` only those rows of the B*N are drawn.
     """
     R = B * N
     sa, sb, sm, sdy = _tensors(cfg_id, T, 4, B, N)
@@ -237,10 +238,10 @@ def matrix_rot2(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 / 
         A[..., 0, 0], A[..., 0, 1], A[..., 1, 0], A[..., 1, 1] = c, -s, s, c
         return A
 
-    A = _draw(sa, (R, T, 2, 2), rot)
-    reset = _draw(sm, (R, T), lambda r, s: r.random(s) < p_reset, dtype=bool)
+    A = _draw(sa, (R, T, 2, 2), rot, rows=rows)
+    reset = _draw(sm, (R, T), lambda r, s: r.random(s) < p_reset, dtype=bool, rows=rows)
     A[reset] = 0.0
-    return {"A": A, "B": _draw(sb, (R, T, 2, 1), _n01), "dy": _draw(sdy, (R, T, 2, 1), _n01),
+    return {"A": A, "B": _draw(sb, (R, T, 2, 1), _n01, rows=rows), "dy": _draw(sdy, (R, T, 2, 1), _n01, rows=rows),
             "reset": reset, "k": 2, "v": 1}
 
 
@@ -260,10 +261,12 @@ def _orthonormal_qr_q(G: np.ndarray) -> np.ndarray:
     return Q
 
 
-def matrix_orth4(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 / 2048, cfg_id: int = 52):
+def matrix_orth4(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 / 2048, cfg_id: int = 52,
+                 rows=None):
     """k=4, v=4, fp32: A_t = 0.9 * Q_t with Q_t the Q factor (positive diag R)
     of an N(0,1) 4x4 matrix; B ~ N(0,1) [4,4]; resets A = 0 with probability
-    p_reset i.i.d. per (lane, t); dy ~ N(0,1) [4,4].
+    p_reset i.i.d. per (lane, t); dy ~ N(0,1) [4,4]. With ``rows`` only those
+    rows of the B*N are drawn.
 
     Tensors (spawn order): A (from G), B, reset mask, dy.
     """
@@ -274,10 +277,10 @@ def matrix_orth4(B: int = 8, N: int = 512, T: int = 8192, p_reset: float = 1.0 /
         G = _n01(rng, shp).astype(np.float64)
         return (0.9 * _orthonormal_qr_q(G)).astype(np.float32)
 
-    A = _draw(sa, (R, T, 4, 4), orth)
-    reset = _draw(sm, (R, T), lambda r, s: r.random(s) < p_reset, dtype=bool)
+    A = _draw(sa, (R, T, 4, 4), orth, rows=rows)
+    reset = _draw(sm, (R, T), lambda r, s: r.random(s) < p_reset, dtype=bool, rows=rows)
     A[reset] = 0.0
-    return {"A": A, "B": _draw(sb, (R, T, 4, 4), _n01), "dy": _draw(sdy, (R, T, 4, 4), _n01),
+    return {"A": A, "B": _draw(sb, (R, T, 4, 4), _n01, rows=rows), "dy": _draw(sdy, (R, T, 4, 4), _n01, rows=rows),
             "reset": reset, "k": 4, "v": 4}
 
 

@@ -83,7 +83,8 @@ typedef enum {
   MSCAN_ERR_INVALID = 1,
   MSCAN_ERR_UNSUPPORTED = 2,
   MSCAN_ERR_WORKSPACE = 3,
-  MSCAN_ERR_HIP = 4
+  MSCAN_ERR_HIP = 4,
+  MSCAN_ERR_TIMEOUT = 5 /* reported by mscan_workspace_error only (see there) */
 } mscan_status;
 
 typedef enum { MSCAN_F32 = 0, MSCAN_BF16 = 1, MSCAN_F16 = 2 } mscan_dtype;
@@ -234,6 +235,52 @@ MSCAN_API mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, 
 MSCAN_API mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, const float* A,
                                     const float* h, const float* dy, const float* h0, float* dA,
                                     float* dB, float* dh0, void* ws, size_t ws_bytes, void* stream);
+
+/* Measurement aid (not part of the scan): the practical HBM ceiling for a
+ * kernel that reads nsrc arrays and writes ndst arrays of n floats each. It
+ * streams exactly those bytes with the scan kernels' access type
+ * (non-temporal 16-byte loads and stores) and no other work, so a scan's
+ * achieved bandwidth can be set against what the memory system delivers for
+ * the same read:write mix (the associative-scan-triton README,
+ * "performance", reports its kernels against device timings of the same
+ * bytes). Each destination receives the elementwise sum of the sources.
+ *   src : nsrc device pointers, dst : ndst device pointers, all 16-byte
+ *         aligned, n floats each, n a multiple of 4.
+ * Supported (nsrc, ndst): (1,1), (2,1), (3,1), (1,2), (2,2), (3,2), (4,2),
+ * (4,3); other mixes return MSCAN_ERR_UNSUPPORTED, bad pointers or sizes
+ * MSCAN_ERR_INVALID. Enqueues one kernel on `stream`. */
+MSCAN_API mscan_status mscan_stream_ceiling(const float* const* src, int nsrc, float* const* dst, int ndst, size_t n,
+                                            void* stream);
+
+/* Whether the last call that chained tiles through `ws` had a look-back wait
+ * give up ("The dispatch seam" of the minGRU page: a problem is reported,
+ * never turned into a silent wrong result). A wait runs out only when a
+ * predecessor never publishes (a workspace shared by calls that overlap in
+ * time, or a partial launch below); the waiting tile then takes a NaN carry,
+ * so every output that needed the missing value is NaN, and sets the
+ * workspace's error word. This call enqueues a one-thread kernel on `stream`
+ * that writes MSCAN_OK (0) or MSCAN_ERR_TIMEOUT (5) to *flag_out (device or
+ * pinned host memory, 4-byte aligned), ordered after the work before it on
+ * `stream`. The word keeps its value until the next call that chains tiles
+ * through `ws` clears it. Returns MSCAN_ERR_INVALID for a null or misaligned
+ * ws / flag_out or ws_bytes below the 128-byte header, MSCAN_ERR_HIP for a
+ * launch error. */
+MSCAN_API mscan_status mscan_workspace_error(const void* ws, size_t ws_bytes, int32_t* flag_out, void* stream);
+
+/* Test hook for the loud failure above: the forward of scan_fwd (fp32 g = a,
+ * x = b; k = v = 1) or matrix_affine_scan_fwd (A = a, B = b; any (k, v) of
+ * the envelope), with no h0, launching only blocks [first_block, first_block +
+ * nblocks) of the call's grid and letting each look-back wait give up after
+ * spin_limit polls (0 = the library's default limit). With a block whose
+ * predecessors are not launched, its wait runs out, its outputs that depend
+ * on the carry are NaN, mscan_workspace_error reports MSCAN_ERR_TIMEOUT, and
+ * every launched block still ends. The blocks not launched leave their
+ * outputs unwritten. The problem must chain tiles (several tiles per row;
+ * always for the matrix-core shapes), else MSCAN_ERR_UNSUPPORTED; a block
+ * range outside the grid is MSCAN_ERR_INVALID; other errors as scan_fwd. */
+MSCAN_API mscan_status mscan_debug_partial_fwd(const mscan_problem* prob, int k, int v, const float* a, const float* b,
+                                               float* out, void* ws, size_t ws_bytes, int64_t first_block,
+                                               int64_t nblocks, uint32_t spin_limit, void* stream);
 
 MSCAN_API const char* mscan_status_string(int status);
 /* Text of the last HIP error this thread saw inside the library ("" if none). */

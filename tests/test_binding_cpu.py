@@ -68,3 +68,45 @@ def test_strided_views(m):
     # host tensors are refused
     with pytest.raises(ValueError):
         m._rows_view(base, "t")
+
+
+def test_debug_cu_seqlens_host_validation():
+    """Debug mode checks cu_seqlens contents on the host (flash-attn convention)."""
+    import numpy as np
+    import associative_scan_amd as m
+    m._validate_cu_host(np.array([0, 0, 5, 9, 9], np.int32), 9)
+    for bad, T in (([1, 9], 9), ([0, 8], 9), ([0, 5, 4, 9], 9), ([0], 9)):
+        with pytest.raises(ValueError):
+            m._validate_cu_host(np.array(bad, np.int32), T)
+
+
+def test_debug_reporting_path(monkeypatch):
+    """A set error word raises MscanError (status 5) in debug mode, a clear one
+    does not, and nothing is read with debug mode off (the word itself is read
+    on the GPU by mscan_workspace_error; here its value is stubbed)."""
+    import associative_scan_amd as m
+    seen = []
+
+    def fake_read(wsp, wsn, dev, sh):
+        seen.append(wsp)
+        return fake_read.code
+
+    monkeypatch.setattr(m, "_read_ws_error", fake_read)
+    monkeypatch.setattr(m.torch.cuda, "is_current_stream_capturing", lambda: False)  # no device here
+    old = m.debug_enabled()
+    try:
+        m.set_debug(True)
+        fake_read.code = 5
+        with pytest.raises(m.MscanError) as e:
+            m._check("scan_fwd", 0, (1234, 4096, None, 0))
+        assert e.value.status == 5 and "wait gave up" in str(e.value)
+        fake_read.code = 0
+        m._check("scan_fwd", 0, (1234, 4096, None, 0))
+        m._check("scan_fwd", 0, (None, 0, None, 0))  # no workspace used: nothing to read
+        assert seen == [1234, 1234]
+        m.set_debug(False)
+        fake_read.code = 5
+        m._check("scan_fwd", 0, (1234, 4096, None, 0))
+        assert seen == [1234, 1234]
+    finally:
+        m.set_debug(old)

@@ -581,6 +581,62 @@ def test_graph_capture_replays(m, oracle_lib):
         close(he, href, TAU_FWD, f"eager h after replay {rep}")
 
 
+def test_two_graphs_keep_their_own_workspaces(m, oracle_lib):
+    """Two captured graphs whose calls need different workspace sizes (the
+    second larger), then an eager call that needs more still: each graph keeps
+    the workspace it recorded, so replaying both graphs, in either order and
+    with eager calls between, keeps every result correct."""
+    r = np.random.default_rng(4343)
+
+    def inputs(rows, T):
+        g = r.uniform(0, 1, (rows, T)).astype(np.float32)
+        x = r.standard_normal((rows, T)).astype(np.float32)
+        return g, x, _t(g), _t(x)
+
+    g1, x1, g1t, x1t = inputs(4, 3 * 4096)     # 12 tiles of descriptors
+    g2, x2, g2t, x2t = inputs(16, 6 * 4096)    # 96 tiles
+    g3, x3, g3t, x3t = inputs(40, 5 * 4096)    # 200 tiles (eager only)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.scan_fwd(g1t, x1t)
+        m.scan_fwd(g2t, x2t)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph1, graph2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph1):
+        h1 = m.scan_fwd(g1t, x1t)
+    with torch.cuda.graph(graph2):
+        h2 = m.scan_fwd(g2t, x2t)
+    ref1 = oracle_lib.scan_fwd(g1, x1)
+    ref2 = oracle_lib.scan_fwd(g2, x2)
+    ref3 = oracle_lib.scan_fwd(g3, x3)
+    for order in ((graph1, graph2), (graph2, graph1), (graph1, graph2)):
+        h1.zero_()
+        h2.zero_()
+        for gr in order:
+            gr.replay()
+        h3 = m.scan_fwd(g3t, x3t)  # eager, on a cached workspace larger than either graph's
+        torch.cuda.synchronize()
+        close(h1, ref1, TAU_FWD, "graph 1")
+        close(h2, ref2, TAU_FWD, "graph 2")
+        close(h3, ref3, TAU_FWD, "eager")
+    # replays on two streams at once: each graph writes only its own workspace
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    h1.zero_()
+    h2.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        graph1.replay()
+    with torch.cuda.stream(s2):
+        graph2.replay()
+    torch.cuda.synchronize()
+    close(h1, ref1, TAU_FWD, "graph 1 on its own stream")
+    close(h2, ref2, TAU_FWD, "graph 2 on its own stream")
+
+
 def test_binding_rejects_bad_out_and_host_tensors(m):
     """The binding refuses an `out` that is not fp32 or has another shape, and
     host tensors anywhere, before anything reaches the library."""

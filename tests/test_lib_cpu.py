@@ -199,3 +199,28 @@ def test_grid_beyond_one_launch_is_unsupported(m):
     q = _prob(m, rows=(1 << 20) - 1, T=1 << 16)
     assert m.lib.scan_fwd(ctypes.byref(q), 0, FAKE, FAKE, None, FAKE, None, 0, None) == 3
 
+
+
+def test_workspace_error_rejects_bad_arguments_on_host(m):
+    """mscan_workspace_error validates before any HIP call (no GPU needed)."""
+    flag = FAKE
+    assert m.lib.mscan_workspace_error(None, 4096, flag, None) == 1
+    assert m.lib.mscan_workspace_error(FAKE, 64, flag, None) == 1       # below the 128-byte header
+    assert m.lib.mscan_workspace_error(FAKE + 8, 4096, flag, None) == 1  # misaligned workspace
+    assert m.lib.mscan_workspace_error(FAKE, 4096, None, None) == 1
+    assert m.lib.mscan_workspace_error(FAKE, 4096, FAKE + 2, None) == 1  # misaligned flag
+    assert m.lib.mscan_status_string(5)
+
+
+@pytest.mark.parametrize("case,k,v,first,n,status", [
+    (dict(T=100), 1, 1, 0, 1, 2),            # one tile per row: no wait to run out
+    (dict(T=3 * 4096), 1, 1, 0, 0, 1),       # empty block range
+    (dict(T=3 * 4096), 1, 1, 23, 2, 1),      # past the grid (8 rows x 3 tiles = 24 blocks)
+    (dict(T=3 * 4096), 1, 1, -1, 1, 1),
+    (dict(T=3 * 4096), 3, 1, 0, 1, 2),       # outside the envelope
+    (dict(T=500), 2, 1, 0, 1, 2),            # a 2x1 row of one tile
+])
+def test_debug_partial_fwd_host_checks(m, case, k, v, first, n, status):
+    p = _prob(m, **case)
+    big = 1 << 30
+    assert m.lib.mscan_debug_partial_fwd(ctypes.byref(p), k, v, FAKE, FAKE, FAKE, FAKE, big, first, n, 100, None) == status

@@ -84,6 +84,7 @@ def _load():
         "scan_log_bwd_gated": (i32, [P, i32, p, p, p, p, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_fwd": (i32, [P, i32, i32, p, p, p, p, p, sz, p]),
         "matrix_affine_scan_bwd": (i32, [P, i32, i32, p, p, p, p, p, p, p, p, sz, p]),
+        "scan_fwd_noalloc": (i32, [P, i32, p, p, p, p, p]),
         "mscan_workspace_error": (i32, [p, sz, p, p]),
         "mscan_stream_ceiling": (i32, [ctypes.POINTER(p), i32, ctypes.POINTER(p), i32, sz, p]),
         "mscan_debug_partial_fwd": (i32, [P, i32, i32, p, p, p, p, sz, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,

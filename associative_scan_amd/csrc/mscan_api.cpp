@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 
 #include "mscan.h"
 #include "mscan_device.hpp"
@@ -372,6 +374,68 @@ mscan_status matrix_affine_scan_bwd(const mscan_problem* prob, int k, int v, con
   a.stride = prob->row_stride;
   a.ws = ws;
   return hip_status(mscan::launch_matrix(a, k, v, true, st));
+}
+
+// ---------------------------------------------------------------------------
+// scan_fwd_noalloc: scan_fwd with its look-back descriptors in a fixed array
+// the library owns on each device, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// The fixed scratch array. Each device holds its own copy from the moment the
+// library's code is loaded on it until the process ends. Host code must not
+// use the name as an address (on the host it is only a stand-in for the
+// symbol); every use goes through the per-device address resolved below.
+static_assert(MSCAN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, resolved once per device
+// (hipGetSymbolAddress with that device current) and cached.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+mscan_status scan_fwd_noalloc(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
+                              const float* h0, float* h, void* stream) {
+  // every host-side check of scan_fwd first (nothing is resolved or enqueued
+  // for an invalid call), then the scratch size
+  mscan_status s = check_problem(prob);
+  if (s != MSCAN_OK) return s;
+  if (in_dtype != MSCAN_F32 && in_dtype != MSCAN_BF16 && in_dtype != MSCAN_F16) return MSCAN_ERR_UNSUPPORTED;
+  if (!g || !x || !h) return MSCAN_ERR_INVALID;
+  if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
+  if ((s = check_grid(prob, scalar_tiles_for(prob, in_dtype))) != MSCAN_OK) return s;
+  if (scalar_ws_bytes(prob, 3, false) > (size_t)MSCAN_NOALLOC_SCRATCH_BYTES) return MSCAN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const mscan_status r = hip_status(scratch_on_current_device(&ws));
+  if (r != MSCAN_OK) return r;
+  return scalar_fwd_impl(prob, in_dtype, MSCAN_GATE_NONE, g, x, h0, h, ws, MSCAN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 mscan_status mscan_stream_ceiling(const float* const* src, int nsrc, float* const* dst, int ndst, size_t n,

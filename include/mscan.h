@@ -282,6 +282,26 @@ MSCAN_API mscan_status mscan_debug_partial_fwd(const mscan_problem* prob, int k,
                                                float* out, void* ws, size_t ws_bytes, int64_t first_block,
                                                int64_t nblocks, uint32_t spin_limit, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): scan_fwd
+ * with no workspace argument. The look-back descriptors of rows that span
+ * several tiles live in a fixed array of MSCAN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on, from the first use of its code on
+ * that device until the process ends. The call allocates and frees nothing;
+ * it clears the part of the array it uses with a small fill kernel on
+ * `stream` (no memset node), so a previous call's contents do not matter.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (different streams, or graphs replayed concurrently)
+ * race and give wrong results; serialise them. A problem whose descriptors do
+ * not fit (more than about 349,000 chained tiles of 4096 elements; rows of at
+ * most one tile need none) returns MSCAN_ERR_WORKSPACE and enqueues nothing.
+ * Arguments, results and every other error are those of scan_fwd; the
+ * device's address of the array is resolved on the first call made with that
+ * device current (a HIP failure there returns MSCAN_ERR_HIP). */
+#define MSCAN_NOALLOC_SCRATCH_BYTES (8u << 20)
+MSCAN_API mscan_status scan_fwd_noalloc(const mscan_problem* prob, int in_dtype, const void* g, const void* x,
+                                        const float* h0, float* h, void* stream);
+
 MSCAN_API const char* mscan_status_string(int status);
 /* Text of the last HIP error this thread saw inside the library ("" if none). */
 MSCAN_API const char* mscan_last_hip_error(void);

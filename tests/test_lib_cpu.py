@@ -224,3 +224,15 @@ def test_debug_partial_fwd_host_checks(m, case, k, v, first, n, status):
     p = _prob(m, **case)
     big = 1 << 30
     assert m.lib.mscan_debug_partial_fwd(ctypes.byref(p), k, v, FAKE, FAKE, FAKE, FAKE, big, first, n, 100, None) == status
+
+
+def test_scan_fwd_noalloc_host_checks(m):
+    """scan_fwd_noalloc refuses bad problems and problems whose descriptors do
+    not fit its fixed scratch array on the host, before any HIP call."""
+    p = _prob(m, rows=0)
+    assert m.lib.scan_fwd_noalloc(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, None) == 1
+    p = _prob(m, rows=12288, T=1 << 20)  # 12288 rows x 256 tiles of descriptors: 75 MB > 8 MiB
+    assert m.workspace_bytes(p, m.OP_SCAN_FWD) > 8 << 20
+    assert m.lib.scan_fwd_noalloc(ctypes.byref(p), 0, FAKE, FAKE, None, FAKE, None) == 3
+    assert m.lib.scan_fwd_noalloc(ctypes.byref(_prob(m)), 7, FAKE, FAKE, None, FAKE, None) == 2
+    assert m.lib.scan_fwd_noalloc(ctypes.byref(_prob(m)), 0, FAKE + 4, FAKE, None, FAKE, None) == 1

@@ -31,7 +31,7 @@ import threading
 import torch
 
 __all__ = [
-    "lib", "library_path", "Problem", "MscanError",
+    "lib", "library_path", "stress_library_path", "load_library", "Problem", "MscanError",
     "scan_fwd", "scan_bwd", "scan_log_fwd", "scan_log_bwd", "matrix_affine_scan_fwd", "matrix_affine_scan_bwd",
     "scan_fwd_gated", "scan_bwd_gated", "scan_log_fwd_gated", "scan_log_bwd_gated",
     "scan_causal", "scan_bidirectional_branched", "scan_log", "matrix_scan", "GATE_SIGMOID", "GATE_NEG_SOFTPLUS",
@@ -65,11 +65,16 @@ class Problem(ctypes.Structure):
     ]
 
 
-def _load():
-    if not os.path.exists(library_path):
-        raise ImportError(
-            f"libmscan.so not found at {library_path}; build it with `python associative_scan_amd/build.py`")
-    L = ctypes.CDLL(library_path)
+stress_library_path = os.path.join(_HERE, "libmscan_stress.so")
+
+
+def load_library(path: str):
+    """A libmscan build at `path` (e.g. the race-stress build
+    libmscan_stress.so) as a ctypes library with every entry point's argument
+    types set, for callers that drive the C ABI directly."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found; build it with `python associative_scan_amd/build.py`")
+    L = ctypes.CDLL(path)
     P, p, sz, i32 = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     sig = {
         "mscan_workspace_bytes": (sz, [P, i32, i32, i32]),
@@ -100,6 +105,10 @@ def _load():
     if L.mscan_abi_version() != 1:
         raise ImportError("libmscan ABI version mismatch")
     return L
+
+
+def _load():
+    return load_library(library_path)
 
 
 lib = _load()

@@ -3,7 +3,10 @@
 Usage: python associative_scan_amd/build.py   (or call build()); run as a
 script, since importing the package needs the library this builds.
 Each source compiles to an object under associative_scan_amd/_build/, in
-parallel, then links into associative_scan_amd/libmscan.so.
+parallel, then links into associative_scan_amd/libmscan.so. A second library,
+libmscan_stress.so, is the same code with MSCAN_RACE_STRESS defined (a
+pseudo-random pause before every look-back publish); only the race-stress
+tests load it.
 """
 from __future__ import annotations
 
@@ -44,9 +47,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+STRESS_OUT = os.path.join(HERE, "libmscan_stress.so")
+STRESS_FLAGS = ["-DMSCAN_RACE_STRESS"]
+
+
+def _compile(job) -> str:
+    src, variant = job
+    d = os.path.join(BUILD, variant) if variant else BUILD
+    obj = os.path.join(d, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *FLAGS, *(STRESS_FLAGS if variant == "stress" else []), "-c", src, "-o", obj]
     try:
         r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
     except subprocess.TimeoutExpired as e:
@@ -60,20 +69,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source under csrc/ and link libmscan.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, stress: bool = True) -> str:
+    """Compile every source under csrc/ and link libmscan.so (and the race-stress
+    build libmscan_stress.so); returns the path of libmscan.so."""
+    variants = ["", "stress"] if stress else [""]
+    for v in variants:
+        os.makedirs(os.path.join(BUILD, v) if v else BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = [(src, v) for v in variants for src in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(srcs)], OUT)
+    if stress:
+        _link(objs[len(srcs):], STRESS_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT}" + (f" and {STRESS_OUT}" if stress else ""))
     return OUT
 
 

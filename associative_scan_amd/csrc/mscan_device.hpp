@@ -255,6 +255,25 @@ __device__ __forceinline__ Workspace ws_view(void* ws) {
 constexpr uint32_t kSpinLimit = 1u << 22;
 __device__ __forceinline__ uint32_t spin_limit(uint32_t requested) { return requested ? requested : kSpinLimit; }
 
+// Race stress (a test build only: the library built with MSCAN_RACE_STRESS
+// defined, see the build script): every publish of a look-back descriptor or
+// of a chained state first waits a pseudo-random 0 to ~7700 cycles, different
+// per workgroup and publish site, so that tiles publish in orders and at
+// distances the ordinary timing rarely produces. Without the macro it is
+// nothing.
+__device__ __forceinline__ void stress_pause(uint32_t site) {
+#ifdef MSCAN_RACE_STRESS
+  uint32_t x = blockIdx.x * 2654435761u ^ (site + 1u) * 40503u;
+  x ^= x >> 15;
+  x *= 0x2c1b3c6du;
+  x ^= x >> 12;
+  const uint32_t n = (x >> 7) & 15u;  // wave-uniform
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+#else
+  (void)site;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Scan "ops": one summary type S (a map from the state before a span to the
 // state after it) and one carry type C (a state), stored as small float arrays

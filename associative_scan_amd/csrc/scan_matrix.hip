@@ -430,6 +430,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
         {
           const S tagg = (WAVES > 1) ? tile_agg() : wagg;
           hard = Ops::hard(tagg);
+          stress_pause(1);
           if (l == 0) {
             if (!hard) {
 #pragma unroll
@@ -442,6 +443,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
           }
         }
         if (c > 0) carry = lookback<Ops, true>(ws, rd, c, spin_limit(a.spin));
+        stress_pause(2);
         if (l == 0) {
           if (!hard) {
             const S tagg = (WAVES > 1) ? tile_agg() : wagg;

@@ -286,6 +286,7 @@ constexpr uint32_t kMcTag = 2u;
 constexpr size_t kMcPubBytes = 256 * 8;  // one published h_out
 
 __device__ __forceinline__ void mc_publish(uint64_t* w, v4f v) {
+  stress_pause(3);
   uint64_t* p = w + threadIdx.x;
   st_u64(p + 0 * 64, pack_word(kMcTag, v.x));
   st_u64(p + 1 * 64, pack_word(kMcTag, v.y));
@@ -453,6 +454,7 @@ constexpr size_t kSegPubBytes = 16 * 8;  // one published 4 x 4 h_out
 
 // lane (b, q) publishes / reads column q of a 4 x 4 block (word 4 i + j = h[i][j])
 __device__ __forceinline__ void seg_publish(uint64_t* w, v4f v) {
+  stress_pause(4);
   const int q = (int)(threadIdx.x & 3);
   st_u64(w + 0 * 4 + q, pack_word(kMcTag, v.x));
   st_u64(w + 1 * 4 + q, pack_word(kMcTag, v.y));

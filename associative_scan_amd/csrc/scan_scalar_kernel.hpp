@@ -616,6 +616,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       if (w == 0) {
         const uint32_t tagA = kTagAgg, tagI = kTagIncl;
         const bool hard = Ops::hard(tagg);
+        stress_pause(1);
         if (l == 0) {
           if (!hard) {
 #pragma unroll
@@ -627,6 +628,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
           }
         }
         if (c > 0) carry = lookback<Ops, kTileMajor>(ws, rd, c, spin_limit(a.spin));
+        stress_pause(2);
         if (l == 0) {
           if (!hard) {
             const C inc = Ops::apply(tagg, carry);

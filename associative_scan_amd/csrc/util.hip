@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void k_stream(const StreamArgs a) {
 
 template <int NS, int ND>
 static hipError_t launch_stream_nd(const StreamArgs& a, hipStream_t st) {
-  // enough workgroups to fill every CU several times over; each lane then
-  // walks the arrays in rounds of four units
+  // one workgroup per 1024 units (16 KiB of every array), as the scan
+  // kernels take one tile per workgroup; a grid beyond 2^20 workgroups loops
   const size_t want = (a.n4 + 1023) / 1024;
-  const unsigned blocks = (unsigned)(want < 8192 ? (want ? want : 1) : 8192);
+  const unsigned blocks = (unsigned)(want < (1u << 20) ? (want ? want : 1) : (1u << 20));
   hipLaunchKernelGGL((k_stream<NS, ND>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }

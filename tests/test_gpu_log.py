@@ -219,3 +219,60 @@ def test_log_short_row_tiles(m, oracle_lib, T):
             rd = obwd(la, lb, href, dy, log_h0=lh0, cu_seqlens=cu, reverse=rev)
             for got, ref, nm in zip(d, rd, ("dlog_a", "dlog_b", "dlog_h0")):
                 close(got, ref, TAU_LOG, f"{nm} rev {rev} gated {gated}")
+
+
+# ---------------------------------------------------------------------------
+# extreme ranges inside one row
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_lanes_outside_the_linear_range(m, oracle_lib, reverse):
+    """Rows mixing ordinary values with log a far below and above zero (-95,
+    +70), log b beyond +-80, partial values near e^80 and runs of tiny terms,
+    both directions, against the oracle (relative error)."""
+    r = np.random.default_rng(3100 + reverse)
+    rows, T = 6, 5 * 4096 + 17
+    la, lb = _inputs(r, rows, T)
+    la[0, 1000:1003] = -95.0          # log a below the range
+    la[1, 5000] = 70.0                # above it
+    lb[2, 9000:9004] = 86.0           # log b above the range
+    lb[3, 12000:12004] = -90.0        # and below it, alone in its lane
+    lb[3, 12004:12016] = -90.0
+    la[3, 12000:12016] = 0.0
+    lb[4, 15000:15016] = 79.0         # partial values beyond 16 e^80 need the check on M + R
+    la[4, 15000:15016] = 0.0
+    lb[5, 7000:7016] = -75.0          # every term tiny: log Q must stay accurate
+    la[5, 7000:7016] = -0.5
+    h = m.scan_log_fwd(_t(la), _t(lb), reverse=reverse)
+    ref = oracle_lib.scan_log_fwd(la, lb, reverse=reverse)
+    close(h, ref, TAU_LOG, "h", relative=True)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_log_large_carry_takes_the_exact_apply(m, oracle_lib, reverse):
+    """States near e^75 carried across tiles, and a state that decays from
+    there back to ordinary values, both directions, against the oracle."""
+    r = np.random.default_rng(3200 + reverse)
+    rows, T = 4, 3 * 4096 + 5
+    la = np.full((rows, T), -0.01, np.float32)
+    lb = (70.0 + 0.1 * r.standard_normal((rows, T))).astype(np.float32)
+    # row 1 decays from there: log a = -2 after the middle
+    la[1, T // 2:] = -2.0
+    lb[1, T // 2:] = r.standard_normal(T - T // 2).astype(np.float32)
+    h = m.scan_log_fwd(_t(la), _t(lb), reverse=reverse)
+    ref = oracle_lib.scan_log_fwd(la, lb, reverse=reverse)
+    close(h, ref, TAU_LOG, "h", relative=True)
+
+
+def test_log_gated_lanes_with_logits(m, oracle_lib):
+    """The -softplus gate-logit forward with logits far out (z = 80: log a =
+    -80) and a reset (z = +inf), both directions."""
+    r = np.random.default_rng(3300)
+    rows, T = 4, 3 * 4096 + 100
+    z = r.standard_normal((rows, T)).astype(np.float32)
+    z[1, 2000:2010] = 80.0
+    z[2, 5000] = np.inf  # a reset: log a = -inf
+    lb = r.standard_normal((rows, T)).astype(np.float32)
+    for rev in (False, True):
+        h = m.scan_log_fwd_gated(_t(z), _t(lb), reverse=rev)
+        ref = oracle_lib.scan_log_fwd_gated(z, lb, reverse=rev)
+        close(h, ref, TAU_LOG, "h", relative=True)

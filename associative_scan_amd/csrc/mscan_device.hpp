@@ -71,6 +71,15 @@ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
 // is still one contiguous block of memory) and spreads the lanes that read
 // unit c of their blocks over 16 different 16-byte bank groups. swz is its
 // own inverse.
+// Cache policy of the direct loads: nontemporal (nt), as the register loads
+// of the streamed arrays are. Every staged array is read exactly once; without
+// the hint these loads allocate in the caches and, behind a large write (dirty
+// lines left in L2 and the Infinity Cache), spend their time on the evictions:
+// log-space forward 8192 rows x T = 8192 after a 1 GiB fill, 204 -> 142 us;
+// (2, 1) matrix forward / backward 4096 rows x T = 8192, 266 -> 190 us and
+// 389 -> 346 us.
+constexpr int kLdsNT = 2;
+
 template <int N, int EL>
 struct Stage {
   static constexpr int FLOATS = N * 64 * EL;  // floats per window
@@ -92,7 +101,7 @@ struct Stage {
       for (int i = 0; i < UNITS / 64; ++i) {
         const int u = swz(i * 64 + l);
         __builtin_amdgcn_global_load_lds((const void*)(g + u * 4),
-                                         (__attribute__((address_space(3))) void*)(lds + i * 256), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(lds + i * 256), 16, 0, kLdsNT);
       }
     } else {
 #pragma unroll 4
@@ -101,7 +110,7 @@ struct Stage {
         const int f = swz(p >> 2) * 4 + (p & 3);
         if (f < nvalid)
           __builtin_amdgcn_global_load_lds((const void*)(g + f),
-                                           (__attribute__((address_space(3))) void*)(lds + i * 64), 4, 0, 0);
+                                           (__attribute__((address_space(3))) void*)(lds + i * 64), 4, 0, kLdsNT);
       }
     }
   }
@@ -320,16 +329,16 @@ struct LinOps {
 // own contribution as a max-shifted sum, log value = m + log s with s >= 1.
 // Carry C = (m, s) for log h = m + log s. Composing two pairs needs one exp
 // and no log; the output is h = e^m * s. P = -inf (a = 0) is hard.
+// Written with selects, not early returns: every lane runs the same
+// instructions (branches around the -inf cases cost the log-space kernels an
+// exec-mask save, a branch and a restore per call).
 __device__ __forceinline__ void lse_pair(float am, float as, float bm, float bs, float& m, float& s) {
   const float M = fmaxf(am, bm);
-  if (M == -__builtin_inff()) {
-    m = M;
-    s = 0.f;
-    return;
-  }
   const float d = am - bm;
   const float E = __expf(-fabsf(d));
-  s = (d >= 0.f) ? __builtin_fmaf(bs, E, as) : __builtin_fmaf(as, E, bs);
+  const bool ge = d >= 0.f;
+  const float t = __builtin_fmaf(ge ? bs : as, E, ge ? as : bs);
+  s = (M == -__builtin_inff()) ? 0.f : t;
   m = M;
 }
 
@@ -342,18 +351,18 @@ struct LogOps {
   __device__ static __forceinline__ C cident() { return C{{-__builtin_inff(), 0.f}}; }
   __device__ static __forceinline__ bool hard(const S& s) { return s.v[0] == -__builtin_inff(); }
   __device__ static __forceinline__ void compose(const S& e, S& l) {
-    if (l.v[0] == -__builtin_inff()) return;
+    const bool hard = l.v[0] == -__builtin_inff();
     float m, s;
     lse_pair(l.v[0] + e.v[1], e.v[2], l.v[1], l.v[2], m, s);
-    l.v[0] = e.v[0] + l.v[0];
-    l.v[1] = m;
-    l.v[2] = s;
+    l.v[0] = hard ? l.v[0] : e.v[0] + l.v[0];
+    l.v[1] = hard ? l.v[1] : m;
+    l.v[2] = hard ? l.v[2] : s;
   }
   __device__ static __forceinline__ C apply(const S& s, const C& c) {
-    if (s.v[0] == -__builtin_inff()) return C{{s.v[1], s.v[2]}};
+    const bool hard = s.v[0] == -__builtin_inff();
     C r;
     lse_pair(s.v[0] + c.v[0], c.v[1], s.v[1], s.v[2], r.v[0], r.v[1]);
-    return r;
+    return C{{hard ? s.v[1] : r.v[0], hard ? s.v[2] : r.v[1]}};
   }
   __device__ static __forceinline__ S of_carry(const C& c) { return S{{-__builtin_inff(), c.v[0], c.v[1]}}; }
   __device__ static __forceinline__ C carry_of_hard(const S& s) { return C{{s.v[1], s.v[2]}}; }

@@ -487,19 +487,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       const int64_t u0 = span_lo(s);
       uint32_t lm = 0;
       if constexpr (!VARLEN) {
-        // one sequence per row: first / last are the row's ends
+        // one sequence per row: first / last are the row's ends, which lie in
+        // the spans of at most two lanes of the row (one range test per lane,
+        // the per-element tests only in those lanes)
         const int64_t tf = REV ? T - 1 : 0, tl = REV ? 0 : T - 1;
+        const int64_t q0 = u0 - lead;
+        const bool ends = (tf >= q0 && tf < q0 + EL) || (BWD && tl >= q0 && tl < q0 + EL);
+        if (ends) {
 #pragma unroll
-        for (int e = 0; e < EL; ++e) {
-          const int64_t t = u0 + P_(e) - lead;
-          if (t == tf) {
-            if constexpr (!BWD) Ops::first_ab(A[s][e], B[s][e], h0row, has_h0);
-            else A[s][e] = 0.f;
-          }
-          if constexpr (BWD) {
-            if (t == tl) {
-              N[s][e] = h0row;
-              lm |= 1u << e;
+          for (int e = 0; e < EL; ++e) {
+            const int64_t t = q0 + P_(e);
+            if (t == tf) {
+              if constexpr (!BWD) Ops::first_ab(A[s][e], B[s][e], h0row, has_h0);
+              else A[s][e] = 0.f;
+            }
+            if constexpr (BWD) {
+              if (t == tl) {
+                N[s][e] = h0row;
+                lm |= 1u << e;
+              }
             }
           }
         }

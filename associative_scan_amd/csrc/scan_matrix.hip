@@ -567,8 +567,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
 template <int K, int V>
 struct MatCfg;
 // waves per workgroup and steps per lane, forward (WF, EF) and backward
-// (WB, EB), from timing sweeps at 4096 rows x T = 8192
-template <> struct MatCfg<2, 1> { static constexpr int WF = 8, EF = 4, WB = 4, EB = 4; };
+// (WB, EB), from timing sweeps at 4096 rows x T = 8192 (the (2, 1) shapes
+// again with nontemporal staged loads and a 1 GiB write before every timed
+// call: forward 4 x 8 0.184 ms, 8 x 4 0.190, 2 x 8 0.194, 4 x 4 0.194, 8 x 8
+// 0.31; backward 4 x 4 0.343 ms, 2 x 4 0.345, 2 x 8 0.36, 4 x 2 0.37, 8 x 4
+// 0.38)
+template <> struct MatCfg<2, 1> { static constexpr int WF = 4, EF = 8, WB = 4, EB = 4; };
 template <> struct MatCfg<2, 2> { static constexpr int WF = 4, EF = 4, WB = 4, EB = 2; };
 template <> struct MatCfg<4, 1> { static constexpr int WF = 1, EF = 4, WB = 2, EB = 2; };
 

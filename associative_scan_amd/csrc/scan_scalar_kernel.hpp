@@ -168,7 +168,10 @@ __device__ __forceinline__ int slice_find(const SegSlice& s, int64_t q) {
 enum : int { kRowLoop = 0, kLookback = 1 };
 enum : int { kGateNone = 0, kGateSigmoid = 1, kGateNegSoftplus = 2 };
 
-__device__ __forceinline__ float sigmoid_f(float z) { return __frcp_rn(1.f + __expf(-z)); }
+// sigmoid(z) = 1 / (1 + e^{-z}) with the hardware reciprocal (1 ulp; exactly 1
+// at z = +inf and 0 at z = -inf). The correctly rounded reciprocal is an
+// eleven-instruction division sequence that made the gated scans VALU-bound.
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 // log(1 + e^z) = max(z, 0) + log1p(u), u = e^{-|z|} in (0, 1], without overflow
 // and without losing its tail for z << 0. log1p(u): for u < 1/16 the series
 // u - u^2/2 + u^3/3 - u^4/4 + u^5/5 (truncation below u^6/6 < 1e-8 relative);
@@ -426,7 +429,14 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         }
       }
     }
-    if constexpr (VARLEN && MODE == kLookback) lookback_slice();
+    // a tile with no sequence start or end inside (its sequence began before
+    // it and ends after it) needs no per-lane boundary search below
+    bool quiet = false;
+    if constexpr (VARLEN && MODE == kLookback) {
+      lookback_slice();
+      const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
+      quiet = seg.n == 2 && (int64_t)seg.v[0] < plo && (int64_t)seg.v[1] > phi;
+    }
     if constexpr (LOGB) {
       // b = e^{log b} (a = e^{log a} was taken on load, 0 for log a = -inf)
 #pragma unroll
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         const int64_t q0 = u0 - lead;
         int k = 0;
         bool walk = false;
-        if (seg.n > 0) {
+        if (seg.n > 0 && !quiet) {
           k = slice_find(seg, max(q0, (int64_t)0));
           // a sequence starts or ends inside [q0, q0 + EL) only if the found
           // start is q0 or the next start is at most q0 + EL

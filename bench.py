@@ -18,8 +18,9 @@ Printed: one JSON line.
   the cache cleared between repetitions): for every measurement below, each
   repetition is preceded by a 1 GiB write to a scratch buffer (outside the
   timed interval, larger than the L2 caches and the 256 MB Infinity Cache),
-  timed alone with HIP events on the launch stream; median, p10 and p90 are
-  reported, with elements/s, GB/s and the fraction of the 8 TB/s peak.
+  timed alone with HIP events on the launch stream, after as many untimed
+  flushed warm-up repetitions; median, p10 and p90 are reported, with
+  elements/s, GB/s and the fraction of the 8 TB/s peak.
 - `ceilings`: the practical bandwidth for each kernel's exact bytes and
   read:write mix, from the library's streaming kernel (mscan_stream_ceiling).
 - `cpu_baseline` (headline) and `cpu_oracle` (every other workload): the fp64
@@ -99,7 +100,12 @@ class Protocol:
     def time(self, fn, reps=None):
         torch = self.torch
         reps = reps or self.reps
-        fn()
+        # warm-up: as many untimed repetitions, each behind its flush, as are
+        # timed (the first few dozen calls on freshly allocated tensors run
+        # up to 10% slower than the steady state)
+        for _ in range(reps):
+            self.flush()
+            fn()
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for e0, e1 in evs:

@@ -149,18 +149,25 @@ __device__ __forceinline__ int wave_count_le(const int32_t* cu, int n, int64_t k
 
 constexpr int kCuSlice = 1024;  // cu_seqlens entries cached in LDS per workgroup
 
+// A run of cu_seqlens entries: in the workgroup's LDS copy (lds) or, for a
+// slice too long for it, in global memory (g). The kernels read it through
+// an accessor that names the array, so each read is an LDS or a global load:
+// one pointer that could be either made every read a flat load, whose wait
+// also waits for the tile's outstanding global loads.
 struct SegSlice {
-  const int32_t* v;  // slice values (LDS or global)
+  const int32_t* g;  // slice values in global memory (when !lds)
   int n;             // entries
-  int k0;            // absolute index of v[0]
+  int k0;            // absolute index of entry 0
+  bool lds;          // entries in the workgroup's LDS copy
 };
 
-// Largest i in [0, n) with v[i] <= q (0 if none).
-__device__ __forceinline__ int slice_find(const SegSlice& s, int64_t q) {
-  int lo = 0, hi = s.n;  // answer in [lo, hi)
+// Largest i in [0, n) with at(i) <= q (0 if none).
+template <class At>
+__device__ __forceinline__ int slice_find(int n, const At& at, int64_t q) {
+  int lo = 0, hi = n;  // answer in [lo, hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)s.v[mid] <= q) lo = mid; else hi = mid;
+    if (at(mid) <= q) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   if constexpr (MODE == kLookback) ws = ws_view(a.ws);
 
   // ---- sequence table ------------------------------------------------------
-  SegSlice seg{nullptr, 0, 0};
+  SegSlice seg{nullptr, 0, 0, false};
   if constexpr (VARLEN) {
     if constexpr (MODE == kRowLoop) {
       // the row's whole table, cached once
@@ -274,9 +281,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       if (n <= kCuSlice) {
         for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[i];
         __syncthreads();
-        seg = SegSlice{s_cu, n, 0};
+        seg = SegSlice{nullptr, n, 0, true};
       } else {
-        seg = SegSlice{a.cu, n, 0};
+        seg = SegSlice{a.cu, n, 0, false};
       }
     }
   }
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         if (l == 0) { s_cu_n = n; s_cu_k0 = ka; }
       }
       __syncthreads();
-      seg = SegSlice{s_cu, s_cu_n, s_cu_k0};
+      seg = SegSlice{nullptr, s_cu_n, s_cu_k0, true};
       return;
     }
     if (w == 0) {
@@ -323,10 +330,17 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     if (n <= kCuSlice) {
       for (int i = threadIdx.x; i < n; i += WAVES * 64) s_cu[i] = a.cu[k0 + i];
       __syncthreads();
-      seg = SegSlice{s_cu, n, k0};
+      seg = SegSlice{nullptr, n, k0, true};
     } else {
-      seg = SegSlice{a.cu + k0, n, k0};
+      seg = SegSlice{a.cu + k0, n, k0, false};
     }
+  };
+  // entry i of the slice, from LDS (LDS = true) or global memory; code that
+  // reads the slice is instantiated for each and chosen by seg.lds (a select
+  // between the two arrays would be compiled into one flat load)
+  auto segv_in = [&](auto in_lds, int i) -> int64_t {
+    if constexpr (decltype(in_lds)::value) return (int64_t)s_cu[i];
+    else return (int64_t)seg.g[i];
   };
 
   C carry = Ops::cident();  // state entering the current tile
@@ -435,7 +449,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     if constexpr (VARLEN && MODE == kLookback) {
       lookback_slice();
       const int64_t plo = max(ut_lo - lead, (int64_t)0), phi = min(ut_lo + TILE - lead, T);
-      quiet = seg.n == 2 && (int64_t)seg.v[0] < plo && (int64_t)seg.v[1] > phi;
+      quiet = seg.n == 2 && seg.lds && segv_in(std::true_type{}, 0) < plo && segv_in(std::true_type{}, 1) > phi;
     }
     if constexpr (LOGB) {
       // b = e^{log b} (a = e^{log a} was taken on load, 0 for log a = -inf)
@@ -519,26 +533,24 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             }
           }
         }
-      } else {
+      } else if (seg.n > 0 && !quiet) {
         // walk the elements in physical order against the sequence table
+        auto bounds = [&](auto in_lds) {
+        auto segv = [&](int i) -> int64_t { return segv_in(in_lds, i); };
         const int64_t q0 = u0 - lead;
-        int k = 0;
-        bool walk = false;
-        if (seg.n > 0 && !quiet) {
-          k = slice_find(seg, max(q0, (int64_t)0));
-          // a sequence starts or ends inside [q0, q0 + EL) only if the found
-          // start is q0 or the next start is at most q0 + EL
-          const int64_t next = (k + 1 < seg.n) ? (int64_t)seg.v[k + 1] : INT64_MAX;
-          walk = ((int64_t)seg.v[k] >= q0) || (next <= q0 + EL);
-        }
+        int k = slice_find(seg.n, segv, max(q0, (int64_t)0));
+        // a sequence starts or ends inside [q0, q0 + EL) only if the found
+        // start is q0 or the next start is at most q0 + EL
+        const int64_t next = (k + 1 < seg.n) ? segv(k + 1) : INT64_MAX;
+        const bool walk = (segv(k) >= q0) || (next <= q0 + EL);
         if (walk) {
 #pragma unroll
           for (int ep = 0; ep < EL; ++ep) {
             const int64_t q = q0 + ep;
             if (q < 0 || q >= T) continue;
-            while (k + 1 < seg.n && (int64_t)seg.v[k + 1] <= q) ++k;
-            const bool is_start = (int64_t)seg.v[k] == q;
-            const bool is_end = (k + 1 < seg.n) && ((int64_t)seg.v[k + 1] - 1 == q);
+            while (k + 1 < seg.n && segv(k + 1) <= q) ++k;
+            const bool is_start = segv(k) == q;
+            const bool is_end = (k + 1 < seg.n) && (segv(k + 1) - 1 == q);
             const int e = REV ? EL - 1 - ep : ep;
             const bool first = REV ? is_end : is_start;
             const bool last = REV ? is_start : is_end;
@@ -558,6 +570,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             }
           }
         }
+        };
+        if (seg.lds) bounds(std::true_type{});
+        else bounds(std::false_type{});
       }
       if constexpr (BWD) lastmask[s] = lm;
     }
@@ -737,7 +752,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
             if (!(lastmask[s] & (1u << e))) continue;
             const int64_t t = u0 + P_(e) - lead;
             int sk = 0;
-            if constexpr (VARLEN) sk = min(max(seg.k0 + slice_find(seg, t), 0), a.nseg - 1);
+            if constexpr (VARLEN) {
+              const int kk = seg.lds ? slice_find(seg.n, [&](int i) { return segv_in(std::true_type{}, i); }, t)
+                                     : slice_find(seg.n, [&](int i) { return segv_in(std::false_type{}, i); }, t);
+              sk = min(max(seg.k0 + kk, 0), a.nseg - 1);
+            }
             // dh0 = g * lam; log space: dlog_h0 = a * lam * h0 (N holds h0 there);
             // nothing reaches h0 through a zero gate (a reset)
             const float gl = G[s][e] * O[s][e];

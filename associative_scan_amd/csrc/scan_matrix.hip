@@ -36,6 +36,8 @@
 // first element is (0, dy). Outputs dB = lam, dA_t = lam_t h_prev^T with
 // h_prev the forward state before t (h0 at a sequence start), and
 // dh0 = A_s^T lam_s at each sequence's forward-first step s.
+#include <type_traits>
+
 #include "mscan_device.hpp"
 #include "mscan_launch.hpp"
 
@@ -153,12 +155,13 @@ __device__ __forceinline__ void gload(const float* p, float* o) {
   for (int i = 0; i < N; ++i) o[i] = p[i];
 }
 
-// Largest i in [0, n) with v[i] <= q (0 if none).
-__device__ __forceinline__ int seg_find(const int32_t* v, int n, int64_t q) {
+// Largest i in [0, n) with at(i) <= q (0 if none).
+template <class At>
+__device__ __forceinline__ int seg_find(const At& at, int n, int64_t q) {
   int lo = 0, hi = n;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)v[mid] <= q) lo = mid; else hi = mid;
+    if (at(mid) <= q) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
     }
   };
 
-  const int32_t* cuv = a.cu;
+  bool cu_lds = false;  // the table is in s_cu (else read from global memory)
   const int ncu = a.nseg + 1;
 
   C carry = Ops::cident();  // state entering the tile
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
       if (ncu <= kMatCuLds) {
         for (int i = threadIdx.x; i < ncu; i += WAVES * 64) s_cu[i] = a.cu[i];
         __syncthreads();
-        cuv = s_cu;
+        cu_lds = true;
       }
     }
     wait_stage_loads();
@@ -280,19 +283,30 @@ __global__ __launch_bounds__(WAVES * 64) void k_matrix(const MatArgs a) {
         if (t == tl) lastm |= 1u << e;
       }
     } else {
-      int k = seg_find(cuv, ncu, max(tlane, (int64_t)0));
+      // instantiated for the LDS copy and for global memory, chosen by a
+      // uniform flag (a pointer that could be either compiles to flat loads,
+      // whose waits also wait for the window's outstanding loads)
+      auto walk = [&](auto in_lds) {
+        auto cuv = [&](int i) -> int64_t {
+          if constexpr (decltype(in_lds)::value) return (int64_t)s_cu[i];
+          else return (int64_t)a.cu[i];
+        };
+        int k = seg_find(cuv, ncu, max(tlane, (int64_t)0));
 #pragma unroll
-      for (int ep = 0; ep < EL; ++ep) {
-        const int64_t q = tlane + ep;
-        if (q >= T) continue;
-        while (k + 1 < ncu && (int64_t)cuv[k + 1] <= q) ++k;
-        const bool is_start = (int64_t)cuv[k] == q;
-        const bool is_end = (k + 1 < ncu) && ((int64_t)cuv[k + 1] - 1 == q);
-        const int e = REV ? EL - 1 - ep : ep;
-        segk[e] = min(max(k, 0), a.nseg - 1);
-        if (REV ? is_end : is_start) firstm |= 1u << e;
-        if (REV ? is_start : is_end) lastm |= 1u << e;
-      }
+        for (int ep = 0; ep < EL; ++ep) {
+          const int64_t q = tlane + ep;
+          if (q >= T) continue;
+          while (k + 1 < ncu && cuv(k + 1) <= q) ++k;
+          const bool is_start = cuv(k) == q;
+          const bool is_end = (k + 1 < ncu) && (cuv(k + 1) - 1 == q);
+          const int e = REV ? EL - 1 - ep : ep;
+          segk[e] = min(max(k, 0), a.nseg - 1);
+          if (REV ? is_end : is_start) firstm |= 1u << e;
+          if (REV ? is_start : is_end) lastm |= 1u << e;
+        }
+      };
+      if (cu_lds) walk(std::true_type{});
+      else walk(std::false_type{});
     }
     auto valid = [&](int e) -> bool { return wlo + sidx(e) < T; };
 

@@ -73,7 +73,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--T", type=int, default=4096)
-    p.add_argument("--reps", type=int, default=30, help="repetitions per protocol measurement")
+    p.add_argument("--reps", type=int, default=50, help="timed repetitions per protocol measurement")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-workloads", action="store_true", help="skip the packed, log-space and matrix workloads")
@@ -133,7 +133,7 @@ def ceiling(m, torch, dev, proto, nsrc, ndst, n_floats):
     n = (n_floats + 3) // 4 * 4
     src = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(nsrc)]
     dst = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(ndst)]
-    t = proto.time(lambda: m.stream_ceiling(src, dst), reps=max(5, proto.reps // 2))
+    t = proto.time(lambda: m.stream_ceiling(src, dst))
     nbytes = (nsrc + ndst) * 4 * n
     del src, dst
     torch.cuda.empty_cache()
@@ -244,7 +244,6 @@ def main():
             gs = torch.rand((B, C, Ts), device=dev, generator=gen_t)
             xs = torch.randn((B, C, Ts), device=dev, generator=gen_t)
             dys = torch.randn((B, C, Ts), device=dev, generator=gen_t)
-            reps = max(5, min(args.reps, int(4e9 // (ns * 32))))
 
             def run(bwd):
                 hs = m.scan_fwd(gs, xs, h0=h0)
@@ -253,7 +252,7 @@ def main():
 
             res = {"T": Ts, "elements": ns}
             for name, bwd, nb in (("fwd", False, BYTES_FWD), ("fwd_bwd", True, BYTES_FWD + BYTES_BWD)):
-                res[name] = _rate(proto.time(lambda: run(bwd), reps=reps), nb * ns, ns, "elements")
+                res[name] = _rate(proto.time(lambda: run(bwd)), nb * ns, ns, "elements")
             if Ts in PAGE_FWDBWD_MS:
                 res["page_h100_fwd_bwd_ms"] = PAGE_FWDBWD_MS[Ts]
             sweep.append(res)
@@ -464,11 +463,10 @@ def other_workloads(m, gen, torch, dev, proto, np):
         h = m.matrix_affine_scan_fwd(A, Bm)
         fb, bb = 4 * (k * k + 2 * k * v), 4 * (2 * k * k + 3 * k * v)
         steps = R * T
-        reps = max(5, proto.reps // 3)
         out[name] = {"workload": f"B=8 x {R // 8} state blocks, T={T}, k={k} v={v}, fp32, resets 1/2048",
-                     "fwd": _rate(proto.time(lambda: m.matrix_affine_scan_fwd(A, Bm), reps=reps), fb * steps, steps,
+                     "fwd": _rate(proto.time(lambda: m.matrix_affine_scan_fwd(A, Bm)), fb * steps, steps,
                                   "steps"),
-                     "bwd": _rate(proto.time(lambda: m.matrix_affine_scan_bwd(A, h, dyk, need_dh0=False), reps=reps),
+                     "bwd": _rate(proto.time(lambda: m.matrix_affine_scan_bwd(A, h, dyk, need_dh0=False)),
                                   bb * steps, steps, "steps")}
         del A, Bm, dyk, h
         torch.cuda.empty_cache()

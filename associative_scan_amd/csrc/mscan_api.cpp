@@ -37,19 +37,32 @@ mscan_status check_problem(const mscan_problem* p) {
   return MSCAN_OK;
 }
 
-// Tiles per row of the scalar kernels for one input type.
+// Tiles per row of the linear scalar kernels for one input type.
 int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
-  return mscan::scalar_tiles(p->T, p->row_stride, mscan::scalar_vec(in_dtype), mscan::scalar_tile_elems(in_dtype));
+  return mscan::scalar_tiles(p->T, p->row_stride, mscan::scalar_vec(in_dtype),
+                             mscan::scalar_tile_elems(in_dtype, p->T));
 }
+// Tiles per row of the log-space kernels (forward and backward).
+int64_t log_tiles_for(const mscan_problem* p) {
+  return mscan::scalar_tiles(p->T, p->row_stride, 4, mscan::log_tile_elems());
+}
+
+enum class ScalarOp { Linear, LinearF32, Log };
 
 // Workspace for a scalar-layout op: header, then (only when rows are chained by
 // look-back) `words` descriptor words per tile (3 for the linear scan, 5 for
-// the log-space scan).
-size_t scalar_ws_bytes(const mscan_problem* p, int words, bool f32_only) {
+// the log-space scan). Linear: every input type (the size does not depend on
+// the call's dtype); LinearF32: fp32 inputs only.
+size_t scalar_ws_bytes(const mscan_problem* p, int words, ScalarOp op) {
   int64_t nt = 0;
-  for (int dt = MSCAN_F32; dt <= (f32_only ? MSCAN_F32 : MSCAN_F16); ++dt) {
-    const int64_t n = scalar_tiles_for(p, dt);
-    if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
+  if (op == ScalarOp::Log) {
+    const int64_t n = log_tiles_for(p);
+    if (mscan::scalar_uses_lookback(p->rows, n)) nt = n;
+  } else {
+    for (int dt = MSCAN_F32; dt <= (op == ScalarOp::LinearF32 ? MSCAN_F32 : MSCAN_F16); ++dt) {
+      const int64_t n = scalar_tiles_for(p, dt);
+      if (mscan::scalar_uses_lookback(p->rows, n) && n > nt) nt = n;
+    }
   }
   if (nt == 0) return mscan::kWsHeaderBytes;
   return mscan::ws_desc_offset() + (size_t)p->rows * (size_t)nt * (size_t)words * sizeof(uint64_t);
@@ -98,15 +111,15 @@ size_t mscan_workspace_bytes(const mscan_problem* prob, int op, int k, int v) {
   switch (op) {
     case MSCAN_OP_SCAN_FWD:
     case MSCAN_OP_SCAN_BWD:
-      return scalar_ws_bytes(prob, 3, false);
+      return scalar_ws_bytes(prob, 3, ScalarOp::Linear);
     case MSCAN_OP_SCAN_LOG_FWD:
-      return scalar_ws_bytes(prob, 5, true);
+      return scalar_ws_bytes(prob, 5, ScalarOp::Log);
     case MSCAN_OP_SCAN_LOG_BWD:
-      return scalar_ws_bytes(prob, 3, true);
+      return scalar_ws_bytes(prob, 3, ScalarOp::Log);
     case MSCAN_OP_MATRIX_FWD:
     case MSCAN_OP_MATRIX_BWD:
       if (!matrix_shape_ok(k, v)) return 0;
-      if (k == 1 && v == 1) return scalar_ws_bytes(prob, 3, true);
+      if (k == 1 && v == 1) return scalar_ws_bytes(prob, 3, ScalarOp::LinearF32);
       return matrix_ws_bytes(prob, k, v);
     default:
       return 0;
@@ -132,7 +145,7 @@ mscan_status scalar_fwd_impl(const mscan_problem* prob, int in_dtype, int gate, 
   if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, false)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, ScalarOp::Linear)))
     return MSCAN_ERR_WORKSPACE;
   mscan::ScalarArgs a{};
   a.g = g;
@@ -162,7 +175,7 @@ mscan_status scalar_bwd_impl(const mscan_problem* prob, int in_dtype, int gate, 
   if ((h0 && ((uintptr_t)h0 & 3u)) || (dh0 && ((uintptr_t)dh0 & 3u))) return MSCAN_ERR_INVALID;
   const int64_t nt = scalar_tiles_for(prob, in_dtype);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, false)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, ScalarOp::Linear)))
     return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dh0 && prob->cu_seqlens) {
@@ -197,9 +210,9 @@ mscan_status log_fwd_impl(const mscan_problem* prob, int gate, const float* log_
   if (!log_a || !log_b || !h) return MSCAN_ERR_INVALID;
   if (!aligned16(log_a) || !aligned16(log_b) || !aligned16(h) || (log_h0 && ((uintptr_t)log_h0 & 3u)))
     return MSCAN_ERR_INVALID;
-  const int64_t nt = scalar_tiles_for(prob, MSCAN_F32);
+  const int64_t nt = log_tiles_for(prob);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 5, true)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 5, ScalarOp::Log)))
     return MSCAN_ERR_WORKSPACE;
   mscan::ScalarArgs a{};
   a.g = log_a;
@@ -227,9 +240,9 @@ mscan_status log_bwd_impl(const mscan_problem* prob, int gate, const float* log_
       !aligned16(dlog_b))
     return MSCAN_ERR_INVALID;
   if ((log_h0 && ((uintptr_t)log_h0 & 3u)) || (dlog_h0 && ((uintptr_t)dlog_h0 & 3u))) return MSCAN_ERR_INVALID;
-  const int64_t nt = scalar_tiles_for(prob, MSCAN_F32);
+  const int64_t nt = log_tiles_for(prob);
   if ((s = check_grid(prob, nt)) != MSCAN_OK) return s;
-  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, true)))
+  if (mscan::scalar_uses_lookback(prob->rows, nt) && (!ws || !aligned16(ws) || ws_bytes < scalar_ws_bytes(prob, 3, ScalarOp::Log)))
     return MSCAN_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (dlog_h0 && prob->cu_seqlens) {
@@ -431,7 +444,7 @@ mscan_status scan_fwd_noalloc(const mscan_problem* prob, int in_dtype, const voi
   if (!g || !x || !h) return MSCAN_ERR_INVALID;
   if (!aligned16(g) || !aligned16(x) || !aligned16(h) || (h0 && ((uintptr_t)h0 & 3u))) return MSCAN_ERR_INVALID;
   if ((s = check_grid(prob, scalar_tiles_for(prob, in_dtype))) != MSCAN_OK) return s;
-  if (scalar_ws_bytes(prob, 3, false) > (size_t)MSCAN_NOALLOC_SCRATCH_BYTES) return MSCAN_ERR_WORKSPACE;
+  if (scalar_ws_bytes(prob, 3, ScalarOp::Linear) > (size_t)MSCAN_NOALLOC_SCRATCH_BYTES) return MSCAN_ERR_WORKSPACE;
   void* ws = nullptr;
   const mscan_status r = hip_status(scratch_on_current_device(&ws));
   if (r != MSCAN_OK) return r;
@@ -474,7 +487,7 @@ mscan_status mscan_debug_partial_fwd(const mscan_problem* prob, int k, int v, co
   if (scalar) {
     per_row = scalar_tiles_for(prob, MSCAN_F32);
     chained = !mscan::scalar_short_rows(prob->T, prob->row_stride) && mscan::scalar_uses_lookback(prob->rows, per_row);
-    need = scalar_ws_bytes(prob, 3, false);
+    need = scalar_ws_bytes(prob, 3, ScalarOp::Linear);
   } else if (mscan::matrix_core_shape(k, v)) {
     per_row = mscan::matrix_core_chunks(prob->T, false, k, v);
     chained = true;

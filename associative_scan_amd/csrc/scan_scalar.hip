@@ -4,12 +4,20 @@
 
 namespace mscan {
 
-// Tile shape, every input type: 4 waves x 4 sub-chunks x 64 lanes x 4 elements
-// (rows of at most 2048 elements take the smaller one-per-row shapes of
-// scan_scalar_short.hip instead).
+// Tile shape of the linear scans, every input type: 4 waves x 4 sub-chunks x
+// 64 lanes x 4 elements (rows of at most 2048 elements take the smaller
+// one-per-row shapes of scan_scalar_short.hip instead). fp32 rows of 4097 to
+// 8191 elements take one tile of 8 waves (8192 elements) instead of two chained
+// ones: 12288 rows of T = 5000 / 6000, forward 151 -> 130 / 172 -> 155 us,
+// backward 258 -> 235 / 295 -> 275 us (a second, mostly empty tile and its
+// look-back cost more than the wider workgroup); at T = 8192 both shapes time
+// alike.
 // (8192-element tiles for the 16-bit forward measured within run-to-run noise,
 // +-8% on the packed bf16 workload.)
-int64_t scalar_tile_elems(int) { return 4 * 4 * 64 * 4; }
+bool scalar_wide_tile(int in_dtype, int64_t T) { return in_dtype == 0 && T > 4096 && T < 8192; }
+int64_t scalar_tile_elems(int in_dtype, int64_t T) { return scalar_wide_tile(in_dtype, T) ? 8192 : 4096; }
+// the log-space kernels: 4096-element tiles at every length
+int64_t log_tile_elems() { return 4 * 64 * 16; }
 int scalar_vec(int) { return 4; }
 
 int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
@@ -31,6 +39,12 @@ template <int GATE>
 static hipError_t launch_scalar_gate(const ScalarArgs& a, int in_dtype, bool bwd, hipStream_t st) {
   if (scalar_short_rows(a.T, a.stride)) return launch_scalar_short(a, in_dtype, GATE, bwd, st);
   const bool rev = a.rev != 0;
+  if (scalar_wide_tile(in_dtype, a.T)) {
+    if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 8, 4, 1, false, GATE>(a, st)
+                        : launch_cfg<LinOps, float, true, false, 8, 4, 1, false, GATE>(a, st);
+    return rev ? launch_cfg<LinOps, float, false, true, 8, 4, 1, false, GATE>(a, st)
+               : launch_cfg<LinOps, float, false, false, 8, 4, 1, false, GATE>(a, st);
+  }
   if (in_dtype == 0) {
     if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, false, GATE>(a, st)
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, false, GATE>(a, st);

@@ -6,15 +6,17 @@ namespace mscan {
 
 // Tile shape of the linear scans, every input type: 4 waves x 4 sub-chunks x
 // 64 lanes x 4 elements (rows of at most 2048 elements take the smaller
-// one-per-row shapes of scan_scalar_short.hip instead). fp32 rows of 4097 to
-// 8191 elements take one tile of 8 waves (8192 elements) instead of two chained
-// ones: 12288 rows of T = 5000 / 6000, forward 151 -> 130 / 172 -> 155 us,
-// backward 258 -> 235 / 295 -> 275 us (a second, mostly empty tile and its
-// look-back cost more than the wider workgroup); at T = 8192 both shapes time
-// alike.
-// (8192-element tiles for the 16-bit forward measured within run-to-run noise,
-// +-8% on the packed bf16 workload.)
-bool scalar_wide_tile(int in_dtype, int64_t T) { return in_dtype == 0 && T > 4096 && T < 8192; }
+// one-per-row shapes of scan_scalar_short.hip instead). Rows of 4097 to 8191
+// elements (8192 for 16-bit inputs) take one tile of 8 waves (8192 elements)
+// instead of two chained ones (a second, mostly empty tile and its look-back
+// cost more than the wider workgroup). 12288 rows, flushed forward /
+// backward: fp32 T = 5000 151 -> 130 / 258 -> 235 us, T = 8000 209 -> 193 /
+// 368 -> 349 us; bf16 T = 5000 155 -> 98 / 235 -> 228 us, T = 8000 192 -> 136 /
+// 344 -> 316 us, T = 8192 138 -> 132 / 309 -> 302 us (fp32 at T = 8192: the
+// forward 2% slower, so it keeps two tiles).
+// (8192-element tiles for the packed bf16 forward, 16 tiles per row, measured
+// within run-to-run noise.)
+bool scalar_wide_tile(int in_dtype, int64_t T) { return T > 4096 && T <= (in_dtype == 0 ? 8191 : 8192); }
 int64_t scalar_tile_elems(int in_dtype, int64_t T) { return scalar_wide_tile(in_dtype, T) ? 8192 : 4096; }
 // the log-space kernels: 4096-element tiles at every length
 int64_t log_tile_elems() { return 4 * 64 * 16; }
@@ -40,10 +42,22 @@ static hipError_t launch_scalar_gate(const ScalarArgs& a, int in_dtype, bool bwd
   if (scalar_short_rows(a.T, a.stride)) return launch_scalar_short(a, in_dtype, GATE, bwd, st);
   const bool rev = a.rev != 0;
   if (scalar_wide_tile(in_dtype, a.T)) {
-    if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 8, 4, 1, false, GATE>(a, st)
-                        : launch_cfg<LinOps, float, true, false, 8, 4, 1, false, GATE>(a, st);
-    return rev ? launch_cfg<LinOps, float, false, true, 8, 4, 1, false, GATE>(a, st)
-               : launch_cfg<LinOps, float, false, false, 8, 4, 1, false, GATE>(a, st);
+    if (in_dtype == 0) {
+      if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 8, 4, 1, false, GATE>(a, st)
+                          : launch_cfg<LinOps, float, true, false, 8, 4, 1, false, GATE>(a, st);
+      return rev ? launch_cfg<LinOps, float, false, true, 8, 4, 1, false, GATE>(a, st)
+                 : launch_cfg<LinOps, float, false, false, 8, 4, 1, false, GATE>(a, st);
+    }
+    if (in_dtype == 2) {
+      if (bwd) return rev ? launch_cfg<LinOps, _Float16, true, true, 8, 4, 1, false, GATE>(a, st)
+                          : launch_cfg<LinOps, _Float16, true, false, 8, 4, 1, false, GATE>(a, st);
+      return rev ? launch_cfg<LinOps, _Float16, false, true, 8, 4, 1, false, GATE>(a, st)
+                 : launch_cfg<LinOps, _Float16, false, false, 8, 4, 1, false, GATE>(a, st);
+    }
+    if (bwd) return rev ? launch_cfg<LinOps, uint16_t, true, true, 8, 4, 1, false, GATE>(a, st)
+                        : launch_cfg<LinOps, uint16_t, true, false, 8, 4, 1, false, GATE>(a, st);
+    return rev ? launch_cfg<LinOps, uint16_t, false, true, 8, 4, 1, false, GATE>(a, st)
+               : launch_cfg<LinOps, uint16_t, false, false, 8, 4, 1, false, GATE>(a, st);
   }
   if (in_dtype == 0) {
     if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, false, GATE>(a, st)

@@ -144,12 +144,14 @@ def test_exact_odd_row_offsets(m, oracle_lib, dt, stride_pad):
             run_exact(m, oracle_lib, g, x, dy, h0[:1], None, rev, dt, gated, stride=T + stride_pad)
 
 
-@pytest.mark.parametrize("T", [4097, 6001, 8185, 8188, 8191])
-def test_exact_one_wide_tile_rows(m, oracle_lib, T):
-    """fp32 rows of 4097 to 8191 elements run as one 8192-element tile; rows
-    that start off a vector boundary near 8191 need a second one (look-back).
-    Dense and packed, gated and not, both directions, aligned and odd strides."""
-    r = np.random.default_rng(1250 + T)
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("T", [4097, 6001, 8185, 8188, 8191, 8192])
+def test_exact_one_wide_tile_rows(m, oracle_lib, dt, T):
+    """Rows of 4097 to 8191 elements (8192 for 16-bit inputs) run as one
+    8192-element tile; rows that start off a vector boundary near the end need
+    a second one (look-back). Dense and packed, gated and not, both
+    directions, aligned and odd strides."""
+    r = np.random.default_rng(1250 + T + 10000 * DTYPES.index(dt))
     rows = 5
     for gated in (False, True):
         g, x, dy = _exact_inputs(r, rows, T, gated)
@@ -157,8 +159,8 @@ def test_exact_one_wide_tile_rows(m, oracle_lib, T):
         h0 = r.integers(-1, 2, (4, rows)).astype(np.float32)
         for rev in (False, True):
             for pad in (0, 1, 3):
-                run_exact(m, oracle_lib, g, x, dy, h0, cu, rev, "fp32", gated, stride=T + pad)
-                run_exact(m, oracle_lib, g, x, dy, h0[:1], None, rev, "fp32", gated, stride=T + pad)
+                run_exact(m, oracle_lib, g, x, dy, h0, cu, rev, dt, gated, stride=T + pad)
+                run_exact(m, oracle_lib, g, x, dy, h0[:1], None, rev, dt, gated, stride=T + pad)
 
 
 @pytest.mark.parametrize("dt", DTYPES)

@@ -44,7 +44,7 @@ int64_t scalar_tiles_for(const mscan_problem* p, int in_dtype) {
 }
 // Tiles per row of the log-space kernels (forward and backward).
 int64_t log_tiles_for(const mscan_problem* p) {
-  return mscan::scalar_tiles(p->T, p->row_stride, 4, mscan::log_tile_elems());
+  return mscan::scalar_tiles(p->T, p->row_stride, 4, mscan::log_tile_elems(p->T));
 }
 
 enum class ScalarOp { Linear, LinearF32, Log };

@@ -31,7 +31,8 @@ struct ScalarArgs {
 // Elements per tile of the scalar kernels, and tiles per row for a given T.
 bool scalar_wide_tile(int in_dtype, int64_t T);       // linear scan: one 8192-element tile
 int64_t scalar_tile_elems(int in_dtype, int64_t T);    // linear scans
-int64_t log_tile_elems();                              // log-space scans
+bool log_wide_tile(int64_t T);                         // log-space scan: one 8192-element tile
+int64_t log_tile_elems(int64_t T);                     // log-space scans
 int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile);
 int scalar_vec(int in_dtype);
 // Whether a scalar call chains the tiles of a row by look-back (few long rows).

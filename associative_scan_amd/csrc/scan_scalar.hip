@@ -18,8 +18,12 @@ namespace mscan {
 // within run-to-run noise.)
 bool scalar_wide_tile(int in_dtype, int64_t T) { return T > 4096 && T <= (in_dtype == 0 ? 8191 : 8192); }
 int64_t scalar_tile_elems(int in_dtype, int64_t T) { return scalar_wide_tile(in_dtype, T) ? 8192 : 4096; }
-// the log-space kernels: 4096-element tiles at every length
-int64_t log_tile_elems() { return 4 * 64 * 16; }
+// The log-space kernels: 4096-element tiles, and one 8192-element tile of 8
+// waves for rows of 4097 to 8192 elements (8192 rows of T = 8192, flushed:
+// forward 137 -> 135 us, backward 274 -> 266 us, plus the look-back's
+// descriptor fill saved).
+bool log_wide_tile(int64_t T) { return T > 4096 && T <= 8192; }
+int64_t log_tile_elems(int64_t T) { return log_wide_tile(T) ? 8192 : 4096; }
 int scalar_vec(int) { return 4; }
 
 int64_t scalar_tiles(int64_t T, int64_t stride, int vec, int64_t tile) {
@@ -94,6 +98,9 @@ hipError_t launch_scalar_sigmoid(const ScalarArgs& a, int in_dtype, bool bwd, hi
 // 6-11% slower that way and keep 4-element lanes.)
 hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
   if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNone, false, st);
+  if (log_wide_tile(a.T))
+    return a.rev ? launch_cfg<LogOps, float, false, true, 8, 1, 4, false, kGateNone, true>(a, st)
+                 : launch_cfg<LogOps, float, false, false, 8, 1, 4, false, kGateNone, true>(a, st);
   return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNone, true>(a, st)
                : launch_cfg<LogOps, float, false, false, 4, 1, 4, false, kGateNone, true>(a, st);
 }
@@ -101,6 +108,9 @@ hipError_t launch_log(const ScalarArgs& a, hipStream_t st) {
 // Log-space backward: the fp32 adjoint scan with exponentiated gates.
 hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
   if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNone, true, st);
+  if (log_wide_tile(a.T))
+    return a.rev ? launch_cfg<LinOps, float, true, true, 8, 4, 1, true>(a, st)
+                 : launch_cfg<LinOps, float, true, false, 8, 4, 1, true>(a, st);
   return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true>(a, st)
                : launch_cfg<LinOps, float, true, false, 4, 4, 1, true>(a, st);
 }
@@ -108,6 +118,12 @@ hipError_t launch_log_bwd(const ScalarArgs& a, hipStream_t st) {
 // Log-space scan with log a = -softplus(z): forward and backward.
 hipError_t launch_log_softplus(const ScalarArgs& a, bool bwd, hipStream_t st) {
   if (scalar_short_rows(a.T, a.stride)) return launch_log_short(a, kGateNegSoftplus, bwd, st);
+  if (log_wide_tile(a.T)) {
+    if (bwd) return a.rev ? launch_cfg<LinOps, float, true, true, 8, 4, 1, true, kGateNegSoftplus>(a, st)
+                          : launch_cfg<LinOps, float, true, false, 8, 4, 1, true, kGateNegSoftplus>(a, st);
+    return a.rev ? launch_cfg<LogOps, float, false, true, 8, 1, 4, false, kGateNegSoftplus, true>(a, st)
+                 : launch_cfg<LogOps, float, false, false, 8, 1, 4, false, kGateNegSoftplus, true>(a, st);
+  }
   if (bwd) return a.rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, true, kGateNegSoftplus>(a, st)
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, true, kGateNegSoftplus>(a, st);
   return a.rev ? launch_cfg<LogOps, float, false, true, 4, 1, 4, false, kGateNegSoftplus, true>(a, st)

@@ -52,7 +52,7 @@ def test_logspace_workload_full(m, oracle_lib):
     close(h, ref, TAU_LOG, "h")
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 4095, 4096, 4097, 20000])
+@pytest.mark.parametrize("T", [1, 2, 7, 4095, 4096, 4097, 6000, 8192, 8193, 20000])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_log_lengths_with_h0(m, oracle_lib, T, reverse):
     r = np.random.default_rng(T + 7 * reverse)
@@ -138,7 +138,7 @@ def test_log_bwd_workload_full(m, oracle_lib):
     _log_bwd_case(m, oracle_lib, d["log_a"], d["log_b"], dy)
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 4095, 4096, 4097, 20000])
+@pytest.mark.parametrize("T", [1, 2, 7, 4095, 4096, 4097, 6000, 8192, 8193, 20000])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_log_bwd_lengths_with_h0(m, oracle_lib, T, reverse):
     r = np.random.default_rng(100 + T + reverse)

@@ -429,6 +429,32 @@ __device__ __forceinline__ void tile_of_block(int64_t rows, int ntiles, uint32_t
   }
 }
 
+// Row and tile of this workgroup in grouped order: a row's tiles in groups of
+// K consecutive tiles (the last group of a row may be shorter), the groups
+// tile-major (group g of every row before group g + 1 of any row) and the K
+// tiles of a group row-major, dispatched one after another. K = 1 is
+// tile-major, K >= ntiles row-major. A tile's predecessor in its row is always
+// an earlier block.
+__device__ __forceinline__ void tile_of_block_grouped(int64_t rows, int ntiles, uint32_t blk0, int K, int64_t& r,
+                                                      int& c) {
+  const uint64_t b = (uint64_t)blockIdx.x + blk0;
+  const int nfull = ntiles / K;                // full groups per row
+  const uint64_t per = (uint64_t)K * (uint64_t)rows;  // blocks per full group index
+  const uint64_t g = b / per;
+  if (g < (uint64_t)nfull) {
+    const uint64_t w = b - g * per;
+    const uint64_t q = w / (uint64_t)K;
+    r = (int64_t)q;
+    c = (int)(g * (uint64_t)K + (w - q * (uint64_t)K));
+  } else {
+    const uint64_t Kt = (uint64_t)(ntiles - nfull * K);  // the short last group
+    const uint64_t w = b - (uint64_t)nfull * per;
+    const uint64_t q = w / Kt;
+    r = (int64_t)q;
+    c = (int)((uint64_t)nfull * (uint64_t)K + (w - q * Kt));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decoupled look-back. Descriptor set of tile i = NS aggregate words followed
 // by NC inclusive words (the state at the tile's end). Run by one whole wave;

@@ -431,12 +431,20 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
     h = first ? Y[s] : hn;  // h holds lam in the backward
     if constexpr (BWD) {
       // dA_t = lam h_prev^T (the transpose is a whole-wave operation)
-      const v4f dA = TL::mm(TL::d_to_r(s_t, h), H[s], mc_zero());
+      const v4f lamR = TL::d_to_r(s_t, h);
       if (s < n) {
         const int64_t j = j0 + s;
         const int64_t t = wk.phys(j);
-        wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
-        wk.sh.stA_D(wk.blkA(a.out1, t), dA);
+        if constexpr (FULL) {
+          // both leave as rows, one 16-byte store per lane each: dB = lam from
+          // its R layout, and dA from h_prev lam^T = dA^T, whose D layout is
+          // the R layout of dA (16 x 16, 512 rows x T = 4096: 2.29 -> 2.23 ms)
+          *(v4f*)(wk.blkB(a.out0, t) + TL::dc() * 16 + TL::dr0()) = lamR;
+          *(v4f*)(wk.blkA(a.out1, t) + TL::dc() * 16 + TL::dr0()) = TL::mm(H[s], lamR, mc_zero());
+        } else {
+          wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
+          wk.sh.stA_D(wk.blkA(a.out1, t), TL::mm(lamR, H[s], mc_zero()));
+        }
       }
       if (((lastm >> s) & 1u) && a.dh0 && s < n) {
         // dh0 = A_s^T lam_s (A_s^T in R layout is A_s in D layout); 0 where
@@ -449,9 +457,9 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
     } else if constexpr (FULL) {
       // h leaves as rows: one 16-byte store per lane (16 x 16 forward, 512 rows
       // x T = 4096 after a 1 GiB fill, with the row loads above: 1.35 -> 1.22
-      // ms). (The same in the backward, for dB and dA, measured 30% slower:
-      // there the compiler's waits for the loaded operands also wait for the
-      // stores issued after them.)
+      // ms). Nontemporal here; in the backward nontemporal row stores were 9%
+      // slower than plain ones, and row loads of its D-layout operands (two
+      // more LDS transposes per step at one wave per SIMD) 40% slower.
       const v4f hR = TL::d_to_r(s_t, h);
       if (s < n) __builtin_nontemporal_store(hR, (v4f*)(wk.blkB(a.out0, wk.phys(j0 + s)) + TL::dc() * 16 + TL::dr0()));
     } else {

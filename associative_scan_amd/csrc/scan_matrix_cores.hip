@@ -656,8 +656,9 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
     h = sel4(first, Y[s], hn);  // h holds lam in the backward
     if constexpr (BWD) {
       const v4f lamR = TL::d_to_r(s_t, h);
-      const v4f dA = TL::mm(lamR, H[s], mc_zero());
-      const v4f dAR = FULL ? TL::d_to_r(s_t, dA) : dA;  // FULL: stored as rows
+      // dA = lam h_prev^T; FULL stores it as rows, computed as h_prev lam^T =
+      // dA^T, whose D layout is the R layout of dA (no transpose)
+      const v4f dAR = FULL ? TL::mm(H[s], lamR, mc_zero()) : TL::mm(lamR, H[s], mc_zero());
       if (s < nb) {
         const int64_t t = wk.phys(jb + s);
         if constexpr (FULL) {
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
           *(v4f*)(wk.blkA(a.out1, t) + TL::dc() * 4) = dAR;
         } else {
           wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
-          wk.sh.stA_D(wk.blkA(a.out1, t), dA);
+          wk.sh.stA_D(wk.blkA(a.out1, t), dAR);
         }
       }
       const bool l = ((lastm >> s) & 1u) && s < nb;

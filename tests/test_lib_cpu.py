@@ -61,8 +61,20 @@ def test_workspace_sizes(m):
     # the log-space scan publishes 5 words per tile
     assert m.workspace_bytes(_prob(m, rows=3, T=65536), m.OP_SCAN_LOG_FWD) == 128 + 3 * 16 * 40
     assert m.workspace_bytes(_prob(m, rows=3, T=65536), m.OP_SCAN_FWD) == 128 + 3 * 16 * 24
-    # rows that do not all start 16-byte aligned may need one more tile
-    assert m.workspace_bytes(_prob(m, rows=3, T=8190, stride=8193), m.OP_SCAN_FWD) == 128 + 3 * 3 * 24
+    # rows of 4097 to 8191 elements (8192 for 16-bit inputs; 8192 for the
+    # log-space scan) take one 8192-element tile: no chain when the rows start
+    # 16-byte aligned, two tiles when a row start off that grid pushes the
+    # row's last elements past the tile
+    assert m.workspace_bytes(_prob(m, rows=3, T=8190, stride=8192), m.OP_SCAN_FWD) == 128
+    assert m.workspace_bytes(_prob(m, rows=3, T=8190, stride=8193), m.OP_SCAN_FWD) == 128 + 3 * 2 * 24
+    assert m.workspace_bytes(_prob(m, rows=3, T=8192), m.OP_SCAN_LOG_FWD) == 128
+    assert m.workspace_bytes(_prob(m, rows=3, T=8193), m.OP_SCAN_LOG_FWD) == 128 + 3 * 3 * 40
+    # fp32 rows of 8192 keep two 4096-element tiles
+    assert m.workspace_bytes(_prob(m, rows=3, T=8192), m.OP_SCAN_FWD) == 128 + 3 * 2 * 24
+    # beyond 8192, 4096-element tiles; rows that do not all start 16-byte
+    # aligned may need one more
+    assert m.workspace_bytes(_prob(m, rows=3, T=12288), m.OP_SCAN_FWD) == 128 + 3 * 3 * 24
+    assert m.workspace_bytes(_prob(m, rows=3, T=12286, stride=12289), m.OP_SCAN_FWD) == 128 + 3 * 4 * 24
     assert m.workspace_bytes(_prob(m, rows=0), m.OP_SCAN_FWD) == 0
     assert m.workspace_bytes(_prob(m, T=10, stride=5), m.OP_SCAN_FWD) == 0
 

@@ -230,12 +230,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
   static_assert(!XP || (SUBS == 1 && EL == 16 && sizeof(Tin) == 4), "staged windows are fp32, 16 per lane");
   using SX = Stage<1, EL>;
   // Look-back dispatch order (see tile_of_block), from timing each workload
-  // (packed: C = 1536 x 65536 tokens in 16 sequences): dense linear rows
-  // stream memory best row-major (tile-major cost ~10% at T = 16384), and so
-  // do the packed linear backward (tile-major 5-7% slower) and the packed fp32
-  // forward (4%); the packed 16-bit forward (row-major 8% slower) and the
-  // log-space kernels resolve their look-back faster tile-major.
-  constexpr bool kTileMajor = (VARLEN && !BWD && sizeof(Tin) == 2) || LOGB || !std::is_same<Ops, LinOps>::value;
+  // (packed: C = 1536 x 65536 tokens in 16 sequences): linear rows stream
+  // memory best row-major, dense (tile-major cost ~10% at T = 16384; 16-bit
+  // rows at T = 65536 7%) and packed alike (backward 5-7%, fp32 forward 4%,
+  // 16-bit forward 2% since its boundaries are found without a per-lane
+  // search); the log-space kernels resolve their look-back faster tile-major.
+  constexpr bool kTileMajor = LOGB || !std::is_same<Ops, LinOps>::value;
   constexpr int NXR = BWD ? (LOGB ? 4 : 3) : 2;  // staged arrays per wave
   __shared__ __attribute__((aligned(16))) float s_x[XP ? WAVES : 1][XP ? NXR * SX::FLOATS : 4];
 
@@ -505,6 +505,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 
     // ---- sequence boundaries ------------------------------------------------
     // first: a sequence's first element in processing order; last: its last.
+    // few: a forward call without initial states whose tile is covered by at
+    // most kFewBounds table entries (the common packed case: a few sequence
+    // starts per tile). Every lane then tests each entry against its span in
+    // a wave-uniform loop instead of searching the slice and walking its
+    // elements (a per-lane binary search and a divergent walk, both through
+    // LDS: 9% of the packed 16-bit forward, C = 1536 x 65536 tokens in 16
+    // sequences, 156 -> 143 us).
+    constexpr int kFewBounds = 8;
+    const bool few = VARLEN && !BWD && !has_h0 && seg.lds && seg.n <= kFewBounds;
     uint32_t lastmask[BWD ? SUBS : 1];
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
@@ -531,6 +540,28 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
                 lm |= 1u << e;
               }
             }
+          }
+        }
+      } else if (few && !quiet) {
+        // Position q starts a sequence iff some entry equals q, and ends one
+        // iff some entry equals q + 1 (the entries are sorted and the first is
+        // at or before the tile's first element). The processing order's
+        // first element is the start (forward) or the end (reverse).
+        const int64_t q0 = u0 - lead;
+        uint32_t fm = 0;
+#pragma unroll
+        for (int i = 0; i < kFewBounds; ++i) {
+          if (i < seg.n) {
+            const int64_t q = segv_in(std::true_type{}, i) - (REV ? 1 : 0);
+            const int64_t d = q - q0;
+            if ((uint64_t)q < (uint64_t)T && (uint64_t)d < (uint64_t)EL) fm |= 1u << (int)d;
+          }
+        }
+        if (fm) {
+#pragma unroll
+          for (int ep = 0; ep < EL; ++ep) {
+            const int e = REV ? EL - 1 - ep : ep;
+            if ((fm >> ep) & 1u) Ops::first_ab(A[s][e], B[s][e], 0.f, false);
           }
         }
       } else if (seg.n > 0 && !quiet) {

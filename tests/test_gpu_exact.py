@@ -128,6 +128,39 @@ def test_exact_varlen_every_kernel(m, oracle_lib, dt, gated, reverse):
     run_exact(m, oracle_lib, g, x, dy, h0, cu, reverse, dt, gated)
 
 
+def _boundaries_at_every_offset(T):
+    """cu_seqlens for 5 tiles and a tail: the first tile holds sequence starts
+    at every offset inside a lane's 4-element span, at a wave edge (1024,
+    twice: an empty sequence) and on its last element (6 entries inside: the
+    wave-uniform pass); the second holds 12 (the per-lane search); the third
+    3 at sub-chunk and wave edges; none in the fourth (one sequence spans
+    it); a length-one sequence at the row's end."""
+    assert T > 5 * 4096
+    cuts = [1, 258, 515, 1024, 1024, 4095]
+    cuts += [4096 + 3 + 37 * i for i in range(12)]
+    cuts += [8192 + 256, 8192 + 1023, 8192 + 2048]
+    cuts += [4 * 4096 + 616, T - 1]
+    assert all(0 < c < T for c in cuts)
+    return np.array([0] + sorted(cuts) + [T], np.int32)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("stride_pad", [0, 1])
+def test_exact_varlen_no_h0_boundary_offsets(m, oracle_lib, dt, gated, reverse, stride_pad):
+    """Packed rows without initial states: the forward finds the boundaries of
+    a tile covered by few cu_seqlens entries with one wave-uniform pass and
+    falls back to its per-lane search above that; both must mark exactly the
+    oracle's sequence starts (ends in reverse), bit for bit, at every offset
+    and alignment."""
+    r = np.random.default_rng(3000 + DTYPES.index(dt) * 8 + gated * 4 + reverse * 2 + stride_pad)
+    rows, T = 2, 5 * 4096 + 77
+    g, x, dy = _exact_inputs(r, rows, T, gated)
+    cu = _boundaries_at_every_offset(T)
+    run_exact(m, oracle_lib, g, x, dy, None, cu, reverse, dt, gated, stride=T + stride_pad)
+
+
 @pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("stride_pad", [1, 2, 3])
 def test_exact_odd_row_offsets(m, oracle_lib, dt, stride_pad):

@@ -609,34 +609,54 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     }
 
     // ---- lane-serial summaries and wave scans ---------------------------
-    S sum[SUBS];
+    // plain: every step of the wave allows the operator's plain form (log
+    // space: all log a and log b finite), decided per wave; the wave's own
+    // compositions and applications then skip the -inf selects.
+    bool plain = false;
+    if constexpr (Ops::kHasPlain) {
+      bool ok = true;
 #pragma unroll
-    for (int s = 0; s < SUBS; ++s) {
-      S run = Ops::ident();
+      for (int s = 0; s < SUBS; ++s)
 #pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        S el = Ops::elem(A[s][e], B[s][e]);
-        Ops::compose(run, el);
-        run = el;
-      }
-      sum[s] = run;
+        for (int e = 0; e < EL; ++e) ok = ok && Ops::plain_elem(A[s][e], B[s][e]);
+      plain = __ballot(!ok) == 0ull;
     }
-    {
+    S sum[SUBS];
+    auto wave_scan = [&](auto plain_c) {
+      constexpr bool PL = decltype(plain_c)::value;
+#pragma unroll
+      for (int s = 0; s < SUBS; ++s) {
+        S run = Ops::ident();
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          S el = Ops::elem(A[s][e], B[s][e]);
+          if constexpr (PL) Ops::compose_plain(run, el);
+          else Ops::compose(run, el);
+          run = el;
+        }
+        sum[s] = run;
+      }
       // step-major so the SUBS independent scans interleave
       const bool v1 = (l & 15) >= 1, v2 = (l & 15) >= 2, v4 = (l & 15) >= 4, v8 = (l & 15) >= 8;
       const bool v16 = (l & 16) != 0, v32 = l >= 32;
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr1, 0xf>(sum[s], v1);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr1, 0xf, PL>(sum[s], v1);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr2, 0xf>(sum[s], v2);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr2, 0xf, PL>(sum[s], v2);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr4, 0xf>(sum[s], v4);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr4, 0xf, PL>(sum[s], v4);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr8, 0xf>(sum[s], v8);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowShr8, 0xf, PL>(sum[s], v8);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast15, 0xa>(sum[s], v16);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast15, 0xa, PL>(sum[s], v16);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast31, 0xc>(sum[s], v32);
+      for (int s = 0; s < SUBS; ++s) scan_step<Ops, kRowBcast31, 0xc, PL>(sum[s], v32);
+    };
+    if constexpr (Ops::kHasPlain) {
+      if (plain) wave_scan(std::true_type{});
+      else wave_scan(std::false_type{});
+    } else {
+      wave_scan(std::false_type{});
     }
     // wave aggregate = sub-chunk totals (lane 63) in order
     S wagg = Ops::ident();
@@ -709,21 +729,37 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     // ---- apply: every element from its exact carry-in ---------------------------
     C hs = Ops::apply(ex, carry);  // state entering this wave's span
     float O[SUBS][EL];
+    auto wave_apply = [&](auto plain_c) {
+      constexpr bool PL = decltype(plain_c)::value;
 #pragma unroll
-    for (int s = 0; s < SUBS; ++s) {
-      const C v = Ops::apply(sum[s], hs);  // state after this lane
-      C st;
+      for (int s = 0; s < SUBS; ++s) {
+        C v;  // state after this lane
+        if constexpr (PL) v = Ops::apply_plain(sum[s], hs);
+        else v = Ops::apply(sum[s], hs);
+        C st;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        st.v[i] = __shfl_up(v.v[i], 1, 64);
-        if (l == 0) st.v[i] = hs.v[i];
-        hs.v[i] = readlane_f(v.v[i], 63);
+        for (int i = 0; i < NC; ++i) {
+          st.v[i] = __shfl_up(v.v[i], 1, 64);
+          if (l == 0) st.v[i] = hs.v[i];
+          hs.v[i] = readlane_f(v.v[i], 63);
+        }
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          if constexpr (PL) {
+            st = Ops::step_plain(A[s][e], B[s][e], st);
+            O[s][e] = Ops::out_plain(st);
+          } else {
+            st = Ops::step(A[s][e], B[s][e], st);
+            O[s][e] = Ops::out(st);
+          }
+        }
       }
-#pragma unroll
-      for (int e = 0; e < EL; ++e) {
-        st = Ops::step(A[s][e], B[s][e], st);
-        O[s][e] = Ops::out(st);
-      }
+    };
+    if constexpr (Ops::kHasPlain) {
+      if (plain) wave_apply(std::true_type{});
+      else wave_apply(std::false_type{});
+    } else {
+      wave_apply(std::false_type{});
     }
     carry = Ops::apply(tagg, carry);  // state at the end of the tile
 

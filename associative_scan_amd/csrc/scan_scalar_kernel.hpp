@@ -514,6 +514,19 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
     // sequences, 156 -> 143 us).
     constexpr int kFewBounds = 8;
     const bool few = VARLEN && !BWD && !has_h0 && seg.lds && seg.n <= kFewBounds;
+    // the marked positions (starts, or ends when reversed) of the few entries,
+    // read once per tile into wave-uniform registers; -1 for none or outside
+    // the row
+    uint32_t fq[VARLEN && !BWD ? kFewBounds : 1];
+    if constexpr (VARLEN && !BWD) {
+      if (few) {
+#pragma unroll
+        for (int i = 0; i < kFewBounds; ++i) {
+          const int64_t q = (i < seg.n) ? (int64_t)s_cu[i] - (REV ? 1 : 0) : -1;
+          fq[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint64_t)q < (uint64_t)T ? q : -1));
+        }
+      }
+    }
     uint32_t lastmask[BWD ? SUBS : 1];
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
@@ -547,14 +560,15 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         // iff some entry equals q + 1 (the entries are sorted and the first is
         // at or before the tile's first element). The processing order's
         // first element is the start (forward) or the end (reverse).
-        const int64_t q0 = u0 - lead;
+        // (q - q0 lies in (-2^32 + EL, 2^32), so its low 32 bits are below EL
+        // exactly when q - q0 is)
+        const uint32_t q0 = (uint32_t)(u0 - lead);
         uint32_t fm = 0;
 #pragma unroll
         for (int i = 0; i < kFewBounds; ++i) {
-          if (i < seg.n) {
-            const int64_t q = segv_in(std::true_type{}, i) - (REV ? 1 : 0);
-            const int64_t d = q - q0;
-            if ((uint64_t)q < (uint64_t)T && (uint64_t)d < (uint64_t)EL) fm |= 1u << (int)d;
+          if (i < seg.n && fq[i] != 0xffffffffu) {
+            const uint32_t d = fq[i] - q0;
+            if (d < (uint32_t)EL) fm |= 1u << d;
           }
         }
         if (fm) {

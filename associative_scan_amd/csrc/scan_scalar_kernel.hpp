@@ -505,15 +505,18 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 
     // ---- sequence boundaries ------------------------------------------------
     // first: a sequence's first element in processing order; last: its last.
-    // few: a forward call without initial states whose tile is covered by at
-    // most kFewBounds table entries (the common packed case: a few sequence
-    // starts per tile). Every lane then tests each entry against its span in
-    // a wave-uniform loop instead of searching the slice and walking its
-    // elements (a per-lane binary search and a divergent walk, both through
-    // LDS: 9% of the packed 16-bit forward, C = 1536 x 65536 tokens in 16
-    // sequences, 156 -> 143 us).
+    // few: a forward tile covered by at most kFewBounds table entries (the
+    // common packed case: a few sequence starts per tile). Every lane then
+    // tests each entry against its span in a wave-uniform loop instead of
+    // searching the slice and walking its elements (a per-lane binary search
+    // and a divergent walk, both through LDS: 9% of the packed 16-bit
+    // forward, C = 1536 x 65536 tokens in 16 sequences, 156 -> 143 us).
+    // With initial states it serves the reverse direction only: the lookup of
+    // each start's h0 raised the causal kernel to 91 VGPRs (5 waves per SIMD
+    // instead of 6, 6% slower without h0) and gained nothing there, while the
+    // reverse one kept its registers and ran 8% faster with h0.
     constexpr int kFewBounds = 8;
-    const bool few = VARLEN && !BWD && !has_h0 && seg.lds && seg.n <= kFewBounds;
+    const bool few = VARLEN && !BWD && seg.lds && seg.n <= kFewBounds && (REV || !has_h0);
     // the marked positions (starts, or ends when reversed) of the few entries,
     // read once per tile into wave-uniform registers; -1 for none or outside
     // the row
@@ -577,7 +580,23 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
 #pragma unroll
           for (int ep = 0; ep < EL; ++ep) {
             const int e = REV ? EL - 1 - ep : ep;
-            if ((fm >> ep) & 1u) Ops::first_ab(A[s][e], B[s][e], 0.f, false);
+            if ((fm >> ep) & 1u) {
+              float hv = 0.f;
+              if constexpr (REV) {
+                if (has_h0) {
+                  // the sequence this element ends: one before the first
+                  // entry equal to its successor (the walk's k)
+                  const uint32_t q = q0 + (uint32_t)ep;
+                  int k = 0;
+#pragma unroll
+                  for (int i = kFewBounds - 1; i >= 0; --i)
+                    if (i < seg.n && fq[i] == q) k = i;
+                  const int sk = min(max(seg.k0 + k - 1, 0), a.nseg - 1);
+                  hv = h0val((int64_t)sk * a.rows + r);
+                }
+              }
+              Ops::first_ab(A[s][e], B[s][e], hv, has_h0);
+            }
           }
         }
       } else if (seg.n > 0 && !quiet) {

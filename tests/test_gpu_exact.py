@@ -148,17 +148,20 @@ def _boundaries_at_every_offset(T):
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("stride_pad", [0, 1])
-def test_exact_varlen_no_h0_boundary_offsets(m, oracle_lib, dt, gated, reverse, stride_pad):
-    """Packed rows without initial states: the forward finds the boundaries of
-    a tile covered by few cu_seqlens entries with one wave-uniform pass and
-    falls back to its per-lane search above that; both must mark exactly the
-    oracle's sequence starts (ends in reverse), bit for bit, at every offset
-    and alignment."""
-    r = np.random.default_rng(3000 + DTYPES.index(dt) * 8 + gated * 4 + reverse * 2 + stride_pad)
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_exact_varlen_boundary_offsets(m, oracle_lib, dt, gated, reverse, stride_pad, with_h0):
+    """Packed rows: the forward finds the boundaries of a tile covered by few
+    cu_seqlens entries with one wave-uniform pass (and each start's initial
+    state by the entry's index) and falls back to its per-lane search above
+    that; both must mark exactly the oracle's sequence starts (ends in
+    reverse) and inject the right h0, bit for bit, at every offset and
+    alignment."""
+    r = np.random.default_rng(3000 + DTYPES.index(dt) * 16 + gated * 8 + reverse * 4 + stride_pad * 2 + with_h0)
     rows, T = 2, 5 * 4096 + 77
     g, x, dy = _exact_inputs(r, rows, T, gated)
     cu = _boundaries_at_every_offset(T)
-    run_exact(m, oracle_lib, g, x, dy, None, cu, reverse, dt, gated, stride=T + stride_pad)
+    h0 = r.integers(-1, 2, (len(cu) - 1, rows)).astype(np.float32) if with_h0 else None
+    run_exact(m, oracle_lib, g, x, dy, h0, cu, reverse, dt, gated, stride=T + stride_pad)
 
 
 @pytest.mark.parametrize("dt", DTYPES)

@@ -537,13 +537,16 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
       uint32_t lm = 0;
       if constexpr (!VARLEN) {
         // one sequence per row: first / last are the row's ends, which lie in
-        // the spans of at most two lanes of the row. Lanes of 16 elements test
-        // their span once before the per-element tests; lanes of 4 compare
-        // every element (the range test and its branch cost the dense fp32
-        // backward 0.5%)
+        // the spans of at most two lanes of the row. Lanes test their span
+        // once before the per-element tests, except in the linear scans'
+        // one-tile rows (4-element lanes), where comparing every element was
+        // 0.5% faster on the dense fp32 backward; elsewhere the per-element
+        // form raised registers past an occupancy step (log-space adjoint 114
+        // -> 137 VGPRs, 11% slower; look-back backward 109 -> 138)
         const int64_t tf = REV ? T - 1 : 0, tl = REV ? 0 : T - 1;
         const int64_t q0 = u0 - lead;
-        const bool ends = EL < 8 || (tf >= q0 && tf < q0 + EL) || (BWD && tl >= q0 && tl < q0 + EL);
+        constexpr bool kEachElem = EL < 8 && !LOGB && MODE == kRowLoop;
+        const bool ends = kEachElem || (tf >= q0 && tf < q0 + EL) || (BWD && tl >= q0 && tl < q0 + EL);
         if (ends) {
 #pragma unroll
           for (int e = 0; e < EL; ++e) {

@@ -530,6 +530,27 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         }
       }
     }
+    // cm: bit s EL + ep marks element ep (physical order) of the lane's span
+    // in sub-chunk s. A lane's spans lie 64 EL apart, so one pass over the
+    // entries places each in its sub-chunk. (Differences of the low 32 bits
+    // stand for differences below 2^32 in size: a position before the spans
+    // wraps to a value far past them.)
+    uint32_t cm = 0;
+    if constexpr (VARLEN && !BWD) {
+      static_assert(SUBS * EL <= 32, "one bit per element of a lane's spans");
+      if (few) {
+        constexpr uint32_t kSpanStride = 64 * EL;
+        const uint32_t q00 = (uint32_t)(span_lo(0) - lead);
+#pragma unroll
+        for (int i = 0; i < kFewBounds; ++i) {
+          if (i < seg.n && fq[i] != 0xffffffffu) {
+            const uint32_t m = REV ? q00 + (uint32_t)(EL - 1) - fq[i] : fq[i] - q00;
+            const uint32_t sc = m / kSpanStride, e = m % kSpanStride;
+            if (sc < (uint32_t)SUBS && e < (uint32_t)EL) cm |= 1u << (sc * EL + (REV ? EL - 1 - e : e));
+          }
+        }
+      }
+    }
     uint32_t lastmask[BWD ? SUBS : 1];
 #pragma unroll
     for (int s = 0; s < SUBS; ++s) {
@@ -567,18 +588,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_scalar(const ScalarArgs a) {
         // Position q starts a sequence iff some entry equals q, and ends one
         // iff some entry equals q + 1 (the entries are sorted and the first is
         // at or before the tile's first element). The processing order's
-        // first element is the start (forward) or the end (reverse).
-        // (q - q0 lies in (-2^32 + EL, 2^32), so its low 32 bits are below EL
-        // exactly when q - q0 is)
+        // first element is the start (forward) or the end (reverse); cm holds
+        // the marks.
         const uint32_t q0 = (uint32_t)(u0 - lead);
-        uint32_t fm = 0;
-#pragma unroll
-        for (int i = 0; i < kFewBounds; ++i) {
-          if (i < seg.n && fq[i] != 0xffffffffu) {
-            const uint32_t d = fq[i] - q0;
-            if (d < (uint32_t)EL) fm |= 1u << d;
-          }
-        }
+        const uint32_t fm = (cm >> (s * EL)) & ((1u << EL) - 1u);
         if (fm) {
 #pragma unroll
           for (int ep = 0; ep < EL; ++ep) {

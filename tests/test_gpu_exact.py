@@ -200,6 +200,22 @@ def test_exact_one_wide_tile_rows(m, oracle_lib, dt, T):
 
 
 @pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("T", [4, 8, 64, 128, 256, 512, 1024])
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_exact_short_power_of_two_rows(m, oracle_lib, dt, T, with_h0):
+    """Short dense rows of 4 to 1024 elements stored back to back (37 rows),
+    both directions, gate values and logits, with and without h0, bit for
+    bit: every row is one tile of the short-row kernel."""
+    r = np.random.default_rng(4000 + DTYPES.index(dt) * 64 + T % 61 + with_h0)
+    rows = 37
+    for gated in (False, True):
+        g, x, dy = _exact_inputs(r, rows, T, gated)
+        h0 = r.integers(-1, 2, (1, rows)).astype(np.float32) if with_h0 else None
+        for rev in (False, True):
+            run_exact(m, oracle_lib, g, x, dy, h0, None, rev, dt, gated)
+
+
+@pytest.mark.parametrize("dt", DTYPES)
 @pytest.mark.parametrize("T", [200, 256, 1000, 1024, 2047, 2048])
 def test_exact_short_rows(m, oracle_lib, dt, T):
     """Rows that fit the 256-, 1024- and 2048-element one-per-row tiles."""

@@ -66,6 +66,12 @@ static hipError_t launch_scalar_gate(const ScalarArgs& a, int in_dtype, bool bwd
   if (in_dtype == 0) {
     if (bwd) return rev ? launch_cfg<LinOps, float, true, true, 4, 4, 1, false, GATE>(a, st)
                         : launch_cfg<LinOps, float, true, false, 4, 4, 1, false, GATE>(a, st);
+    // A forward row that fits one tile runs it as 8 waves of 2 sub-chunks
+    // (B=8 C=1536 T=4096: 98.0 -> 95.3 us); the backward (165.9 vs 168.6 us)
+    // and chained tiles (T = 65536 forward: 1.51 vs 1.59 ms) keep 4 x 4.
+    if (scalar_tiles(a.T, a.stride, 4, 4096) == 1)
+      return rev ? launch_cfg<LinOps, float, false, true, 8, 2, 1, false, GATE>(a, st)
+                 : launch_cfg<LinOps, float, false, false, 8, 2, 1, false, GATE>(a, st);
     return rev ? launch_cfg<LinOps, float, false, true, 4, 4, 1, false, GATE>(a, st)
                : launch_cfg<LinOps, float, false, false, 4, 4, 1, false, GATE>(a, st);
   }

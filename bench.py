@@ -144,8 +144,8 @@ def ceiling(m, torch, dev, proto, nsrc, ndst, n_floats):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no communication; see the design notes). Use --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(rows would shard across GPUs with no communication). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -297,7 +297,7 @@ constexpr size_t kMcPubBytes = 256 * 8;  // one published h_out
 
 __device__ __forceinline__ void mc_publish(uint64_t* w, v4f v) {
   stress_pause(3);
-  uint64_t* p = w + threadIdx.x;
+  uint64_t* p = w + (threadIdx.x & 63);
   st_u64(p + 0 * 64, pack_word(kMcTag, v.x));
   st_u64(p + 1 * 64, pack_word(kMcTag, v.y));
   st_u64(p + 2 * 64, pack_word(kMcTag, v.z));
@@ -306,7 +306,7 @@ __device__ __forceinline__ void mc_publish(uint64_t* w, v4f v) {
 // h_out of a chunk once every lane sees all four of its words published;
 // false after `limit` polls (then the header's error word is set)
 __device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, uint32_t limit, v4f& v) {
-  const uint64_t* p = w + threadIdx.x;
+  const uint64_t* p = w + (threadIdx.x & 63);
   for (uint32_t spins = 0;; ++spins) {
     const uint64_t a = ld_u64(p + 0 * 64), b = ld_u64(p + 1 * 64), c = ld_u64(p + 2 * 64), d = ld_u64(p + 3 * 64);
     const bool ok = word_tag(a) == kMcTag && word_tag(b) == kMcTag && word_tag(c) == kMcTag &&
@@ -316,24 +316,37 @@ __device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, uint32
       return true;
     }
     if (spins > limit) {
-      if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
+      if ((threadIdx.x & 63) == 0) st_u32(hdr + kHdrError, 1u);  // lane 0 of the waiting wave
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
   }
 }
 
-// Tile16 only: a wave owns S steps of one row.
-template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
-__global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
+// Tile16 only: a workgroup of WG waves owns a chunk of WG S consecutive steps
+// of one row, wave w the steps w S .. w S + S - 1 of it. With WG > 1 the waves
+// pass their summaries through LDS: wave w composes the summaries of waves
+// 0 .. w-1 in that fixed order (its carry-in as a map of the chunk's
+// carry-in), the last wave also its own (the chunk's summary), so rounding
+// stays the same from call to call. The last wave waits for the chunk before,
+// publishes h_out and hands the carry-in to the others. Several waves per
+// chunk keep a CU's waves on one contiguous stretch of a row: as timing-only
+// copies with the 16 x 16 forward's loads and stores (512 rows x T = 4096),
+// one wave per 32-step chunk took 1.18 ms, two or four waves of 32 steps
+// 1.05 ms; the kernels' own timings are with the chunk sizes below.
+template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S, int WG>
+__global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
   static_assert(S <= 32, "step masks are 32-bit");
-  __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
+  static_assert(WG >= 1 && WG <= 8, "waves per chunk");
+  __shared__ __attribute__((aligned(16))) float s_tw[WG][16 * 20];  // transpose tile per wave
+  const int w = WG > 1 ? (int)(threadIdx.x >> 6) : 0;
+  float* const s_t = s_tw[w];
   int64_t r;
   int c;
   tile_of_block<true>(a.rows, a.ntiles, a.blk0, r, c);
   McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
-  const int64_t j0 = (int64_t)c * S;
-  const int n = (int)min((int64_t)S, a.T - j0);
+  const int64_t j0 = ((int64_t)c * WG + w) * S;
+  const int n = (int)max((int64_t)0, min((int64_t)S, a.T - j0));  // 0: a wave past the row's end
 
   // sequence starts and ends in the chunk (before the loads: nothing is live yet)
   uint32_t firstm, lastm;
@@ -413,17 +426,77 @@ __global__ __launch_bounds__(64) void k_mc_scan(const MatArgs a) {
   uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
   const int64_t me = r * a.ntiles + c;
   const bool publish = c + 1 < a.ntiles;
-  if (publish && hard) mc_publish(pub + me * 256, Q);  // h_out = Q whatever the carry-in
-  const v4f PR = (publish && !hard) ? TL::d_to_r(s_t, P) : mc_zero();  // off the chain
-  v4f hin = mc_zero();
-  if (!first0) {
-    // a wait that gave up leaves NaN, never a plausible wrong carry
-    if (!mc_wait(pub + (me - 1) * 256, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
+  v4f h;  // this wave's carry-in
+  if constexpr (WG == 1) {
+    if (publish && hard) mc_publish(pub + me * 256, Q);  // h_out = Q whatever the carry-in
+    const v4f PR = (publish && !hard) ? TL::d_to_r(s_t, P) : mc_zero();  // off the chain
+    v4f hin = mc_zero();
+    if (!first0) {
+      // a wait that gave up leaves NaN, never a plausible wrong carry
+      if (!mc_wait(pub + (me - 1) * 256, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
+    }
+    if (publish && !hard) mc_publish(pub + me * 256, TL::mm(PR, hin, Q));
+    h = hin;
+  } else {
+    // wave summaries F_u = (P_u, Q_u): P_u in D and R layout, Q_u in D layout
+    __shared__ v4f s_PD[WG][64], s_PR[WG][64], s_Q[WG][64], s_hin[64];
+    __shared__ uint32_t s_hard[WG];
+    const int lane = (int)(threadIdx.x & 63);
+    s_PD[w][lane] = P;
+    s_PR[w][lane] = TL::d_to_r(s_t, P);
+    s_Q[w][lane] = Q;
+    if (lane == 0) s_hard[w] = (uint32_t)hard | ((uint32_t)first0 << 1);
+    __syncthreads();
+    // G = F_{w-1} o ... o F_0, the map from the chunk's carry-in to this
+    // wave's: `have` once a summary is taken, hardG once one of them is hard
+    // (then G no longer depends on the carry-in: PG = 0)
+    v4f PG = mc_zero(), QG = mc_zero();
+    bool have = false, hardG = false;
+    for (int u = 0; u < w; ++u) {
+      const uint32_t hu = s_hard[u];
+      const v4f Qu = s_Q[u][lane];
+      if (hu & 1u) {
+        PG = mc_zero();
+        QG = Qu;
+        hardG = true;
+      } else if (!have) {
+        PG = s_PD[u][lane];
+        QG = Qu;
+      } else {
+        const v4f PuR = s_PR[u][lane];
+        if (!hardG) PG = TL::mm(PuR, PG, mc_zero());
+        QG = TL::mm(PuR, QG, Qu);
+      }
+      have = true;
+    }
+    // the chunk's carry-in is needed unless its first step is hard
+    const bool need_in = (s_hard[0] & 2u) == 0u;
+    const v4f PGR = (have && !hardG) ? TL::d_to_r(s_t, PG) : mc_zero();  // off the chain
+    if (w == WG - 1) {
+      // chunk summary F_w o G, published at once when it is hard
+      v4f PC = P, QC = Q;
+      const bool hardC = hard || hardG;
+      if (!hard && have) {
+        const v4f PwR = s_PR[w][lane];
+        PC = hardG ? mc_zero() : TL::mm(PwR, PG, mc_zero());
+        QC = TL::mm(PwR, QG, Q);
+      }
+      if (publish && hardC) mc_publish(pub + me * 256, QC);
+      const v4f PCR = (publish && !hardC) ? TL::d_to_r(s_t, PC) : mc_zero();  // off the chain
+      v4f hin = mc_zero();
+      if (need_in) {
+        // a wait that gave up leaves NaN, never a plausible wrong carry
+        if (!mc_wait(pub + (me - 1) * 256, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
+      }
+      if (publish && !hardC) mc_publish(pub + me * 256, TL::mm(PCR, hin, QC));
+      s_hin[lane] = hin;
+    }
+    __syncthreads();
+    const v4f hin = s_hin[lane];
+    h = !have ? hin : hardG ? QG : TL::mm(PGR, hin, QG);
   }
-  if (publish && !hard) mc_publish(pub + me * 256, TL::mm(PR, hin, Q));
 
   // ---- apply from the registers
-  v4f h = hin;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const bool first = (hardm >> s) & 1u;
@@ -693,11 +766,15 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
 // ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
-// Steps per chunk, from timing 8 / 16 / 32 at (16, 16), 512 rows, T = 4096:
-// the forward is fastest with 32 (half the chained hops and published words
-// of 16, despite one wave per SIMD), the backward ties at 16 and 32 and takes
-// 16 (32 spills).
-constexpr int kChunkFwd = 32, kChunkBwd = 16;
+// Steps per wave (kChunk) and waves per chunk (kWaves; a chunk is kWaves x
+// kChunk steps), from timing at (16, 16), 512 rows, T = 4096, flushed.
+// Forward, waves x steps: 1 x 32 1.24 ms (one wave per SIMD), 2 x 32 1.35,
+// 4 x 32 1.54, 2 x 16 1.19, 4 x 8 1.19, 4 x 12 1.21, 8 x 8 1.11, 8 x 16 1.42,
+// 4 x 16 1.09-1.11 (two waves per SIMD, a 64-step chunk). Backward: 1 x 16
+// 2.24 ms, 2 x 16 2.21, 4 x 16 2.60, 4 x 8 3.62, 8 x 8 2.72 (32 steps per wave
+// spill).
+constexpr int kChunkFwd = 16, kChunkBwd = 16;
+constexpr int kWavesFwd = 4, kWavesBwd = 2;
 // Steps per lane group of the 4 x 4 row-segment kernel (a wave spans 16 x that),
 // from timing 4 / 8 / 16 / 24 / 32 at (4, 4), 4096 rows x T = 8192: 16 and 32
 // tie (forward 1.27 ms, backward 2.19 ms; 8 took 1.37 / 2.46 ms) and 32 spills
@@ -707,7 +784,7 @@ constexpr int kSegSteps = 16;
 static bool tile4_shape(int k, int v) { return k <= 4 && v <= 4; }
 
 int64_t matrix_core_chunks(int64_t T, bool bwd, int k, int v) {
-  const int64_t S = tile4_shape(k, v) ? 16 * kSegSteps : (bwd ? kChunkBwd : kChunkFwd);
+  const int64_t S = tile4_shape(k, v) ? 16 * kSegSteps : (bwd ? kWavesBwd * kChunkBwd : kWavesFwd * kChunkFwd);
   return (T + S - 1) / S;
 }
 
@@ -716,16 +793,16 @@ size_t matrix_core_ws_bytes(int64_t rows, int64_t T, int k, int v) {
   return ws_desc_offset() + (size_t)(rows * n) * (tile4_shape(k, v) ? kSegPubBytes : kMcPubBytes);
 }
 
-template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+template <class TL, bool FULL, bool BWD, bool REV, bool VARLEN, int S, int WG>
 static hipError_t launch_mc_dir(const MatArgs& a0, hipStream_t st) {
   MatArgs a = a0;
-  a.ntiles = (int32_t)((a.T + S - 1) / S);
+  a.ntiles = (int32_t)((a.T + WG * S - 1) / (WG * S));
   const int64_t n = a.rows * a.ntiles;
   // fresh words (and header) for this call: a zero tag = not published
   const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kMcPubBytes, st);
   if (z != hipSuccess) return z;
-  hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S>), dim3(launch_blocks((uint64_t)n, a.nblk)), dim3(64), 0,
-                     st, a);
+  hipLaunchKernelGGL((k_mc_scan<TL, FULL, BWD, REV, VARLEN, S, WG>), dim3(launch_blocks((uint64_t)n, a.nblk)),
+                     dim3(64 * WG), 0, st, a);
   return hipGetLastError();
 }
 
@@ -743,14 +820,14 @@ static hipError_t launch_seg_dir(const MatArgs& a0, hipStream_t st) {
 
 template <class TL, bool FULL>
 static hipError_t launch_mc_shape(const MatArgs& a, bool bwd, hipStream_t st) {
-  constexpr int SF = kChunkFwd, SB = kChunkBwd;
+  constexpr int SF = kChunkFwd, SB = kChunkBwd, WF = kWavesFwd, WB = kWavesBwd;
   const bool rev = a.rev != 0, vl = a.cu != nullptr;
   if (bwd) {
-    if (rev) return vl ? launch_mc_dir<TL, FULL, true, true, true, SB>(a, st) : launch_mc_dir<TL, FULL, true, true, false, SB>(a, st);
-    return vl ? launch_mc_dir<TL, FULL, true, false, true, SB>(a, st) : launch_mc_dir<TL, FULL, true, false, false, SB>(a, st);
+    if (rev) return vl ? launch_mc_dir<TL, FULL, true, true, true, SB, WB>(a, st) : launch_mc_dir<TL, FULL, true, true, false, SB, WB>(a, st);
+    return vl ? launch_mc_dir<TL, FULL, true, false, true, SB, WB>(a, st) : launch_mc_dir<TL, FULL, true, false, false, SB, WB>(a, st);
   }
-  if (rev) return vl ? launch_mc_dir<TL, FULL, false, true, true, SF>(a, st) : launch_mc_dir<TL, FULL, false, true, false, SF>(a, st);
-  return vl ? launch_mc_dir<TL, FULL, false, false, true, SF>(a, st) : launch_mc_dir<TL, FULL, false, false, false, SF>(a, st);
+  if (rev) return vl ? launch_mc_dir<TL, FULL, false, true, true, SF, WF>(a, st) : launch_mc_dir<TL, FULL, false, true, false, SF, WF>(a, st);
+  return vl ? launch_mc_dir<TL, FULL, false, false, true, SF, WF>(a, st) : launch_mc_dir<TL, FULL, false, false, false, SF, WF>(a, st);
 }
 
 template <bool FULL>

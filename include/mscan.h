@@ -212,12 +212,12 @@ MSCAN_API mscan_status scan_log_bwd_gated(const mscan_problem* prob, int gate /*
  * k=2, v=1 and matrix_affine_scan is generic (k, v)). Supported: the page's
  * kernel envelope, k and v each in {1, 2, 4, 8, 16}, any T >= 1; any other
  * (k, v) returns MSCAN_ERR_UNSUPPORTED. (1, 1) is the scalar scan; (2,1),
- * (2,2), (4,1) and (4,4) run on the vector ALUs; every other pair runs its
- * products on the matrix cores, zero-padded to 4 x 4 (k, v <= 4) or 16 x 16,
- * with fp32 operands and fp32 accumulation (the page's precision guard at
- * k = 16), and always needs the workspace (mscan_workspace_bytes: 2 KiB per
- * chunk of 16 or 32 steps and row, or per 16 rows when k, v <= 4). Its
- * results are bit-reproducible from call to call.
+ * (2,2) and (4,1) run on the vector ALUs; every other pair, (4,4) included,
+ * runs its products on the matrix cores, zero-padded to 4 x 4 (k, v <= 4) or
+ * 16 x 16, with fp32 operands and fp32 accumulation (the page's precision
+ * guard at k = 16), and always needs the workspace (mscan_workspace_bytes:
+ * per row, 2 KiB per chunk of 32 steps, or 128 bytes per chunk of 256 steps
+ * when k, v <= 4). Its results are bit-reproducible from call to call.
  *   A : fp32 [rows][T][k][k]; B : fp32 [rows][T][k][v];
  *   h0 : fp32 [nseg][rows][k][v] or NULL; h : fp32 [rows][T][k][v], written. */
 MSCAN_API mscan_status matrix_affine_scan_fwd(const mscan_problem* prob, int k, int v, const float* A,

@@ -173,10 +173,10 @@ def test_matrix_core_workspace_always_required(m):
     # The matrix-core shapes chain their chunks through the workspace on every
     # call: header (128), then per chunk and row the published state after it
     # as tagged 8-byte words, sized for the larger chunk count. k or v above 4:
-    # chunks of 32 (forward) / 16 (backward) steps, a padded 16 x 16 state (256
+    # chunks of 64 (forward) / 32 (backward) steps, a padded 16 x 16 state (256
     # words); k, v <= 4: spans of 16 x 16 steps, a padded 4 x 4 state (16 words).
     p = _prob(m, rows=5, T=100)
-    need16 = 128 + 5 * 7 * 256 * 8
+    need16 = 128 + 5 * 4 * 256 * 8
     for k, v in ((16, 16), (8, 8), (1, 16), (16, 1), (4, 8)):
         assert m.workspace_bytes(p, m.OP_MATRIX_FWD, k, v) == need16
         assert m.workspace_bytes(p, m.OP_MATRIX_BWD, k, v) == need16

@@ -35,9 +35,10 @@
 // next step's operand without moving data between lanes; the R layout of X is
 // the D layout of X^T.
 //
-// One kernel per call, carries chained from wave to wave through the
+// One kernel per call, carries chained from chunk to chunk through the
 // workspace: k_mc_scan (Tile16) gives a wave S steps of one row; k_mc_rowseg
-// (Tile4) gives a wave 16 S steps of one row, S per group of 4 lanes.
+// (Tile4) gives a wave 16 S steps of one row, S per group of 4 lanes; a chunk
+// is the consecutive spans of the waves of one workgroup.
 // Forward element (X, Y) = (A_t, B_t); backward element = (A of the previous
 // step in processing order, transposed; dy_t). A sequence's first step in
 // processing order is hard: forward h = A h0 + B, backward lam = dy. So is a
@@ -93,7 +94,7 @@ struct Tile16 {
 
 struct Tile4 {
   static constexpr int E = 4;
-  __device__ static __forceinline__ int lrow() { return (int)(threadIdx.x >> 2); }  // lane group (block)
+  __device__ static __forceinline__ int lrow() { return (int)((threadIdx.x >> 2) & 15); }  // lane group (block)
   // this lane group's block is all zero (uniform across the group)
   __device__ static __forceinline__ bool zero(v4f x) {
     return ((__ballot(mc_nonzero(x)) >> (4 * lrow())) & 0xfull) == 0ull;
@@ -578,7 +579,7 @@ __device__ __forceinline__ bool seg_wait(const uint64_t* w, uint32_t* hdr, uint3
       return true;
     }
     if (spins > limit) {
-      if (threadIdx.x == 0) st_u32(hdr + kHdrError, 1u);
+      if ((threadIdx.x & 63) == 0) st_u32(hdr + kHdrError, 1u);  // lane 0 of the waiting wave
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -600,19 +601,30 @@ __device__ __forceinline__ v4f sel4(bool c, v4f a, v4f b) {
 // order, so the order, not the chain, sets the pace; whole rows back to back
 // (row-major) would stream faster still (copy 1.21 ms) but serialise the
 // carry chain (2.09 ms), and 16-chunk groups were slower (1.46 ms).
-constexpr int kSegGroup = 8;
+// The forward's chunks are 4 waves long (4 x 256 steps per workgroup) and run
+// in groups of 2 (forward 1.26 -> 1.21 ms; waves x group: 1 x 8 1.26 ms,
+// 2 x 8 1.32, 2 x 4 1.25, 2 x 2 1.24, 4 x 8 1.33, 4 x 4 1.26, 4 x 1 1.22,
+// 8 x 1 1.44); the backward keeps one wave per chunk (2 waves: 2.18 -> 2.45 ms).
+constexpr int kSegGroupFwd = 2, kSegGroupBwd = 8;
 
-template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
-__global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
+// A workgroup of WG waves owns WG consecutive wave spans of the row; with
+// WG > 1 the waves combine their spans' summaries through LDS as k_mc_scan's
+// do, and only the last one waits for the chunk before and publishes.
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S, int WG>
+__global__ __launch_bounds__(64 * WG) void k_mc_rowseg(const MatArgs a) {
   static_assert(S <= 32, "step masks are 32-bit");
+  static_assert(WG >= 1 && WG <= 8, "waves per chunk");
   using TL = Tile4;
-  __shared__ __attribute__((aligned(16))) float s_t[16 * 20];  // transpose tile
+  __shared__ __attribute__((aligned(16))) float s_tw[WG][16 * 20];  // transpose tile per wave
+  const int w = WG > 1 ? (int)(threadIdx.x >> 6) : 0;
+  float* const s_t = s_tw[w];
   int64_t r;
   int c;
-  tile_of_block_grouped(a.rows, a.ntiles, a.blk0, kSegGroup, r, c);
+  tile_of_block_grouped(a.rows, a.ntiles, a.blk0, BWD ? kSegGroupBwd : kSegGroupFwd, r, c);
   McWalk<TL, FULL, BWD, REV, VARLEN> wk(a, r);
   const int b = TL::lrow();
-  const int64_t jb = (int64_t)c * (16 * S) + (int64_t)b * S;  // this group's first processing step
+  // this group's first processing step
+  const int64_t jb = ((int64_t)c * WG + w) * (16 * S) + (int64_t)b * S;
   const int nb = (int)max((int64_t)0, min((int64_t)S, a.T - jb));
 
   uint32_t firstm, lastm;  // per group
@@ -703,21 +715,78 @@ __global__ __launch_bounds__(64) void k_mc_rowseg(const MatArgs a) {
   const bool whard = __shfl((int)hard, 60, 64) != 0;
   const bool first0 = __shfl((int)(hardm & 1u), 0, 64) != 0;
 
-  // ---- carry-in from the wave before, h_out for the wave after
+  // ---- carry-in from the chunk before, h_out for the chunk after
   uint32_t* hdr = (uint32_t*)a.ws;
   uint64_t* pub = (uint64_t*)((char*)a.ws + ws_desc_offset());
   const int64_t me = r * a.ntiles + c;
   const bool publish = c + 1 < a.ntiles;
-  if (publish && whard && b == 15) seg_publish(pub + me * 16, Q);  // group 15's Q is the wave's h_out
   const v4f PR = TL::d_to_r(s_t, P);
-  v4f hin = mc_zero();
-  if (!first0) {
-    if (!seg_wait(pub + (me - 1) * 16, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
+  v4f hin = mc_zero();  // the wave's carry-in, in every group
+  v4f out;              // out_b = state after group b
+  if constexpr (WG == 1) {
+    if (publish && whard && b == 15) seg_publish(pub + me * 16, Q);  // group 15's Q is the wave's h_out
+    if (!first0) {
+      if (!seg_wait(pub + (me - 1) * 16, hdr, spin_limit(a.spin), hin)) hin = mc_nan();
+    }
+    out = sel4(hard, Q, TL::mm(PR, hin, Q));
+    if (publish && !whard && b == 15) seg_publish(pub + me * 16, out);
+  } else {
+    // wave summaries F_u = group 15's inclusive (P, Q), copied to every group
+    __shared__ v4f s_PD[WG][4], s_PR[WG][4], s_Q[WG][4], s_hin[4];
+    __shared__ uint32_t s_fl[WG];
+    const int q = (int)(threadIdx.x & 3);
+    if (b == 15) {
+      s_PD[w][q] = P;
+      s_PR[w][q] = PR;
+      s_Q[w][q] = Q;
+    }
+    if ((threadIdx.x & 63) == 0) s_fl[w] = (uint32_t)whard | ((uint32_t)first0 << 1);
+    __syncthreads();
+    // G = F_{w-1} o ... o F_0 in that order (PG = 0 once one of them is hard)
+    v4f PG = mc_zero(), QG = mc_zero();
+    bool have = false, hardG = false;
+    for (int u = 0; u < w; ++u) {
+      const v4f Qu = s_Q[u][q];
+      if (s_fl[u] & 1u) {
+        PG = mc_zero();
+        QG = Qu;
+        hardG = true;
+      } else if (!have) {
+        PG = s_PD[u][q];
+        QG = Qu;
+      } else {
+        const v4f PuR = s_PR[u][q];
+        if (!hardG) PG = TL::mm(PuR, PG, mc_zero());
+        QG = TL::mm(PuR, QG, Qu);
+      }
+      have = true;
+    }
+    const bool need_in = (s_fl[0] & 2u) == 0u;  // unless the chunk's first step is hard
+    const v4f PGR = (have && !hardG) ? TL::d_to_r(s_t, PG) : mc_zero();  // off the chain
+    if (w == WG - 1) {
+      // chunk summary F_w o G, published at once when it is hard
+      v4f PC = s_PD[w][q], QC = s_Q[w][q];
+      const bool hardC = whard || hardG;
+      if (!whard && have) {
+        const v4f PwR = s_PR[w][q];
+        PC = hardG ? mc_zero() : TL::mm(PwR, PG, mc_zero());
+        QC = TL::mm(PwR, QG, QC);
+      }
+      if (publish && hardC && b == 15) seg_publish(pub + me * 16, QC);
+      const v4f PCR = (publish && !hardC) ? TL::d_to_r(s_t, PC) : mc_zero();  // off the chain
+      v4f hc = mc_zero();
+      if (need_in) {
+        if (!seg_wait(pub + (me - 1) * 16, hdr, spin_limit(a.spin), hc)) hc = mc_nan();
+      }
+      const v4f hout = TL::mm(PCR, hc, QC);
+      if (publish && !hardC && b == 15) seg_publish(pub + me * 16, hout);
+      if ((threadIdx.x & 63) < 4) s_hin[q] = hc;
+    }
+    __syncthreads();
+    const v4f hc = s_hin[q];
+    if (w > 0 || need_in) hin = !have ? hc : hardG ? QG : TL::mm(PGR, hc, QG);
+    out = sel4(hard, Q, TL::mm(PR, hin, Q));
   }
-  // out_b = state after group b
-  v4f out = TL::mm(PR, hin, Q);
-  out = sel4(hard, Q, out);
-  if (publish && !whard && b == 15) seg_publish(pub + me * 16, out);
   v4f h = shfl_up4(out, 4);
   if (b == 0) h = hin;
 
@@ -780,11 +849,15 @@ constexpr int kWavesFwd = 4, kWavesBwd = 2;
 // tie (forward 1.27 ms, backward 2.19 ms; 8 took 1.37 / 2.46 ms) and 32 spills
 // in the backward.
 constexpr int kSegSteps = 16;
+// Waves per chunk of the row-segment kernel (a chunk is kSegWaves x 16 x
+// kSegSteps steps).
+constexpr int kSegWavesFwd = 4, kSegWavesBwd = 1;
 
 static bool tile4_shape(int k, int v) { return k <= 4 && v <= 4; }
 
 int64_t matrix_core_chunks(int64_t T, bool bwd, int k, int v) {
-  const int64_t S = tile4_shape(k, v) ? 16 * kSegSteps : (bwd ? kWavesBwd * kChunkBwd : kWavesFwd * kChunkFwd);
+  const int64_t S = tile4_shape(k, v) ? (bwd ? kSegWavesBwd : kSegWavesFwd) * 16 * kSegSteps
+                                      : (bwd ? kWavesBwd * kChunkBwd : kWavesFwd * kChunkFwd);
   return (T + S - 1) / S;
 }
 
@@ -806,15 +879,15 @@ static hipError_t launch_mc_dir(const MatArgs& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool FULL, bool BWD, bool REV, bool VARLEN, int S>
+template <bool FULL, bool BWD, bool REV, bool VARLEN, int S, int WG>
 static hipError_t launch_seg_dir(const MatArgs& a0, hipStream_t st) {
   MatArgs a = a0;
-  a.ntiles = (int32_t)((a.T + 16 * S - 1) / (16 * S));
+  a.ntiles = (int32_t)((a.T + WG * 16 * S - 1) / (WG * 16 * S));
   const int64_t n = a.rows * a.ntiles;
   const hipError_t z = launch_zero(a.ws, ws_desc_offset() + (size_t)n * kSegPubBytes, st);
   if (z != hipSuccess) return z;
-  hipLaunchKernelGGL((k_mc_rowseg<FULL, BWD, REV, VARLEN, S>), dim3(launch_blocks((uint64_t)n, a.nblk)), dim3(64), 0,
-                     st, a);
+  hipLaunchKernelGGL((k_mc_rowseg<FULL, BWD, REV, VARLEN, S, WG>), dim3(launch_blocks((uint64_t)n, a.nblk)),
+                     dim3(64 * WG), 0, st, a);
   return hipGetLastError();
 }
 
@@ -832,14 +905,14 @@ static hipError_t launch_mc_shape(const MatArgs& a, bool bwd, hipStream_t st) {
 
 template <bool FULL>
 static hipError_t launch_seg_shape(const MatArgs& a, bool bwd, hipStream_t st) {
-  constexpr int S = kSegSteps;
+  constexpr int S = kSegSteps, WF = kSegWavesFwd, WB = kSegWavesBwd;
   const bool rev = a.rev != 0, vl = a.cu != nullptr;
   if (bwd) {
-    if (rev) return vl ? launch_seg_dir<FULL, true, true, true, S>(a, st) : launch_seg_dir<FULL, true, true, false, S>(a, st);
-    return vl ? launch_seg_dir<FULL, true, false, true, S>(a, st) : launch_seg_dir<FULL, true, false, false, S>(a, st);
+    if (rev) return vl ? launch_seg_dir<FULL, true, true, true, S, WB>(a, st) : launch_seg_dir<FULL, true, true, false, S, WB>(a, st);
+    return vl ? launch_seg_dir<FULL, true, false, true, S, WB>(a, st) : launch_seg_dir<FULL, true, false, false, S, WB>(a, st);
   }
-  if (rev) return vl ? launch_seg_dir<FULL, false, true, true, S>(a, st) : launch_seg_dir<FULL, false, true, false, S>(a, st);
-  return vl ? launch_seg_dir<FULL, false, false, true, S>(a, st) : launch_seg_dir<FULL, false, false, false, S>(a, st);
+  if (rev) return vl ? launch_seg_dir<FULL, false, true, true, S, WF>(a, st) : launch_seg_dir<FULL, false, true, false, S, WF>(a, st);
+  return vl ? launch_seg_dir<FULL, false, false, true, S, WF>(a, st) : launch_seg_dir<FULL, false, false, false, S, WF>(a, st);
 }
 
 hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st) {

@@ -43,9 +43,9 @@ def _case(r, k, v, rows, T):
 
 # (k, v, T, first step of the last row's last tile): the scalar scan (3 tiles
 # of 4096), the 2x1 VALU kernel (3 tiles of 2048 steps), the 4x4 matrix-core
-# row segments (3 chunks of 256 steps), the 16x16 and 8x2 matrix-core forward
-# chunks (4 chunks of 64 steps)
-CASES = [(1, 1, 3 * 4096, 8192), (2, 1, 5000, 4096), (4, 4, 600, 512), (16, 16, 200, 192), (8, 2, 200, 192)]
+# row-segment forward (3 chunks of 1024 steps), the 16x16 and 8x2 matrix-core
+# forward chunks (4 chunks of 64 steps)
+CASES = [(1, 1, 3 * 4096, 8192), (2, 1, 5000, 4096), (4, 4, 2500, 2048), (16, 16, 200, 192), (8, 2, 200, 192)]
 
 
 @pytest.mark.parametrize("k,v,T,last", CASES)

@@ -513,8 +513,11 @@ __global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
           // both leave as rows, one 16-byte store per lane each: dB = lam from
           // its R layout, and dA from h_prev lam^T = dA^T, whose D layout is
           // the R layout of dA (16 x 16, 512 rows x T = 4096: 2.29 -> 2.23 ms)
-          *(v4f*)(wk.blkB(a.out0, t) + TL::dc() * 16 + TL::dr0()) = lamR;
-          *(v4f*)(wk.blkA(a.out1, t) + TL::dc() * 16 + TL::dr0()) = TL::mm(H[s], lamR, mc_zero());
+          // (nontemporal: 2.22 -> 2.18 ms at 2 waves x 16 steps; A and dy read
+          // as rows instead, with two more LDS transposes per step, 2.9-3.1 ms)
+          __builtin_nontemporal_store(lamR, (v4f*)(wk.blkB(a.out0, t) + TL::dc() * 16 + TL::dr0()));
+          __builtin_nontemporal_store(TL::mm(H[s], lamR, mc_zero()),
+                                      (v4f*)(wk.blkA(a.out1, t) + TL::dc() * 16 + TL::dr0()));
         } else {
           wk.sh.stB_D(wk.blkB(a.out0, t), h);  // dB = lam
           wk.sh.stA_D(wk.blkA(a.out1, t), TL::mm(lamR, H[s], mc_zero()));
@@ -531,9 +534,7 @@ __global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
     } else if constexpr (FULL) {
       // h leaves as rows: one 16-byte store per lane (16 x 16 forward, 512 rows
       // x T = 4096 after a 1 GiB fill, with the row loads above: 1.35 -> 1.22
-      // ms). Nontemporal here; in the backward nontemporal row stores were 9%
-      // slower than plain ones, and row loads of its D-layout operands (two
-      // more LDS transposes per step at one wave per SIMD) 40% slower.
+      // ms), nontemporal like the backward's.
       const v4f hR = TL::d_to_r(s_t, h);
       if (s < n) __builtin_nontemporal_store(hR, (v4f*)(wk.blkB(a.out0, wk.phys(j0 + s)) + TL::dc() * 16 + TL::dr0()));
     } else {

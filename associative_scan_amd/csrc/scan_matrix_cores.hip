@@ -848,8 +848,10 @@ constexpr int kWavesFwd = 4, kWavesBwd = 2;
 // Steps per lane group of the 4 x 4 row-segment kernel (a wave spans 16 x that),
 // from timing 4 / 8 / 16 / 24 / 32 at (4, 4), 4096 rows x T = 8192: 16 and 32
 // tie (forward 1.27 ms, backward 2.19 ms; 8 took 1.37 / 2.46 ms) and 32 spills
-// in the backward.
-constexpr int kSegSteps = 16;
+// in the backward. A backward of 8 steps per group at two waves per SIMD, 2 or
+// 4 waves per chunk, chunks in groups of 2 to 8, took 2.30-2.38 ms against
+// 2.17 ms.
+constexpr int kSegStepsFwd = 16, kSegStepsBwd = 16;
 // Waves per chunk of the row-segment kernel (a chunk is kSegWaves x 16 x
 // kSegSteps steps).
 constexpr int kSegWavesFwd = 4, kSegWavesBwd = 1;
@@ -857,7 +859,7 @@ constexpr int kSegWavesFwd = 4, kSegWavesBwd = 1;
 static bool tile4_shape(int k, int v) { return k <= 4 && v <= 4; }
 
 int64_t matrix_core_chunks(int64_t T, bool bwd, int k, int v) {
-  const int64_t S = tile4_shape(k, v) ? (bwd ? kSegWavesBwd : kSegWavesFwd) * 16 * kSegSteps
+  const int64_t S = tile4_shape(k, v) ? (bwd ? kSegWavesBwd * 16 * kSegStepsBwd : kSegWavesFwd * 16 * kSegStepsFwd)
                                       : (bwd ? kWavesBwd * kChunkBwd : kWavesFwd * kChunkFwd);
   return (T + S - 1) / S;
 }
@@ -906,14 +908,14 @@ static hipError_t launch_mc_shape(const MatArgs& a, bool bwd, hipStream_t st) {
 
 template <bool FULL>
 static hipError_t launch_seg_shape(const MatArgs& a, bool bwd, hipStream_t st) {
-  constexpr int S = kSegSteps, WF = kSegWavesFwd, WB = kSegWavesBwd;
+  constexpr int SF = kSegStepsFwd, SB = kSegStepsBwd, WF = kSegWavesFwd, WB = kSegWavesBwd;
   const bool rev = a.rev != 0, vl = a.cu != nullptr;
   if (bwd) {
-    if (rev) return vl ? launch_seg_dir<FULL, true, true, true, S, WB>(a, st) : launch_seg_dir<FULL, true, true, false, S, WB>(a, st);
-    return vl ? launch_seg_dir<FULL, true, false, true, S, WB>(a, st) : launch_seg_dir<FULL, true, false, false, S, WB>(a, st);
+    if (rev) return vl ? launch_seg_dir<FULL, true, true, true, SB, WB>(a, st) : launch_seg_dir<FULL, true, true, false, SB, WB>(a, st);
+    return vl ? launch_seg_dir<FULL, true, false, true, SB, WB>(a, st) : launch_seg_dir<FULL, true, false, false, SB, WB>(a, st);
   }
-  if (rev) return vl ? launch_seg_dir<FULL, false, true, true, S, WF>(a, st) : launch_seg_dir<FULL, false, true, false, S, WF>(a, st);
-  return vl ? launch_seg_dir<FULL, false, false, true, S, WF>(a, st) : launch_seg_dir<FULL, false, false, false, S, WF>(a, st);
+  if (rev) return vl ? launch_seg_dir<FULL, false, true, true, SF, WF>(a, st) : launch_seg_dir<FULL, false, true, false, SF, WF>(a, st);
+  return vl ? launch_seg_dir<FULL, false, false, true, SF, WF>(a, st) : launch_seg_dir<FULL, false, false, false, SF, WF>(a, st);
 }
 
 hipError_t launch_matrix_core(const MatArgs& a, bool bwd, hipStream_t st) {

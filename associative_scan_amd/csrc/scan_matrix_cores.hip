@@ -324,6 +324,23 @@ __device__ __forceinline__ bool mc_wait(const uint64_t* w, uint32_t* hdr, uint32
   }
 }
 
+// A 16 x 16 block staged in LDS by one direct 16-byte load per lane: lane l
+// takes 16-byte unit swz(l) of the block (unit 4 row + col / 4) into LDS slot
+// l. The swizzle spreads the four row groups of a column-wise read (rows
+// 4q .. 4q+3, q = 0..3) over different banks; it is its own inverse.
+__device__ __forceinline__ int mc_swz(int u) { return u ^ (((u >> 4) & 3) << 2); }
+__device__ __forceinline__ void mc_stage(const float* blk, float* lds) {
+  __builtin_amdgcn_global_load_lds((const void*)(blk + mc_swz((int)(threadIdx.x & 63)) * 4),
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, kLdsNT);
+}
+// the staged block in D layout: register i = X[dr0 + i][dc]
+__device__ __forceinline__ v4f mc_unstage(const float* lds) {
+  const int r0 = Tile16::dr0(), c = Tile16::dc();
+  const int o = c & 3, u = c >> 2;
+  return v4f{lds[mc_swz((r0 + 0) * 4 + u) * 4 + o], lds[mc_swz((r0 + 1) * 4 + u) * 4 + o],
+             lds[mc_swz((r0 + 2) * 4 + u) * 4 + o], lds[mc_swz((r0 + 3) * 4 + u) * 4 + o]};
+}
+
 // Tile16 only: a workgroup of WG waves owns a chunk of WG S consecutive steps
 // of one row, wave w the steps w S .. w S + S - 1 of it. With WG > 1 the waves
 // pass their summaries through LDS: wave w composes the summaries of waves
@@ -357,27 +374,53 @@ __global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
   // layout); backward also the forward state one processing step on, in R
   // layout (h_prev^T in D layout, for dA = lam h_prev^T). Steps past the row's
   // end (s >= n) hold zeros and are computed but never stored or published.
-  v4f X[S], Y[S], H[BWD ? S : 1];
+  // The FULL backward stages X and Y in LDS instead (kStage): each block is
+  // one direct 16-byte-per-lane row load into LDS, read back column-wise at
+  // each use, so neither the column-wise global loads nor their registers are
+  // needed. Xs(s) / Ys(s) give a step's operands either way.
+  constexpr bool kStage = FULL && BWD;
+  __shared__ __attribute__((aligned(16))) float s_stg[kStage ? WG * S * 2 * 256 : 4];
+  float* const stg = s_stg + (kStage ? w * S * 2 * 256 : 0);
+  v4f X[kStage ? 1 : S], Y[kStage ? 1 : S], H[BWD ? S : 1];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    X[s] = mc_zero();
-    Y[s] = mc_zero();
+    if constexpr (!kStage) {
+      X[s] = mc_zero();
+      Y[s] = mc_zero();
+    }
     if constexpr (BWD) H[s] = mc_zero();
     if (s < n) {
       const int64_t j = j0 + s;
       const int64_t t = wk.phys(j);
-      // forward, FULL: B is read as rows (one 16-byte load per lane instead of
-      // four 4-byte ones) and turned into the D layout below
-      Y[s] = (FULL && !BWD) ? wk.sh.ldB_R(wk.blkB(a.B, t)) : wk.sh.ldB_D(wk.blkB(a.B, t));
-      if constexpr (!BWD) {
-        X[s] = wk.sh.ldA_R(wk.blkA(a.A, t));
+      if constexpr (kStage) {
+        if (j > 0) mc_stage(wk.blkA(a.A, wk.phys(j - 1)), stg + (2 * s) * 256);  // A one processing step back
+        mc_stage(wk.blkB(a.B, t), stg + (2 * s + 1) * 256);
       } else {
-        if (j > 0) X[s] = wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j - 1)));  // (A one processing step back)^T
+        // forward, FULL: B is read as rows (one 16-byte load per lane instead
+        // of four 4-byte ones) and turned into the D layout below
+        Y[s] = (FULL && !BWD) ? wk.sh.ldB_R(wk.blkB(a.B, t)) : wk.sh.ldB_D(wk.blkB(a.B, t));
+        if constexpr (!BWD) {
+          X[s] = wk.sh.ldA_R(wk.blkA(a.A, t));
+        } else {
+          if (j > 0) X[s] = wk.sh.ldA_D(wk.blkA(a.A, wk.phys(j - 1)));  // (A one processing step back)^T
+        }
+      }
+      if constexpr (BWD) {
         if (j + 1 < a.T) H[s] = wk.sh.ldB_R(wk.blkB(a.hs, wk.phys(j + 1)));
       }
     }
   }
   wait_stage_loads();
+  // operands of step s (zero where nothing was loaded: past the row's end,
+  // and X at the row's first processing step)
+  auto Xs = [&](int s) -> v4f {
+    if constexpr (kStage) return (s < n && j0 + s > 0) ? mc_unstage(stg + (2 * s) * 256) : mc_zero();
+    else return X[s];
+  };
+  auto Ys = [&](int s) -> v4f {
+    if constexpr (kStage) return s < n ? mc_unstage(stg + (2 * s + 1) * 256) : mc_zero();
+    else return Y[s];
+  };
   if constexpr (FULL && !BWD) {
 #pragma unroll
     for (int s = 0; s < S; ++s) Y[s] = TL::d_to_r(s_t, Y[s]);  // rows -> D layout
@@ -413,11 +456,12 @@ __global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
   v4f P = tile_ident<TL>(), Q = mc_zero();
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    zerom |= (uint32_t)(s < n && TL::zero(X[s])) << s;
+    const v4f Xv = Xs(s), Yv = Ys(s);
+    zerom |= (uint32_t)(s < n && TL::zero(Xv)) << s;
     const bool f = ((firstm | zerom) >> s) & 1u;
-    const v4f Pn = TL::mm(X[s], P, mc_zero()), Qn = TL::mm(X[s], Q, Y[s]);
+    const v4f Pn = TL::mm(Xv, P, mc_zero()), Qn = TL::mm(Xv, Q, Yv);
     P = f ? mc_zero() : Pn;
-    Q = f ? Y[s] : Qn;
+    Q = f ? Yv : Qn;
   }
   const uint32_t hardm = firstm | zerom;
   const bool hard = hardm != 0u, first0 = (hardm & 1u) != 0u;
@@ -501,8 +545,9 @@ __global__ __launch_bounds__(64 * WG) void k_mc_scan(const MatArgs a) {
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const bool first = (hardm >> s) & 1u;
-    const v4f hn = TL::mm(X[s], h, Y[s]);
-    h = first ? Y[s] : hn;  // h holds lam in the backward
+    const v4f Yv = Ys(s);
+    const v4f hn = TL::mm(Xs(s), h, Yv);
+    h = first ? Yv : hn;  // h holds lam in the backward
     if constexpr (BWD) {
       // dA_t = lam h_prev^T (the transpose is a whole-wave operation)
       const v4f lamR = TL::d_to_r(s_t, h);
@@ -840,9 +885,13 @@ __global__ __launch_bounds__(64 * WG) void k_mc_rowseg(const MatArgs a) {
 // kChunk steps), from timing at (16, 16), 512 rows, T = 4096, flushed.
 // Forward, waves x steps: 1 x 32 1.24 ms (one wave per SIMD), 2 x 32 1.35,
 // 4 x 32 1.54, 2 x 16 1.19, 4 x 8 1.19, 4 x 12 1.21, 8 x 8 1.11, 8 x 16 1.42,
-// 4 x 16 1.09-1.11 (two waves per SIMD, a 64-step chunk). Backward: 1 x 16
-// 2.24 ms, 2 x 16 2.21, 4 x 16 2.60, 4 x 8 3.62, 8 x 8 2.72 (32 steps per wave
-// spill).
+// 4 x 16 1.09-1.11 (two waves per SIMD, a 64-step chunk). Backward, operands
+// in registers: 1 x 16 2.24 ms, 2 x 16 2.21, 4 x 16 2.60, 4 x 8 3.62, 8 x 8
+// 2.72 (32 steps per wave spill); with A and dy staged in LDS: 2 x 16
+// 2.13 ms against 2.14-2.15 in registers, 1 x 16 2.21, 4 x 16 2.44, 2 x 8 3.56,
+// 4 x 8 3.69, 4 x 4 2.41. Shapes that keep more chunks resident than there are
+// rows (512 here) put chunks of one row side by side, each waiting for the one
+// before it.
 constexpr int kChunkFwd = 16, kChunkBwd = 16;
 constexpr int kWavesFwd = 4, kWavesBwd = 2;
 // Steps per lane group of the 4 x 4 row-segment kernel (a wave spans 16 x that),

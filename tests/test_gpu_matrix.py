@@ -283,6 +283,49 @@ def test_matrix_exact_mode_bitwise(m, oracle_lib, kv, reverse):
     assert np.array_equal(dh0.cpu().double().numpy(), rh0)
 
 
+# Forward chunks are shared by several waves (16x16 tile: waves of 16 steps,
+# 64 per chunk; 4x4 tile: waves of 256 steps, 1024 per chunk); backward chunks
+# are 2 x 16 and 1 x 256 steps.
+@pytest.mark.parametrize("kv,span,chunk", [((16, 16), 16, 64), ((8, 2), 16, 64), ((4, 4), 256, 1024),
+                                           ((1, 4), 256, 1024)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_matrix_exact_wave_and_chunk_boundaries(m, oracle_lib, kv, span, chunk, reverse):
+    """Integer data, bit for bit against the oracle: sequence starts (in
+    processing order) and resets placed on, one before and one after the
+    boundaries between the waves of a chunk and between chunks, a sequence
+    that is exactly one wave span, a chunk whose second wave starts with a
+    reset, and chunks crossed by one long sequence (the carry passed from wave
+    to wave and chunk to chunk)."""
+    k, v = kv
+    r = np.random.default_rng(900 + 10 * k + v + reverse)
+    rows, T = 3, 4 * chunk + span // 2 + 3
+    A, B, dy = _signed_perm_case(r, k, v, rows, T, max_run=512 if max(k, v) > 4 else 2048, p_zero=0.0)
+    # processing-order positions: chunk 0 is cut at its wave edges, chunk 1 by
+    # a one-span sequence, chunk 2 has no boundary, chunk 3 is cut just after
+    # a chunk edge and just before a wave edge
+    starts = {span, 2 * span - 1, chunk - 1, chunk + span, chunk + 2 * span, 3 * chunk + 1, 3 * chunk + 2 * span - 1}
+    resets = {chunk + 3 * span, span + 1, 2 * chunk + span - 1, 2 * chunk + 2 * span, 4 * chunk}
+    starts = sorted(j for j in starts if 0 < j < T)
+    phys = (lambda j: T - 1 - j) if reverse else (lambda j: j)
+    # a processing-order start at j is physical step j (forward) or the end of
+    # the physical segment ending at T - 1 - j (reverse)
+    cuts = sorted({T - j for j in starts} if reverse else set(starts))
+    cu = np.array([0] + cuts + [T], np.int64)
+    for j in resets:
+        if j < T:
+            A[:, phys(j)] = 0.0
+    h0 = r.integers(-1, 2, size=(len(cu) - 1, rows, k, v)).astype(np.float32)
+    cu_t, h0_t, Ad = _t(cu, torch.int32), _t(h0), _t(A)
+    h = m.matrix_affine_scan_fwd(Ad, _t(B), h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    href = oracle_lib.matrix_affine_scan_fwd(A, B, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(h.cpu().double().numpy(), href)
+    dA, dB, dh0 = m.matrix_affine_scan_bwd(Ad, h, _t(dy), h0=h0_t, cu_seqlens=cu_t, reverse=reverse)
+    rA, rB, rh0 = oracle_lib.matrix_affine_scan_bwd(A, href, dy, h0=h0, cu_seqlens=cu, reverse=reverse)
+    assert np.array_equal(dB.cpu().double().numpy(), rB)
+    assert np.array_equal(dA.cpu().double().numpy(), rA)
+    assert np.array_equal(dh0.cpu().double().numpy(), rh0)
+
+
 @pytest.mark.parametrize("kv", [(2, 1), (4, 4), (16, 16), (8, 2), (1, 4)])
 @pytest.mark.parametrize("T", [700, 5001])
 @pytest.mark.parametrize("reverse", [False, True])
